@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""MoBA prefill forward on one MI355X: throughput, per-step times, roofline and the
+CPU oracle baseline, printed as one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama8b_128k] [--gpus 1]
+
+A step is one whole moba_forward (centroid pool, gate + top-k, inverted index,
+history attention, current-block attention, merge) over one batch of seeded synthetic
+inputs already resident in HBM.  `value` is effective TFLOP/s: 4 * head_dim * (keys
+each query head attends) summed over query heads and tokens, divided by the step time.
+The per-step times come from HIP events the library records on the launch stream
+(moba_forward_profile) in extra profiled steps after the timed ones.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoBA prefill fwd ms + effective TFLOP/s at 128K, % bf16 MFMA peak (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_history_llama8b_128k_counters.txt")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_long_pool_amd", "csrc", "attn.hip")
+
+
+# ------------------------------------------------------------------ work counts
+def pair_counts(T: int, B: int, k: int):
+    """Per query head: (history pairs, current-block pairs) attended, from the
+    definition (T a multiple of B): B^2 * sum_c min(c, k-1) and nb * B (B+1) / 2."""
+    nb = T // B
+    hist = B * B * sum(min(c, k - 1) for c in range(nb))
+    cur = nb * B * (B + 1) // 2
+    return hist, cur
+
+
+def gate_bytes(w) -> int:
+    """Bytes the gate must move: query rows that have more causal history blocks than
+    slots (the others select every causal block without a score), the idx rows, and
+    the bf16 hi/lo centroids."""
+    nb = w.seqlen // w.block
+    competing_rows = w.batch * w.hq * w.block * sum(1 for c in range(nb) if c > w.topk - 1)
+    q = competing_rows * w.head_dim * 2
+    idx = w.batch * w.hq * w.seqlen * w.topk * 4
+    cent = w.batch * w.hkv * nb * w.head_dim * 2 * 2
+    return q + idx + cent
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per history-attention dispatch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_t = re.search(r"traffic_bytes_per_dispatch:\s*([0-9.eE+]+)", text)
+    if not m_h or not m_t or m_h.group(1) != source_hash(ATTN_SOURCE):
+        return None
+    return float(m_t.group(1))
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(w, inp, budget_s: float):
+    """The float64 oracle, as it is, on a bounded stratified sample of the workload's
+    rows, one thread; the rate is scaled to the whole workload's algorithmic FLOP."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from workloads import bf16_to_f64
+
+    with threadpool_limits(limits=1):
+        K = bf16_to_f64(inp["k"])
+        V = bf16_to_f64(inp["v"])
+        Q = bf16_to_f64(inp["q"])
+        t0 = time.perf_counter()
+        C = oracle.centroids(K, w.block)
+        t_cent = time.perf_counter() - t0
+        rng = np.random.default_rng(12345)
+        nb = w.seqlen // w.block
+        done, flop, t_rows = 0, 0, 0.0
+        start = time.perf_counter()
+        while time.perf_counter() - start < budget_s:
+            c = done % nb                      # round-robin over query blocks
+            row = (0, int(c * w.block + rng.integers(w.block)), int(rng.integers(w.hq)))
+            t1 = time.perf_counter()
+            _, _, sels, _ = oracle.moba_rows(Q, K, V, w.block, w.topk, w.sm_scale, [row], C=C)
+            t_rows += time.perf_counter() - t1
+            n_keys = oracle.attended_keys(sels[0], row[1], w.block, w.seqlen).size
+            flop += 4 * w.head_dim * n_keys
+            done += 1
+    hist, cur = pair_counts(w.seqlen, w.block, w.topk)
+    total_flop = 4 * w.head_dim * w.batch * w.hq * (hist + cur)
+    est_s = t_cent + t_rows * total_flop / flop
+    return {
+        "value": total_flop / est_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} rows (round-robin over the {nb} query blocks, random token and "
+                   f"head) of {w.name} in {t_rows:.1f} s plus the full centroid pool "
+                   f"({t_cent:.2f} s); whole-workload time extrapolated by attended "
+                   f"FLOP: {est_s:.0f} s"),
+    }
+
+
+# ------------------------------------------------------------------ main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_128k")
+    ap.add_argument("--profile-steps", type=int, default=None,
+                    help="extra steps timed per stage (default: --steps)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE "
+              f"{world}): the MoBA layer shards by kv-head with no communication, so "
+              "the figure at N GPUs is N times the one-GPU figure on 1/N of the heads; "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_long_pool_amd as moba
+    from workloads import get_workload, make_inputs, to_torch_bf16
+
+    w = get_workload(a.workload)
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = to_torch_bf16(inp["q"], dev)
+    k = to_torch_bf16(inp["k"], dev)
+    v = to_torch_bf16(inp["v"], dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.hq, w.seqlen), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.batch, w.hq, w.seqlen, w.topk), dtype=torch.int32, device=dev)
+    ws = moba.alloc_workspace(q, k, w.block, w.topk)
+    full_ws, _ = moba.workspace_bytes(w.batch, w.seqlen, w.hq, w.hkv, w.head_dim, w.block,
+                                      w.topk)
+
+    def step(profile=False):
+        return moba.forward(q, k, v, w.block, w.topk, w.sm_scale, workspace=ws, out=out,
+                            lse=lse, idx=idx, profile=profile)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+
+    n_prof = a.steps if a.profile_steps is None else a.profile_steps
+    stage = {s: 0.0 for s in moba.STAGES}
+    for _ in range(n_prof):
+        *_, st = step(profile=True)
+        for s_ in stage:
+            stage[s_] += st[s_] / n_prof
+    print(f"[bench] {ms:.3f} ms/step; stages {stage}", file=sys.stderr, flush=True)
+
+    hist, cur = pair_counts(w.seqlen, w.block, w.topk)
+    heads = w.batch * w.hq
+    flop_hist = 4 * w.head_dim * heads * hist
+    flop_cur = 4 * w.head_dim * heads * cur
+    flop = flop_hist + flop_cur
+    tflops = flop / (ms * 1e-3) / 1e12
+    attn_ms = stage["history"] + stage["current"] + stage["merge"]
+    hist_tflops = flop_hist / (stage["history"] * 1e-3) / 1e12 if stage["history"] else None
+    gbytes = gate_bytes(w)
+    gate_gbs = gbytes / (stage["gate"] * 1e-3) / 1e9 if stage["gate"] else None
+    # history attention runs once per kv-head group; one launch covers all of them when
+    # the workspace holds every head (it does for this workload)
+    one_launch = ws.numel() >= full_ws
+    roofline = {
+        "bound": "mfma",
+        "kernel": "attn_history_kernel (history attention, gathered query tiles)",
+        "achieved": hist_tflops,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": hist_tflops / PEAK_BF16_TFLOPS if hist_tflops else None,
+        "traffic": read_traffic() if one_launch else None,
+        "algorithmic_per_launch": f"{flop_hist:.4e} FLOP = 4 * d * {heads} heads * "
+                                  f"{hist} history pairs per head",
+    }
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen,
+                   "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.head_dim,
+                   "block": w.block, "topk": w.topk, "recipe": w.recipe},
+        "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "stages_ms": stage,
+        "attention_tflops": flop / (attn_ms * 1e-3) / 1e12 if attn_ms else None,
+        "attention_frac_of_bf16_peak": (flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+                                        if attn_ms else None),
+        "gate_gbs": gate_gbs,
+        "gate_frac_of_hbm_peak": gate_gbs / PEAK_HBM_GBS if gate_gbs else None,
+        "gate_algorithmic_bytes": gbytes,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline (~{a.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,259 @@
+"""MoBA prefill forward on MI355X (gfx950): thin Python binding over libmoba.so.
+
+Every step of the path runs in the library's HIP kernels; this module only checks
+tensor arguments, allocates outputs and the workspace with torch, and passes raw
+device pointers and torch's current HIP stream through ctypes.  If libmoba.so is
+missing the import fails loudly: there is no CPU fallback.
+
+    out, lse, idx = forward(q, k, v, block=4096, topk=12)
+
+q [b, T, Hq, d], k and v [b, T, Hkv, d] bfloat16 on the GPU; out like q (bf16),
+lse [b, Hq, T] float32 (natural log), idx [b, Hq, T, topk] int32 (ascending selected
+blocks, -1 padded).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LIB_PATH", "MobaError", "check_args", "workspace_bytes", "forward",
+    "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
+    "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace",
+]
+
+# names of the steps timed by profile=True, in the library's order
+STAGES = ("pool", "gate", "index", "history", "current", "merge")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoba.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_pool_amd.build` "
+        "(hipcc --offload-arch=gfx950).  There is no fallback implementation.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i, _f, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "moba_check_args": (_i, [_i, _i, _i, _i, _i, _i, _i, _f]),
+    "moba_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "moba_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
+                          _vp, _sz, _vp]),
+    "moba_forward_profile": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                  _vp, _vp, _sz, _vp, ctypes.POINTER(_f)]),
+    "moba_strerror": (ctypes.c_char_p, [_i]),
+    "moba_stage_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "moba_pool_centroids": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "moba_gate_topk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "moba_index_entries": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i]),
+    "moba_build_index": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz,
+                              _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+MOBA_OK, MOBA_ERR_INVALID_ARG, MOBA_ERR_UNSUPPORTED, MOBA_ERR_WORKSPACE, MOBA_ERR_HIP = (
+    0, -1, -2, -3, -4)
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def strerror(status: int) -> str:
+    return lib.moba_strerror(int(status)).decode()
+
+
+def _raise(status: int, where: str):
+    if status == MOBA_ERR_INVALID_ARG or status == MOBA_ERR_UNSUPPORTED:
+        raise ValueError(f"{where}: {strerror(status)} (status {status})")
+    if status != MOBA_OK:
+        raise MobaError(status, where)
+
+
+def check_args(batch, seqlen, hq, hkv, head_dim, block, topk, scale) -> int:
+    """Host-only shape check; returns the status code."""
+    return lib.moba_check_args(batch, seqlen, hq, hkv, head_dim, block, topk, float(scale))
+
+
+def workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk):
+    """(bytes for all kv-heads in one pass, bytes for one kv-head per pass)."""
+    mn = ctypes.c_size_t(0)
+    full = lib.moba_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk,
+                                    ctypes.byref(mn))
+    return int(full), int(mn.value)
+
+
+def stage_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk) -> int:
+    return int(lib.moba_stage_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk))
+
+
+def index_entries(batch, seqlen, hq, hkv, block, topk, kv_count) -> int:
+    return int(lib.moba_index_entries(batch, seqlen, hq, hkv, block, topk, kv_count))
+
+
+# ----------------------------------------------------------------------------- torch
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _need(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _alloc_workspace(nbytes, device):
+    torch = _torch()
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def alloc_workspace(q, k, block: int, topk: int, max_workspace_bytes: int | None = None):
+    """A uint8 workspace tensor for these inputs: the all-heads-at-once size, reduced
+    towards the one-kv-head size when it exceeds ``max_workspace_bytes`` (default: 60%
+    of free device memory)."""
+    torch = _torch()
+    b, T, hq, d = q.shape
+    hkv = k.shape[2]
+    full, mn = workspace_bytes(b, T, hq, hkv, d, block, topk)
+    if full == 0:
+        _raise(MOBA_ERR_UNSUPPORTED, "moba_workspace_bytes")
+    if max_workspace_bytes is None:
+        free, _ = torch.cuda.mem_get_info(q.device)
+        max_workspace_bytes = int(0.6 * free)
+    size = full if full <= max_workspace_bytes else max(mn, max_workspace_bytes)
+    return _alloc_workspace(size, q.device)
+
+
+def forward(q, k, v, block: int, topk: int, scale: float | None = None, workspace=None,
+            max_workspace_bytes: int | None = None, out=None, lse=None, idx=None,
+            profile: bool = False):
+    """MoBA prefill forward.  Returns (out bf16, lse fp32, idx int32), and with
+    ``profile=True`` also a dict of per-step GPU milliseconds (HIP events on the
+    current stream; the call then synchronises).
+
+    Outputs and the workspace are allocated with torch unless given."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    b, T, hq, d = q.shape
+    if k.shape[0] != b or k.shape[1] != T or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    hkv = k.shape[2]
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _raise(check_args(b, T, hq, hkv, d, block, topk, scale), "moba_forward")
+    if workspace is None:
+        workspace = alloc_workspace(q, k, block, topk, max_workspace_bytes)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, hq, T), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((b, hq, T, topk), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(idx, "idx", torch.int32, 4)
+    if out.shape != q.shape or lse.shape != (b, hq, T) or idx.shape != (b, hq, T, topk):
+        raise ValueError("output shapes do not match the inputs")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv, d, block, topk,
+            float(scale), out.data_ptr(), lse.data_ptr(), idx.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), _stream_ptr())
+    with torch.cuda.device(q.device):
+        if profile:
+            ms = (ctypes.c_float * len(STAGES))()
+            st = lib.moba_forward_profile(*args, ms)
+        else:
+            st = lib.moba_forward(*args)
+    _raise(st, "moba_forward")
+    if profile:
+        return out, lse, idx, dict(zip(STAGES, (float(x) for x in ms)))
+    return out, lse, idx
+
+
+def pool_centroids(k, block: int):
+    """Centroid mean-pool stage: float32 [b, Hkv, nb, d]."""
+    torch = _torch()
+    _need(k, "k", torch.bfloat16, 4)
+    b, T, hkv, d = k.shape
+    _raise(check_args(b, T, hkv, hkv, d, block, 1, 1.0), "moba_pool_centroids")
+    ws = _alloc_workspace(stage_workspace_bytes(b, T, hkv, hkv, d, block, 1), k.device)
+    cent = torch.empty((b, hkv, T // block, d), dtype=torch.float32, device=k.device)
+    with torch.cuda.device(k.device):
+        st = lib.moba_pool_centroids(k.data_ptr(), b, T, hkv, d, block, cent.data_ptr(),
+                                     ws.data_ptr(), ws.numel(), _stream_ptr())
+    _raise(st, "moba_pool_centroids")
+    return cent
+
+
+def gate_topk(q, centroids, block: int, topk: int):
+    """Gate + top-k stage from float32 centroids: int32 [b, Hq, T, topk]."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(centroids, "centroids", torch.float32, 4)
+    b, T, hq, d = q.shape
+    hkv = centroids.shape[1]
+    if centroids.shape != (b, hkv, T // block, d):
+        raise ValueError(f"centroids must be [b, hkv, nb, d], got {tuple(centroids.shape)}")
+    _raise(check_args(b, T, hq, hkv, d, block, topk, 1.0), "moba_gate_topk")
+    ws = _alloc_workspace(stage_workspace_bytes(b, T, hq, hkv, d, block, topk), q.device)
+    idx = torch.empty((b, hq, T, topk), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.moba_gate_topk(q.data_ptr(), centroids.data_ptr(), b, T, hq, hkv, d, block,
+                                topk, idx.data_ptr(), ws.data_ptr(), ws.numel(),
+                                _stream_ptr())
+    _raise(st, "moba_gate_topk")
+    return idx
+
+
+def build_index(idx, hkv: int, block: int, topk: int, kv_begin: int = 0,
+                kv_count: int | None = None):
+    """Inverted-index stage: (list_offsets int32 [b*kv_count*nb + 1], entries uint32
+    as int32 [n])."""
+    torch = _torch()
+    _need(idx, "idx", torch.int32, 4)
+    b, hq, T, k_ = idx.shape
+    if k_ != topk:
+        raise ValueError("idx last dim must equal topk")
+    if kv_count is None:
+        kv_count = hkv - kv_begin
+    _raise(check_args(b, T, hq, hkv, 64, block, topk, 1.0), "moba_build_index")
+    n = index_entries(b, T, hq, hkv, block, topk, kv_count)
+    if n < 0:
+        raise ValueError("bad kv range")
+    nb = T // block
+    ws = _alloc_workspace(stage_workspace_bytes(b, T, hq, hkv, 64, block, topk), idx.device)
+    offs = torch.empty(b * kv_count * nb + 1, dtype=torch.int32, device=idx.device)
+    ent = torch.empty(max(n, 1), dtype=torch.int32, device=idx.device)
+    with torch.cuda.device(idx.device):
+        st = lib.moba_build_index(idx.data_ptr(), b, T, hq, hkv, block, topk, kv_begin,
+                                  kv_count, offs.data_ptr(), ent.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream_ptr())
+    _raise(st, "moba_build_index")
+    return offs, ent[:n]

@@ -1,0 +1,338 @@
+// Host side of libmoba: argument checks, workspace layout, and the launch sequence
+// of the MoBA prefill forward pass.  Every check runs before the first launch.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moba.h"
+#include "moba_internal.h"
+
+using moba::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBlocks = 2048;  // inverted-index LDS tables hold 6 ints per block
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int check(int batch, int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+          float scale) {
+  if (batch <= 0 || seqlen <= 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || block <= 0 ||
+      topk <= 0)
+    return MOBA_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return MOBA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return MOBA_ERR_INVALID_ARG;
+  if (scale <= 0.f) return MOBA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return MOBA_ERR_UNSUPPORTED;
+  if (block < 16 || block % 16 != 0) return MOBA_ERR_UNSUPPORTED;
+  if (seqlen % block != 0) return MOBA_ERR_UNSUPPORTED;
+  if (topk > 33) return MOBA_ERR_UNSUPPORTED;
+  if (seqlen / block > kMaxBlocks) return MOBA_ERR_UNSUPPORTED;
+  const long long G = hq / hkv;
+  if ((long long)seqlen * G >= (1ll << 27)) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)batch * seqlen * hq >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+// rows of one query head that carry history slot entries, times slots
+long long entries_per_head(const Shape& s) {
+  long long per = 0;
+  for (int c = 0; c < s.nb(); ++c) per += (long long)s.block * (c < s.KH() ? c : s.KH());
+  return per;
+}
+
+struct Layout {
+  // whole-problem buffers
+  size_t pool_partial, cent, chi, clo;
+  // per group of ng kv-heads
+  size_t chunk_counts, list_count, list_offsets, tile_offsets, tiles, entries, part_o,
+      part_lse;
+  size_t total;
+  long long n_entries;
+  long long max_tiles;
+};
+
+Layout make_layout(const Shape& s, int ng) {
+  Layout L{};
+  const size_t nb = s.nb();
+  const size_t splits = moba::pool_splits(s);
+  const size_t ncent = (size_t)s.b * s.hkv * nb * s.d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.pool_partial = take((size_t)s.b * nb * splits * s.hkv * s.d * sizeof(float));
+  L.cent = take(ncent * sizeof(float));
+  L.chi = take(ncent * sizeof(uint16_t));
+  L.clo = take(ncent * sizeof(uint16_t));
+  const size_t nlists = (size_t)s.b * ng * nb;
+  const size_t nchunks = moba::index_chunks(s);
+  L.n_entries = (long long)s.b * ng * s.G() * entries_per_head(s);
+  const int tm = moba::history_tile_rows();
+  L.max_tiles = (L.n_entries + tm - 1) / tm + (long long)nlists;
+  L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
+  L.list_count = take(nlists * sizeof(int32_t));
+  L.list_offsets = take((nlists + 1) * sizeof(int32_t));
+  L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
+  L.tiles = take((size_t)L.max_tiles * sizeof(int4));
+  L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
+  const size_t prow = (size_t)s.b * ng * s.G() * s.T * s.topk;
+  L.part_o = take(prow * s.d * sizeof(float));
+  L.part_lse = take(prow * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+bool layout_ok(const Layout& L) {
+  return L.n_entries < (1ll << 31) && L.max_tiles < (1ll << 31);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_ERR_HIP; }
+
+#define MOBA_TRY(expr)                        \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return MOBA_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int moba_check_args(int batch, int seqlen, int hq, int hkv, int head_dim, int block,
+                    int topk, float scale) {
+  return check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+}
+
+size_t moba_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim,
+                            int block, int topk, size_t* min_bytes) {
+  if (min_bytes) *min_bytes = 0;
+  if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  const Layout one = make_layout(s, 1);
+  if (!layout_ok(one)) return 0;
+  if (min_bytes) *min_bytes = one.total;
+  for (int ng = hkv; ng >= 1; --ng) {
+    const Layout L = make_layout(s, ng);
+    if (layout_ok(L)) return L.total;
+  }
+  return one.total;
+}
+
+const char* moba_strerror(int status) {
+  switch (status) {
+    case MOBA_OK: return "success";
+    case MOBA_ERR_INVALID_ARG: return "invalid argument";
+    case MOBA_ERR_UNSUPPORTED: return "shape or value not supported by this build";
+    case MOBA_ERR_WORKSPACE: return "workspace too small";
+    case MOBA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+// Records HIP events at stage boundaries on the launch stream when profiling.
+struct StageClock {
+  hipStream_t st;
+  bool on;
+  int n = 0;
+  int stage[64];
+  hipEvent_t ev[65];
+  bool begin(hipStream_t s, bool enable) {
+    st = s;
+    on = enable;
+    if (!on) return true;
+    for (int i = 0; i < 65; ++i)
+      if (hipEventCreate(&ev[i]) != hipSuccess) return false;
+    return hipEventRecord(ev[0], st) == hipSuccess;
+  }
+  hipError_t mark(int which) {
+    if (!on || n >= 64) return hipSuccess;
+    stage[n] = which;
+    return hipEventRecord(ev[++n], st);
+  }
+  int finish(float* ms) {
+    if (!on) return MOBA_OK;
+    int status = MOBA_OK;
+    if (hipEventSynchronize(ev[n]) != hipSuccess) status = MOBA_ERR_HIP;
+    for (int i = 0; i < MOBA_NUM_STAGES; ++i) ms[i] = 0.f;
+    for (int i = 0; i < n && status == MOBA_OK; ++i) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, ev[i], ev[i + 1]) != hipSuccess) status = MOBA_ERR_HIP;
+      ms[stage[i]] += t;
+    }
+    for (int i = 0; i < 65; ++i) hipEventDestroy(ev[i]);
+    return status;
+  }
+};
+
+int forward_impl(const void* q, const void* k, const void* v, int batch, int seqlen,
+                 int hq, int hkv, int head_dim, int block, int topk, float scale,
+                 void* out, float* lse, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, void* stream, float* stage_ms) {
+  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out || !lse || !idx || !workspace) return MOBA_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  // the largest group of kv-heads whose buffers fit
+  int ng = hkv;
+  Layout L = make_layout(s, ng);
+  while (ng > 1 && (L.total > workspace_bytes || !layout_ok(L))) L = make_layout(s, --ng);
+  if (L.total > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  if (!layout_ok(L)) return MOBA_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  const uint16_t* vb = static_cast<const uint16_t*>(v);
+  float* cent = reinterpret_cast<float*>(ws + L.cent);
+  uint16_t* chi = reinterpret_cast<uint16_t*>(ws + L.chi);
+  uint16_t* clo = reinterpret_cast<uint16_t*>(ws + L.clo);
+  StageClock clock;
+  if (!clock.begin(hs, stage_ms != nullptr)) return MOBA_ERR_HIP;
+
+  MOBA_TRY(moba::launch_pool(s, kb, reinterpret_cast<float*>(ws + L.pool_partial), cent, hs));
+  MOBA_TRY(moba::launch_centroid_split(s, cent, chi, clo, hs));
+  MOBA_TRY(clock.mark(0));
+  MOBA_TRY(moba::launch_gate(s, qb, chi, clo, idx, hs));
+  MOBA_TRY(clock.mark(1));
+
+  for (int g0 = 0; g0 < hkv; g0 += ng) {
+    const int ngc = ng < hkv - g0 ? ng : hkv - g0;
+    const int nlc = s.b * ngc * s.nb();
+    float* po = reinterpret_cast<float*>(ws + L.part_o);
+    float* pl = reinterpret_cast<float*>(ws + L.part_lse);
+    if (s.KH() > 0) {
+      int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
+      int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
+      uint32_t* entries = reinterpret_cast<uint32_t*>(ws + L.entries);
+      MOBA_TRY(moba::launch_index(s, idx, g0, ngc, moba::history_tile_rows(),
+                                  reinterpret_cast<int32_t*>(ws + L.chunk_counts),
+                                  reinterpret_cast<int32_t*>(ws + L.list_count),
+                                  reinterpret_cast<int32_t*>(ws + L.list_offsets),
+                                  tile_offsets, tiles, entries, L.n_entries, hs));
+      MOBA_TRY(clock.mark(2));
+      const Layout Lc = make_layout(s, ngc);
+      MOBA_TRY(moba::launch_attn_history(s, qb, kb, vb, scale, g0, ngc, tiles,
+                                         tile_offsets + nlc, (int)Lc.max_tiles, entries,
+                                         po, pl, hs));
+      MOBA_TRY(clock.mark(3));
+    }
+    MOBA_TRY(moba::launch_attn_current(s, qb, kb, vb, scale, g0, ngc, po, pl, hs));
+    MOBA_TRY(clock.mark(4));
+    MOBA_TRY(moba::launch_merge(s, g0, ngc, po, pl, static_cast<uint16_t*>(out), lse, hs));
+    MOBA_TRY(clock.mark(5));
+  }
+  return clock.finish(stage_ms);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moba_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
+                 int hq, int hkv, int head_dim, int block, int topk, float scale,
+                 void* out, float* lse, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return forward_impl(q, k, v, batch, seqlen, hq, hkv, head_dim, block, topk, scale, out,
+                      lse, idx, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
+                         int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+                         float scale, void* out, float* lse, int32_t* idx,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         float* stage_ms) {
+  if (!stage_ms) return MOBA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, batch, seqlen, hq, hkv, head_dim, block, topk, scale, out,
+                      lse, idx, workspace, workspace_bytes, stream, stage_ms);
+}
+
+// ------------------------------------------------------------------- stages
+size_t moba_stage_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim,
+                                  int block, int topk) {
+  if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  const Layout L = make_layout(s, hkv);
+  // pool partials, or hi/lo centroids, or the index scratch (chunk counts + counts +
+  // tile offsets)
+  const size_t a = L.cent;
+  const size_t b2 = align_up((size_t)s.b * s.hkv * s.nb() * s.d * sizeof(uint16_t)) * 2;
+  const size_t c = L.tiles - L.chunk_counts;
+  size_t m = a > b2 ? a : b2;
+  return m > c ? m : c;
+}
+
+int moba_pool_centroids(const void* k, int batch, int seqlen, int hkv, int head_dim,
+                        int block, float* centroids, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check(batch, seqlen, hkv, hkv, head_dim, block, 1, 1.f);
+  if (st != MOBA_OK) return st;
+  if (!k || !centroids || !workspace) return MOBA_ERR_INVALID_ARG;
+  const Shape s{batch, seqlen, hkv, hkv, head_dim, block, 1};
+  const Layout L = make_layout(s, 1);
+  if (L.cent > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  return hip_status(moba::launch_pool(s, static_cast<const uint16_t*>(k),
+                                      reinterpret_cast<float*>(workspace), centroids,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moba_gate_topk(const void* q, const float* centroids, int batch, int seqlen, int hq,
+                   int hkv, int head_dim, int block, int topk, int32_t* idx,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f);
+  if (st != MOBA_OK) return st;
+  if (!q || !centroids || !idx || !workspace) return MOBA_ERR_INVALID_ARG;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  const size_t n = (size_t)s.b * s.hkv * s.nb() * s.d;
+  const size_t half = align_up(n * sizeof(uint16_t));
+  if (2 * half > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  uint16_t* chi = static_cast<uint16_t*>(workspace);
+  uint16_t* clo = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + half);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  MOBA_TRY(moba::launch_centroid_split(s, centroids, chi, clo, hs));
+  return hip_status(
+      moba::launch_gate(s, static_cast<const uint16_t*>(q), chi, clo, idx, hs));
+}
+
+int64_t moba_index_entries(int batch, int seqlen, int hq, int hkv, int block, int topk,
+                           int kv_count) {
+  if (check(batch, seqlen, hq, hkv, 64, block, topk, 1.f) != MOBA_OK) return -1;
+  if (kv_count <= 0 || kv_count > hkv) return -1;
+  const Shape s{batch, seqlen, hq, hkv, 64, block, topk};
+  return (int64_t)s.b * kv_count * s.G() * entries_per_head(s);
+}
+
+int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
+                     int block, int topk, int kv_begin, int kv_count,
+                     int32_t* list_offsets, uint32_t* entries, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check(batch, seqlen, hq, hkv, 64, block, topk, 1.f);
+  if (st != MOBA_OK) return st;
+  if (!idx || !list_offsets || !entries || !workspace) return MOBA_ERR_INVALID_ARG;
+  if (kv_begin < 0 || kv_count <= 0 || kv_begin + kv_count > hkv) return MOBA_ERR_INVALID_ARG;
+  if (topk < 2) return MOBA_ERR_UNSUPPORTED;  // no history slots, no index
+  const Shape s{batch, seqlen, hq, hkv, 64, block, topk};
+  const size_t nlists = (size_t)s.b * kv_count * s.nb();
+  const size_t cc = align_up((size_t)s.b * kv_count * moba::index_chunks(s) * s.nb() *
+                             sizeof(int32_t));
+  const size_t lc = align_up(nlists * sizeof(int32_t));
+  const size_t to = align_up((nlists + 1) * sizeof(int32_t));
+  if (cc + lc + to > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(moba::launch_index(
+      s, idx, kv_begin, kv_count, moba::history_tile_rows(),
+      reinterpret_cast<int32_t*>(ws), reinterpret_cast<int32_t*>(ws + cc), list_offsets,
+      reinterpret_cast<int32_t*>(ws + cc + lc), nullptr, entries,
+      (long long)s.b * kv_count * s.G() * entries_per_head(s),
+      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Internal declarations of libmoba: device helpers shared by the kernels and the
+// host-side launchers that moba_api.hip strings together.  Written for gfx950
+// (CDNA4): 64-lane wavefronts, v_mfma_f32_32x32x16_bf16, 160 KB of LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moba {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // every kernel runs 4 wavefronts per workgroup
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// value held by lane (lane ^ 32)
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  return (uint32_t)__shfl_xor((int)v, 32);
+}
+__device__ __forceinline__ float xor32_f32(float v) {
+  return __uint_as_float(xor32_u32(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace moba
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
+namespace moba {
+
+struct Shape {
+  int b, T, hq, hkv, d, block, topk;
+  int nb() const { return T / block; }
+  int G() const { return hq / hkv; }
+  int KH() const { return topk - 1; }
+};
+
+// (a1) centroid mean-pool
+int pool_splits(const Shape& s);
+hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float* cent,
+                       hipStream_t st);
+// fp32 centroids -> bf16 hi + bf16 lo (c ~= hi + lo to ~2^-17 relative)
+hipError_t launch_centroid_split(const Shape& s, const float* cent, uint16_t* chi,
+                                 uint16_t* clo, hipStream_t st);
+// (a2) gate + top-k
+hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
+                       const uint16_t* clo, int32_t* idx, hipStream_t st);
+// (a3) inverted index over kv-heads [g0, g0 + ng)
+int index_chunks(const Shape& s);
+hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int tile_m,
+                        int32_t* chunk_counts, int32_t* list_count,
+                        int32_t* list_offsets, int32_t* tile_offsets,
+                        int4* tiles, uint32_t* entries, long long cap,
+                        hipStream_t st);
+// (a4) history attention partials, (a5) current block + merge
+hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, float scale, int g0, int ng,
+                               const int4* tiles, const int32_t* tile_count,
+                               int max_tiles, const uint32_t* entries, float* part_o,
+                               float* part_lse, hipStream_t st);
+hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, float scale, int g0, int ng,
+                               float* part_o, float* part_lse, hipStream_t st);
+hipError_t launch_merge(const Shape& s, int g0, int ng, const float* part_o,
+                        const float* part_lse, uint16_t* out, float* lse,
+                        hipStream_t st);
+int history_tile_rows();
+
+}  // namespace moba

@@ -1,0 +1,129 @@
+// Centroid mean-pool: C[b][g][j][:] = mean of the keys of block j of kv-head g
+// ("MoBA: Mixture of Block Attention for Long-Context LLMs", paper summary page,
+// section "Approach": a block is represented by its mean-pooled key).
+//
+// HBM-bound.  A token's keys for all kv-heads are one contiguous row of hkv*d bf16,
+// so a workgroup reads whole rows with 16-byte loads (fully coalesced) and keeps one
+// float32 partial sum per column.  Blocks are split into `splits` token ranges so the
+// grid has enough workgroups; a second pass adds the split partials in a fixed order
+// (deterministic, no atomics) and divides by the token count.
+#include "moba_internal.h"
+
+namespace moba {
+
+__global__ __launch_bounds__(kThreads) void pool_partial_kernel(
+    const uint16_t* __restrict__ k, int T, int cols, int block, int rows_per_split,
+    float* __restrict__ partial) {
+  const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int splits = gridDim.x, nb = gridDim.y;
+  const int W = cols / 8;                    // 16-byte column chunks per row
+  const int R = W >= kThreads ? 1 : kThreads / W;
+  const int tid = threadIdx.x;
+  const int rsub = W >= kThreads ? 0 : tid / W;
+  const int cstart = W >= kThreads ? tid : tid % W;
+  const int cstep = W >= kThreads ? kThreads : W;
+  const int row0 = j * block + s * rows_per_split;
+  const int row1 = min(min(row0 + rows_per_split, (j + 1) * block), T);
+  __shared__ float red[2048];                // R * cols <= 2048 whenever R > 1
+  float* dst = partial + ((size_t)(b * nb + j) * splits + s) * cols;
+
+  for (int cc = cstart; cc < W; cc += cstep) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (rsub < R) {
+      const uint16_t* p = k + ((size_t)b * T + row0 + rsub) * cols + cc * 8;
+      const size_t stride = (size_t)R * cols;
+      for (int row = row0 + rsub; row < row1; row += R, p += stride) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16lo(v[e]);
+          acc[2 * e + 1] += bf16hi(v[e]);
+        }
+      }
+    }
+    if (R == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[cc * 8 + e] = acc[e];
+    } else if (rsub < R) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[rsub * cols + cc * 8 + e] = acc[e];
+    }
+  }
+  if (R > 1) {
+    __syncthreads();
+    for (int c = tid; c < cols; c += kThreads) {
+      float sum = 0.f;
+      for (int r = 0; r < R; ++r) sum += red[r * cols + c];
+      dst[c] = sum;
+    }
+  }
+}
+
+// sum the split partials in order, divide by the block's token count
+__global__ __launch_bounds__(kThreads) void pool_finalize_kernel(
+    const float* __restrict__ partial, int b_, int T, int hkv, int d, int block, int nb,
+    int splits, float* __restrict__ cent) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t total = (size_t)b_ * hkv * nb * d;
+  if (i >= total) return;
+  const int dim = (int)(i % d);
+  const int j = (int)((i / d) % nb);
+  const int g = (int)((i / ((size_t)d * nb)) % hkv);
+  const int b = (int)(i / ((size_t)d * nb * hkv));
+  const int cols = hkv * d;
+  const float* p = partial + ((size_t)(b * nb + j) * splits) * cols + g * d + dim;
+  float sum = 0.f;
+  for (int s = 0; s < splits; ++s) sum += p[(size_t)s * cols];
+  const int n = min(block, T - j * block);
+  cent[i] = sum / (float)n;  // layout [b][hkv][nb][d] == i
+}
+
+__global__ __launch_bounds__(kThreads) void centroid_split_kernel(
+    const float* __restrict__ cent, size_t total, uint16_t* __restrict__ chi,
+    uint16_t* __restrict__ clo) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const float c = cent[i];
+  const uint32_t hi = f32_to_bf16_rne(c);
+  const float rest = c - __uint_as_float(hi << 16);  // exact in float32
+  chi[i] = (uint16_t)hi;
+  clo[i] = (uint16_t)f32_to_bf16_rne(rest);
+}
+
+int pool_splits(const Shape& s) {
+  const int nb = s.nb();
+  int splits = (2048 + s.b * nb - 1) / (s.b * nb);
+  splits = max(1, min(splits, s.block / 16));
+  return splits;
+}
+
+hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float* cent,
+                       hipStream_t st) {
+  const int nb = s.nb();
+  const int splits = pool_splits(s);
+  const int rows_per_split = (s.block + splits - 1) / splits;
+  const int cols = s.hkv * s.d;
+  dim3 grid(splits, nb, s.b);
+  hipLaunchKernelGGL(pool_partial_kernel, grid, dim3(kThreads), 0, st, k, s.T, cols,
+                     s.block, rows_per_split, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t total = (size_t)s.b * s.hkv * nb * s.d;
+  hipLaunchKernelGGL(pool_finalize_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, partial, s.b, s.T, s.hkv, s.d, s.block, nb,
+                     splits, cent);
+  return hipGetLastError();
+}
+
+hipError_t launch_centroid_split(const Shape& s, const float* cent, uint16_t* chi,
+                                 uint16_t* clo, hipStream_t st) {
+  const size_t total = (size_t)s.b * s.hkv * s.nb() * s.d;
+  hipLaunchKernelGGL(centroid_split_kernel,
+                     dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, st, cent, total, chi, clo);
+  return hipGetLastError();
+}
+
+}  // namespace moba

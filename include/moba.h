@@ -1,0 +1,152 @@
+/*
+ * moba.h - C ABI of libmoba.so, the MI355X (gfx950) MoBA prefill forward pass.
+ *
+ * MoBA (Mixture of Block Attention): the keys of a sequence are cut into blocks of
+ * `block` tokens, each block is mean-pooled into a centroid, every query is scored
+ * against the centroids of its causal past by inner product and routed to its top-k
+ * blocks, its own current block always among them, and causal softmax attention runs
+ * over the selected blocks only ("MoBA: Mixture of Block Attention for Long-Context
+ * LLMs", paper summary page on atlas.scime.ai, section "Approach"; MoBA README,
+ * intro bullets "Trainable Block Sparse Attention" and "Parameter-less Gating
+ * Mechanism").  The library splits that attention into the history blocks and the
+ * causal current block and merges the two by log-sum-exp.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers named q, k, v, out, centroids, idx, list_offsets, entries, workspace are
+ * DEVICE pointers (hipMalloc'd or torch CUDA tensors); `stream` is a hipStream_t
+ * (NULL = the default stream).  All device work is enqueued on `stream` and the call
+ * returns without synchronising.  The caller owns every buffer; the library allocates
+ * no device memory and keeps no state between calls, so calls on different streams
+ * with separate buffers may run concurrently.  Calls that share a workspace must be
+ * ordered on one stream.
+ *
+ * Layouts (contiguous, row-major; b = batch, T = seqlen, d = head_dim,
+ * nb = ceil(T / block), G = hq / hkv, query head h reads kv-head h / G):
+ *   q, out       [b, T, hq, d]   bfloat16
+ *   k, v         [b, T, hkv, d]  bfloat16
+ *   lse          [b, hq, T]      float32, natural log of the softmax denominator
+ *   idx          [b, hq, T, topk] int32: the selected blocks of each query in
+ *                ascending order (so the current block is the last valid one), then
+ *                -1 padding when fewer than topk blocks are causal
+ *   centroids    [b, hkv, nb, d] float32
+ *
+ * Supported shapes: head_dim 64 or 128; hq % hkv == 0; block >= 16 and a multiple of
+ * 16; seqlen a multiple of block; 1 <= topk <= 33 (topk counts the current block);
+ * scale finite and > 0; seqlen * G < 2^27.  Anything else returns
+ * MOBA_ERR_UNSUPPORTED or MOBA_ERR_INVALID_ARG before any device work.
+ *
+ * Errors: every check runs on the host before the first launch, so a call that
+ * returns an error has written nothing.  MOBA_ERR_HIP means a launch failed; the
+ * outputs are then undefined.  No entry point aborts or throws.
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOBA_OK = 0,
+  MOBA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, hq % hkv != 0 ... */
+  MOBA_ERR_UNSUPPORTED = -2, /* valid MoBA shape this build does not run */
+  MOBA_ERR_WORKSPACE = -3,   /* workspace smaller than the minimum */
+  MOBA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} moba_status;
+
+/* Validates a problem shape on the host (touches no device).  Returns MOBA_OK,
+ * MOBA_ERR_INVALID_ARG or MOBA_ERR_UNSUPPORTED. */
+int moba_check_args(int batch, int seqlen, int hq, int hkv, int head_dim, int block,
+                    int topk, float scale);
+
+/* Bytes of device workspace moba_forward uses.  Returns the size that processes all
+ * kv-heads in one pass, and stores in *min_bytes (if not NULL) the size that
+ * processes one kv-head per pass.  Any size in between also works: moba_forward
+ * then loops over groups of kv-heads.  Returns 0 if the shape is not supported. */
+size_t moba_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim,
+                            int block, int topk, size_t* min_bytes);
+
+/* The whole prefill forward pass (paper summary page, "Approach"):
+ * centroids -> gate and top-k -> inverted index -> history attention ->
+ * current-block causal attention -> log-sum-exp merge.
+ * Writes out, lse and idx.  `workspace` must hold at least the minimum of
+ * moba_workspace_bytes and be 256-byte aligned. */
+int moba_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
+                 int hq, int hkv, int head_dim, int block, int topk, float scale,
+                 void* out, float* lse, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* moba_forward, then a wait for `stream`, and the GPU time of each step measured with
+ * HIP events recorded on `stream` between the steps, in milliseconds, summed over
+ * kv-head groups:
+ *   stage_ms[0] centroid pool   [1] gate + top-k   [2] inverted index
+ *   stage_ms[3] history attention   [4] current-block attention   [5] merge
+ * stage_ms is a HOST array of MOBA_NUM_STAGES floats.  Meant for measurement: it
+ * synchronises, unlike moba_forward. */
+#define MOBA_NUM_STAGES 6
+int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
+                         int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+                         float scale, void* out, float* lse, int32_t* idx,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         float* stage_ms);
+
+/* A static, human-readable message for a status code. */
+const char* moba_strerror(int status);
+
+/* ---------------------------------------------------------------------------
+ * Stage entry points.  Each runs one step of moba_forward on its own, with the
+ * same kernels, so that every step can be checked separately.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes the stage entry points below need for this shape (the largest of
+ * them); 0 if unsupported. */
+size_t moba_stage_workspace_bytes(int batch, int seqlen, int hq, int hkv,
+                                  int head_dim, int block, int topk);
+
+/* Centroid mean-pool (paper summary page, "Approach": each block is represented by
+ * its mean-pooled key): centroids[b][g][j][:] = mean of k[b, jB .. jB+B-1, g, :],
+ * summed in float32 in a fixed order (deterministic). */
+int moba_pool_centroids(const void* k, int batch, int seqlen, int hkv, int head_dim,
+                        int block, float* centroids, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Gate and top-k (paper summary page, "Approach"; README bullet "Parameter-less
+ * Gating Mechanism"; FlashMoBA story on hyper.ai, paragraph on FlashTopK: the score
+ * matrix is never materialised).  For query (t, h) with c = t / block the score of
+ * block j < c is <q[t,h], centroids[h/G][j]>; the topk-1 best history blocks
+ * (score descending, lower index first on ties) and block c are written to idx.
+ * Rows with c + 1 <= topk take every block 0..c. */
+int moba_gate_topk(const void* q, const float* centroids, int batch, int seqlen,
+                   int hq, int hkv, int head_dim, int block, int topk, int32_t* idx,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of inverted-index entries for kv-heads [kv_begin, kv_begin + kv_count):
+ * every (query row, history slot) pair of their query heads. */
+int64_t moba_index_entries(int batch, int seqlen, int hq, int hkv, int block, int topk,
+                           int kv_count);
+
+/* Inverted index (FlashMoBA story, paragraph on Gather-and-Densify: the queries that
+ * chose a block are gathered together).  For each list (b, g, j), g in
+ * [kv_begin, kv_begin + kv_count), the entries of every query row (t, h) with
+ * h / G == g whose history set holds block j < t / block.
+ *   list_offsets  int32 [batch * kv_count * nb + 1]: list L = (b * kv_count +
+ *                 (g - kv_begin)) * nb + j holds entries[list_offsets[L] ..
+ *                 list_offsets[L + 1]).
+ *   entries       uint32 [moba_index_entries(...)]: ((t * G + h % G) << 5) | slot,
+ *                 slot = the position of j in the row of idx.
+ * Lists are ordered by (chunk of 256 rows, slot, row), rows being r = t * G + h % G:
+ * a deterministic order, identical on every run. */
+int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
+                     int block, int topk, int kv_begin, int kv_count,
+                     int32_t* list_offsets, uint32_t* entries, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H */

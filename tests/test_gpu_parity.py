@@ -1,0 +1,353 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU.
+
+Inputs are the seeded synthetic workloads; the oracle reads the same bf16 values
+widened exactly to float64.  Tolerances are those of tests/parity_util.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import (small_workload, get_workload, make_inputs, bf16_to_f64,
+                       to_torch_bf16)
+from parity_util import (check_selection_row, compare_rows, sample_rows, OUT_MAX,
+                         OUT_MEAN, LSE_MAX)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def moba():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_long_pool_amd as m
+    return m
+
+
+def dev(bits):
+    return to_torch_bf16(bits, "cuda")
+
+
+def run_forward(moba, q, k, v, w, **kw):
+    out, lse, idx = moba.forward(dev(q), dev(k), dev(v), w.block, w.topk, w.sm_scale, **kw)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            idx.cpu().numpy())
+
+
+def full_compare(moba, w, inp=None, label=""):
+    """Every row: idx (exemption rule), out, lse."""
+    if inp is None:
+        inp = make_inputs(w)
+    say(f"[full] {label or w.name}: b={w.batch} T={w.seqlen} hq={w.hq} hkv={w.hkv} "
+        f"d={w.head_dim} B={w.block} k={w.topk}")
+    go, gl, gi = run_forward(moba, inp["q"], inp["k"], inp["v"], w)
+    Q, K, V = (bf16_to_f64(inp[x]) for x in "qkv")
+    rows = [(bi, t, h) for bi in range(w.batch) for t in range(w.seqlen) for h in range(w.hq)]
+    stats = compare_rows(Q, K, V, w.block, w.topk, w.sm_scale, rows,
+                         np.stack([go[bi, t, h] for bi, t, h in rows]),
+                         np.array([gl[bi, h, t] for bi, t, h in rows]),
+                         np.stack([gi[bi, h, t] for bi, t, h in rows]))
+    say(f"       {stats}")
+    return go, gl, gi
+
+
+# ------------------------------------------------------------------------- (a1)
+@pytest.mark.parametrize("b,T,hkv,d,B", [
+    (1, 2048, 1, 64, 128), (2, 4096, 8, 128, 512), (1, 1024, 2, 128, 16),
+    (1, 8192, 8, 128, 4096), (1, 512, 32, 64, 256),
+])
+def test_pool_centroids(moba, b, T, hkv, d, B):
+    w = small_workload("pool", b, hkv, hkv, d, T, B, 1, "offset", seed=T + d)
+    inp = make_inputs(w)
+    say(f"[pool] b={b} T={T} hkv={hkv} d={d} B={B}")
+    c = moba.pool_centroids(dev(inp["k"]), B)
+    torch.cuda.synchronize()
+    ref = oracle.centroids(bf16_to_f64(inp["k"]), B)
+    got = c.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=2e-6, atol=2e-6)
+
+
+def test_pool_constant_blocks_exact(moba):
+    """A block of one constant key has exactly that centroid (power-of-two B)."""
+    b, T, hkv, d, B = 1, 1024, 2, 64, 256
+    k = np.zeros((b, T, hkv, d), np.uint16)
+    vals = np.array([0x3FA0, 0xC040, 0x3E80, 0x4110], np.uint16)   # 1.25, -3, 0.25, 9
+    for j in range(4):
+        k[:, j * B:(j + 1) * B] = vals[j]
+    c = moba.pool_centroids(dev(k), B).cpu().numpy()
+    for j in range(4):
+        assert np.all(c[0, :, j] == bf16_to_f64(vals[j:j + 1])[0])
+
+
+# ------------------------------------------------------------------------- (a2)
+@pytest.mark.parametrize("b,T,hq,hkv,d,B,k,recipe", [
+    (1, 2048, 1, 1, 64, 128, 4, "iid"),          # tiny workload shape
+    (1, 8192, 8, 2, 128, 128, 5, "offset"),       # nb=64: two 32-block tiles
+    (1, 8192, 4, 1, 128, 64, 17, "offset"),       # nb=128, KH=16 fills the 16-list
+    (1, 4096, 4, 4, 64, 32, 20, "iid"),           # KH=19 -> 32-list, nb=128
+    (2, 4096, 16, 2, 128, 16, 33, "iid"),         # B=16 (tiles straddle blocks), k max
+    (1, 16384, 32, 8, 128, 512, 3, "iid"),        # GQA 4
+    (1, 4096, 8, 8, 128, 256, 1, "iid"),          # no history slots
+    (1, 2048, 1, 1, 64, 16, 5, "offset"),         # G=1, B=16: a tile spans two blocks
+])
+def test_gate_topk(moba, b, T, hq, hkv, d, B, k, recipe):
+    w = small_workload("gate", b, hq, hkv, d, T, B, k, recipe, seed=T + k)
+    inp = make_inputs(w)
+    say(f"[gate] b={b} T={T} hq={hq} hkv={hkv} d={d} B={B} k={k}")
+    cent = moba.pool_centroids(dev(inp["k"]), B)
+    idx = moba.gate_topk(dev(inp["q"]), cent, B, k).cpu().numpy()
+    Q, K = bf16_to_f64(inp["q"]), bf16_to_f64(inp["k"])
+    C = oracle.centroids(K, B)
+    ref = oracle.select_blocks(Q, C, B, k)
+    mism = np.argwhere((idx != ref).any(axis=-1))
+    say(f"       rows differing before the near-tie rule: {len(mism)} of {b * hq * T}")
+    exempt = 0
+    for bi, h, t in mism:
+        s = oracle.gate_scores_rows(Q, C, B, [(bi, t, h)])[0]
+        ok, ex, _ = check_selection_row(idx[bi, h, t], s, t // B, k)
+        assert ok, (bi, h, t, idx[bi, h, t].tolist(), ref[bi, h, t].tolist())
+        exempt += ex
+    assert exempt == len(mism)
+
+
+def test_gate_zero_query_ties(moba):
+    """Q = 0: every score is exactly 0 -> lower block indices win, exactly."""
+    b, T, hq, hkv, d, B, k = 1, 4096, 8, 2, 128, 64, 6
+    w = small_workload("z", b, hq, hkv, d, T, B, k, "iid", seed=3)
+    inp = make_inputs(w)
+    q = np.zeros_like(inp["q"])
+    cent = moba.pool_centroids(dev(inp["k"]), B)
+    idx = moba.gate_topk(dev(q), cent, B, k).cpu().numpy()
+    for t in range(0, T, 37):
+        c = t // B
+        exp = list(range(min(k - 1, c))) + [c]
+        exp += [-1] * (k - len(exp))
+        assert (idx[0, :, t] == np.array(exp)).all(), (t, idx[0, :, t])
+
+
+def test_gate_duplicated_block_tie(moba):
+    """Block 3's keys copied into block 9: equal centroids, exact tie -> block 3."""
+    b, T, hq, hkv, d, B, k = 1, 2048, 2, 1, 128, 128, 2
+    w = small_workload("dup", b, hq, hkv, d, T, B, k, "iid", seed=4)
+    inp = make_inputs(w)
+    kk = inp["k"].copy()
+    kk[:, 9 * B:10 * B] = kk[:, 3 * B:4 * B]
+    K = bf16_to_f64(kk)
+    C = oracle.centroids(K, B)
+    qf = np.zeros((b, T, hq, d))
+    qf[:, 10 * B:] = C[0, 0, 3] * 8.0           # aim every later query at block 3
+    from workloads import f32_to_bf16_bits
+    q = f32_to_bf16_bits(qf.astype(np.float32))
+    cent = moba.pool_centroids(dev(kk), B)
+    cc = cent.cpu().numpy()
+    assert np.array_equal(cc[0, 0, 3], cc[0, 0, 9])
+    idx = moba.gate_topk(dev(q), cent, B, k).cpu().numpy()
+    assert np.all(idx[0, :, 10 * B:, 0] == 3)
+
+
+# ------------------------------------------------------------------------- (a3)
+def cpu_index(idx, hkv, B, topk, kv_begin, kv_count, chunk=256):
+    """The documented list order, (chunk of 256 rows, slot, row), built on the CPU."""
+    b, hq, T, _ = idx.shape
+    G = hq // hkv
+    nb = T // B
+    lists = [[] for _ in range(b * kv_count * nb)]
+    for bi in range(b):
+        for gi in range(kv_count):
+            g = kv_begin + gi
+            sub = idx[bi, g * G:(g + 1) * G]                     # [G, T, topk]
+            rows = sub.transpose(1, 0, 2).reshape(T * G, topk)   # row r = t*G + hl
+            c = (np.arange(T * G) // G) // B
+            for c0 in range(0, T * G, chunk):
+                for s in range(topk - 1):
+                    js = rows[c0:c0 + chunk, s]
+                    cs = c[c0:c0 + chunk]
+                    for rr in np.nonzero((js >= 0) & (js < cs))[0]:
+                        r = c0 + rr
+                        lists[(bi * kv_count + gi) * nb + js[rr]].append((r << 5) | s)
+    offs = np.zeros(len(lists) + 1, np.int64)
+    offs[1:] = np.cumsum([len(x) for x in lists])
+    ent = np.array([e for x in lists for e in x], np.int64)
+    return offs, ent
+
+
+@pytest.mark.parametrize("b,T,hq,hkv,B,k,kv_begin,kv_count", [
+    (1, 4096, 8, 2, 256, 4, 0, 2),
+    (2, 2048, 4, 1, 64, 9, 0, 1),
+    (1, 8192, 32, 8, 512, 3, 3, 4),
+    (1, 2048, 4, 4, 16, 33, 1, 2),
+])
+def test_inverted_index(moba, b, T, hq, hkv, B, k, kv_begin, kv_count):
+    w = small_workload("idx", b, hq, hkv, 64, T, B, k, "iid", seed=B + k)
+    inp = make_inputs(w)
+    say(f"[index] b={b} T={T} hq={hq} hkv={hkv} B={B} k={k} kv=[{kv_begin},+{kv_count})")
+    cent = moba.pool_centroids(dev(inp["k"]), B)
+    idx_t = moba.gate_topk(dev(inp["q"]), cent, B, k)
+    offs, ent = moba.build_index(idx_t, hkv, B, k, kv_begin, kv_count)
+    offs2, ent2 = moba.build_index(idx_t, hkv, B, k, kv_begin, kv_count)
+    torch.cuda.synchronize()
+    assert torch.equal(offs, offs2) and torch.equal(ent, ent2)        # deterministic
+    ref_offs, ref_ent = cpu_index(idx_t.cpu().numpy(), hkv, B, k, kv_begin, kv_count)
+    assert np.array_equal(offs.cpu().numpy().astype(np.int64), ref_offs)
+    assert np.array_equal(ent.cpu().numpy().astype(np.int64) & 0xFFFFFFFF, ref_ent)
+
+
+# ------------------------------------------------------------------------- (a4, a5)
+SMALL = [
+    # name, b, hq, hkv, d, T, B, k, recipe
+    ("tiny_2k", None),
+    ("gqa4_d128", small_workload("gqa4_d128", 1, 8, 2, 128, 4096, 256, 4, "offset", 7)),
+    ("b2_d64", small_workload("b2_d64", 2, 4, 2, 64, 2048, 128, 5, "iid", 8)),
+    ("blk16_k33", small_workload("blk16_k33", 1, 2, 1, 128, 1024, 16, 33, "iid", 9)),
+    ("blk48", small_workload("blk48", 1, 4, 1, 64, 1536, 48, 3, "offset", 10)),
+    ("g8", small_workload("g8", 1, 16, 2, 128, 2048, 128, 6, "iid", 11)),
+    ("topk1", small_workload("topk1", 1, 4, 2, 128, 2048, 256, 1, "iid", 12)),
+    ("dense", small_workload("dense", 1, 4, 1, 64, 1024, 128, 8, "iid", 13)),
+    ("k_over_nb", small_workload("k_over_nb", 1, 2, 2, 128, 768, 256, 9, "iid", 14)),
+]
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[s[0] for s in SMALL])
+def test_forward_small_all_rows(moba, name, w):
+    if w is None:
+        w = get_workload(name)
+    full_compare(moba, w)
+
+
+def test_forward_dense_equals_sdpa(moba):
+    """topk >= nb: the GPU result is full causal attention (torch SDPA, fp32 CPU)."""
+    w = small_workload("dense", 1, 4, 2, 128, 2048, 256, 8, "iid", 15)
+    inp = make_inputs(w)
+    go, gl, gi = run_forward(moba, inp["q"], inp["k"], inp["v"], w)
+    q, k, v = (torch.from_numpy(bf16_to_f64(inp[x])).float().permute(0, 2, 1, 3)
+               for x in "qkv")
+    k = k.repeat_interleave(2, dim=1)
+    v = v.repeat_interleave(2, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                           scale=w.sm_scale)
+    ref = ref.permute(0, 2, 1, 3).double().numpy()
+    d = np.abs(go - ref)
+    assert d.max() <= OUT_MAX and d.mean() <= OUT_MEAN
+
+
+def test_forward_zero_query_closed_form(moba):
+    """Q = 0: uniform attention, lse = ln|N| and out = mean of V over N."""
+    w = small_workload("zq", 1, 4, 2, 128, 2048, 128, 4, "iid", 16)
+    inp = make_inputs(w)
+    q = np.zeros_like(inp["q"])
+    go, gl, gi = run_forward(moba, q, inp["k"], inp["v"], w)
+    V = bf16_to_f64(inp["v"])
+    B, k = w.block, w.topk
+    for t in range(0, w.seqlen, 13):
+        c = t // B
+        S = list(range(min(k - 1, c))) + [c]
+        n = (len(S) - 1) * B + (t - c * B + 1)
+        for h in range(w.hq):
+            assert gi[0, h, t, :len(S)].tolist() == S
+            assert abs(gl[0, h, t] - math.log(n)) <= LSE_MAX
+            keys = oracle.attended_keys(S, t, B, w.seqlen)
+            assert np.abs(go[0, t, h] - V[0, keys, h // 2].mean(0)).max() <= OUT_MAX
+
+
+def test_forward_constant_values(moba):
+    w = small_workload("cv", 1, 4, 1, 64, 1024, 64, 3, "iid", 17)
+    inp = make_inputs(w)
+    v = np.full_like(inp["v"], 0x3FC0)        # 1.5
+    go, _, _ = run_forward(moba, inp["q"], inp["k"], v, w)
+    assert np.abs(go - 1.5).max() <= 1e-2
+
+
+def test_forward_block_indicator_values(moba):
+    """V[u] = e_blk(u): the output is the attention mass per block; it is nonzero
+    exactly on the selected blocks and sums to 1 (routing seen through attention)."""
+    w = small_workload("ind", 1, 4, 1, 64, 2048, 64, 4, "offset", 18)
+    inp = make_inputs(w)
+    nb = w.seqlen // w.block
+    v = np.zeros_like(inp["v"])
+    v[0, np.arange(w.seqlen), 0, np.arange(w.seqlen) // w.block] = 0x3F80   # 1.0
+    go, _, gi = run_forward(moba, inp["q"], inp["k"], v, w)
+    for h in range(w.hq):
+        for t in range(0, w.seqlen, 7):
+            S = set(gi[0, h, t][gi[0, h, t] >= 0].tolist())
+            nz = set(np.nonzero(go[0, t, h, :nb] > 0)[0].tolist())
+            assert nz == S, (h, t, S, nz)
+            assert abs(go[0, t, h].sum() - 1) < 2e-2
+
+
+def test_forward_deterministic_and_chunked(moba):
+    """Bitwise identical across runs, and when the workspace only fits one kv-head."""
+    w = small_workload("det", 1, 16, 4, 128, 4096, 256, 5, "offset", 19)
+    inp = make_inputs(w)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    a = moba.forward(q, k, v, w.block, w.topk)
+    b = moba.forward(q, k, v, w.block, w.topk)
+    full, mn = moba.workspace_bytes(1, 4096, 16, 4, 128, 256, 5)
+    ws = torch.empty(mn, dtype=torch.uint8, device="cuda")
+    c = moba.forward(q, k, v, w.block, w.topk, workspace=ws)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y) and torch.equal(x, z)
+
+
+def test_forward_rejects_small_workspace(moba):
+    w = small_workload("ws", 1, 4, 2, 64, 1024, 128, 3, "iid", 20)
+    inp = make_inputs(w)
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moba.MobaError):
+        moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.block, w.topk,
+                     workspace=ws)
+
+
+# ------------------------------------------------------------------------- full sizes
+def big_compare(moba, name, per_block, seed):
+    w = get_workload(name)
+    say(f"[big] {name}: generating inputs")
+    inp = make_inputs(w)
+    say(f"[big] {name}: running the GPU path")
+    go_t, gl_t, gi_t = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.block,
+                                    w.topk, w.sm_scale)
+    torch.cuda.synchronize()
+    gi = gi_t.cpu().numpy()
+    Q, K, V = (bf16_to_f64(inp[x]) for x in "qkv")
+    C = oracle.centroids(K, w.block)
+    say(f"[big] {name}: oracle selection for every row")
+    ref = oracle.select_blocks(Q, C, w.block, w.topk)
+    mism = np.argwhere((gi != ref).any(axis=-1))
+    exempt = 0
+    for bi, h, t in mism:
+        s = oracle.gate_scores_rows(Q, C, w.block, [(bi, t, h)])[0]
+        ok, ex, _ = check_selection_row(gi[bi, h, t], s, t // w.block, w.topk)
+        assert ok, (bi, h, t, gi[bi, h, t].tolist(), ref[bi, h, t].tolist())
+        exempt += ex
+    say(f"[big] {name}: {len(mism)} rows differ, all within the near-tie rule "
+        f"({exempt} exempt of {gi.shape[1] * gi.shape[2]})")
+    rows = sample_rows(w.batch, w.seqlen, w.hq, w.block, per_block=per_block, seed=seed,
+                       extra=[(0, w.seqlen - 1, w.hq - 1), (0, 0, 0)])
+    bi_, t_, h_ = (np.array(x) for x in zip(*rows))
+    ib, it, ih = (torch.as_tensor(x, device="cuda") for x in (bi_, t_, h_))
+    go = go_t[ib, it, ih].float().cpu().numpy()
+    gl = gl_t[ib, ih, it].cpu().numpy()
+    stats = compare_rows(Q, K, V, w.block, w.topk, w.sm_scale, rows, go, gl,
+                         gi[bi_, h_, t_], C=C)
+    say(f"[big] {name}: {stats}")
+
+
+def test_llama8b_32k(moba):
+    big_compare(moba, "llama8b_32k", per_block=6, seed=2)
+
+
+def test_llama8b_128k(moba):
+    big_compare(moba, "llama8b_128k", per_block=12, seed=3)
+
+
+def test_llama8b_64k_b128(moba):
+    big_compare(moba, "llama8b_64k_b128", per_block=1, seed=4)

@@ -224,7 +224,9 @@ def _planted_queries(w: Workload, kb: np.ndarray):
             valid = P >= 0
             cnt = valid.sum(axis=1)
             Pc = np.where(valid, P, 0)
-            m = (bm[bi, Pc, g, :] * valid[..., None]).sum(axis=1)   # [T, d]
+            m = np.zeros((T, d))
+            for p in range(8):
+                m += bm[bi, Pc[:, p], g, :] * valid[:, p, None]
             m /= np.maximum(cnt, 1)[:, None]
             nrm = np.linalg.norm(m, axis=1)
             dirn = np.where((cnt > 0)[:, None], math.sqrt(d) * m / np.maximum(nrm, 1e-30)[:, None], 0.0)
