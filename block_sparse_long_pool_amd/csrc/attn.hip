@@ -23,7 +23,16 @@
 
 namespace moba {
 
-constexpr int KN = 64;  // keys per LDS subtile
+// query rows per wavefront = 32 * QT; waves per SIMD the compiler budgets for
+#ifndef MOBA_ATTN_QT
+#define MOBA_ATTN_QT 1
+#endif
+#ifndef MOBA_ATTN_WPE
+#define MOBA_ATTN_WPE 2
+#endif
+
+constexpr int KN = 64;          // keys per LDS subtile
+constexpr float kTau = 8.f;     // lazy rescale: the reference max may lag by 2^8
 
 template <int D>
 __device__ __forceinline__ int k_lds_off(int key, int chunk) {
@@ -40,43 +49,71 @@ struct WaveState {
   float m[QT], l[QT];
 };
 
-// keys [key0, key0 + nvalid) of kv-head row stride `rs` -> LDS (zeros past nvalid)
+// one subtile of K and V in flight through registers (global -> regs -> LDS)
 template <int D>
-__device__ __forceinline__ void stage_kv(char* lk, char* lv, const uint16_t* __restrict__ kp,
-                                         const uint16_t* __restrict__ vp, size_t rs,
-                                         int nvalid) {
-  constexpr int CPR = D / 8;
+struct KVRegs {
+  static constexpr int CPR = D / 8;                                  // 16 B chunks per row
+  static constexpr int NKC = (KN * CPR + kThreads - 1) / kThreads;   // K chunks per thread
+  static constexpr int NVC = ((KN / 4) * CPR + kThreads - 1) / kThreads;
+  u32x4_t k[NKC];
+  u32x4_t v[NVC][4];
+};
+
+// keys [0, nvalid) of a subtile; kp/vp point at its first key, rs = row stride.
+// Rows past nvalid re-read row nvalid-1: those keys are masked (score -inf, p = 0), so
+// their values only need to be finite, and the loads stay branch-free.
+template <int D>
+__device__ __forceinline__ void kv_load(KVRegs<D>& r, const uint16_t* __restrict__ kp,
+                                        const uint16_t* __restrict__ vp, size_t rs,
+                                        int nvalid) {
+  using R = KVRegs<D>;
   const int tid = threadIdx.x;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int ci = tid; ci < KN * CPR; ci += kThreads) {
-    const int key = ci / CPR, ch = ci % CPR;
-    u32x4_t x = zero;
-    if (key < nvalid) x = *reinterpret_cast<const u32x4_t*>(kp + key * rs + ch * 8);
-    *reinterpret_cast<u32x4_t*>(lk + k_lds_off<D>(key, ch)) = x;
+  for (int i = 0; i < R::NKC; ++i) {
+    const int ci = min(tid + i * kThreads, KN * R::CPR - 1);
+    const int key = min(ci / R::CPR, nvalid - 1), ch = ci % R::CPR;
+    r.k[i] = *reinterpret_cast<const u32x4_t*>(kp + key * rs + ch * 8);
   }
 #pragma unroll
-  for (int combo = tid; combo < (KN / 4) * CPR; combo += kThreads) {
-    const int kq = combo / CPR, dc = combo % CPR;
-    u32x4_t rows[4];
+  for (int i = 0; i < R::NVC; ++i) {
+    const int combo = min(tid + i * kThreads, (KN / 4) * R::CPR - 1);
+    const int kq = combo / R::CPR, dc = combo % R::CPR;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int key = 4 * kq + e;
-      rows[e] = zero;
-      if (key < nvalid) rows[e] = *reinterpret_cast<const u32x4_t*>(vp + key * rs + dc * 8);
+      const int key = min(4 * kq + e, nvalid - 1);
+      r.v[i][e] = *reinterpret_cast<const u32x4_t*>(vp + key * rs + dc * 8);
     }
-    // keys 4kq..4kq+3 sit at permuted positions pos..pos+3 of their 16-key group:
-    // groups of four keys are stored in the order 0, 2, 1, 3
+  }
+}
+
+// K rows as they are (16-byte chunks XOR-swizzled by key); V transposed to [dim][key]
+// with each 16-key group stored in the order 0-3, 8-11, 4-7, 12-15, which is the
+// order the score registers hold the keys in (so P^T needs no shuffle).
+template <int D>
+__device__ __forceinline__ void kv_store(const KVRegs<D>& r, char* lk, char* lv) {
+  using R = KVRegs<D>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < R::NKC; ++i) {
+    const int ci = tid + i * kThreads;
+    const int key = ci / R::CPR, ch = ci % R::CPR;
+    if (ci < KN * R::CPR) *reinterpret_cast<u32x4_t*>(lk + k_lds_off<D>(key, ch)) = r.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < R::NVC; ++i) {
+    const int combo = tid + i * kThreads;
+    if (combo >= (KN / 4) * R::CPR) continue;
+    const int kq = combo / R::CPR, dc = combo % R::CPR;
     const int grp = kq & 3;
     const int pos = (kq >> 2) * 16 + (((grp & 1) << 1) | (grp >> 1)) * 4;
     const int chunk = pos >> 3, sub = (pos & 7) * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(rows[1][i], rows[0][i], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(rows[3][i], rows[2][i], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(rows[1][i], rows[0][i], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(rows[3][i], rows[2][i], 0x07060302u);
-      const int dim = dc * 8 + 2 * i;
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo01 = __builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x07060302u);
+      const int dim = dc * 8 + 2 * w;
       *reinterpret_cast<u32x2_t*>(lv + v_lds_off(dim, chunk) + sub) = u32x2_t{lo01, lo23};
       *reinterpret_cast<u32x2_t*>(lv + v_lds_off(dim + 1, chunk) + sub) = u32x2_t{hi01, hi23};
     }
@@ -96,91 +133,148 @@ __device__ __forceinline__ void state_init(WaveState<D, QT>& st) {
   }
 }
 
-// one 64-key subtile staged in LDS.  nkeys: valid keys; causal: mask key > tpos.
-template <int D, int QT>
-__device__ __forceinline__ void attend_subtile(WaveState<D, QT>& st, const char* lk,
-                                               const char* lv, float sl, int nkeys,
-                                               bool causal, int kb, const int (&tpos)[QT]) {
+// 32 keys (half kk of a 64-key subtile staged in LDS) for every query row of the wave.
+// MASK: key rows >= nkeys and keys > tpos (causal) score -inf.  Lazy rescale: the
+// reference max m moves only when a row's max exceeds it by more than kTau (O and l are
+// rescaled then), so p = exp2(s * scale * log2e - m) <= 2^kTau.
+template <int D, int QT, bool MASK>
+__device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk,
+                                            const char* lv, int kk, float sl, int nkeys,
+                                            int kb, const int (&tpos)[QT]) {
   const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  f32x16_t s[2][QT];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kk][qt][i] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8_t a = as_bf16x8(
-          *reinterpret_cast<const u32x4_t*>(lk + k_lds_off<D>(kk * 32 + n, 2 * ks + hf)));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[kk][qt] = mfma32x32x16(a, st.q[qt][ks], s[kk][qt]);
-    }
-  }
-  const bool need_mask = causal || nkeys < KN;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    if (need_mask) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kr = kk * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          const bool ok = kr < nkeys && (!causal || kb + kr <= tpos[qt]);
-          if (!ok) s[kk][qt][i] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][qt][i]);
-    mx = fmaxf(mx, xor32_f32(mx));
-    const float mnew = fmaxf(st.m[qt], mx * sl);
-    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - mref);
-    float rs = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][qt][i], sl, -mref));
-        s[kk][qt][i] = p;
-        rs += p;
-      }
-    st.l[qt] = st.l[qt] * alpha + rs;
-    st.m[qt] = mnew;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[qt][dt][i] *= alpha;
-  }
-  bf16x8_t pb[QT][4];
+  f32x16_t s[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f32x16_t& v = s[ks >> 1][qt];
-      const int o = 8 * (ks & 1);
-      u32x4_t w;
-      w[0] = pack_bf16x2(v[o + 0], v[o + 1]);
-      w[1] = pack_bf16x2(v[o + 2], v[o + 3]);
-      w[2] = pack_bf16x2(v[o + 4], v[o + 5]);
-      w[3] = pack_bf16x2(v[o + 6], v[o + 7]);
-      pb[qt][ks] = as_bf16x8(w);
+    for (int i = 0; i < 16; ++i) s[qt][i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8_t a = as_bf16x8(
+        *reinterpret_cast<const u32x4_t*>(lk + k_lds_off<D>(kk * 32 + n, 2 * ks + hf)));
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) s[qt] = mfma32x32x16(a, st.q[qt][ks], s[qt]);
+  }
+  float mxs[QT];
+  bool need = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    if (MASK) {
+      // key kb + kk*32 + (i/4)*8 + hf*4 + i%4 is live iff its row < nkeys and key <= tpos
+      const int lim = min(nkeys - 1, tpos[qt] - kb) - kk * 32 - hf * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + (i & 3) > lim) s[qt][i] = -INFINITY;
     }
+    float mx = s[qt][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qt][i]);
+    mx = fmaxf(mx, xor32_f32(mx));
+    mxs[qt] = mx * sl;
+    need |= mxs[qt] > st.m[qt] + kTau;
+  }
+  if (__ballot(need) != 0ull) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mnew = fmaxf(st.m[qt], mxs[qt]);
+      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(st.m[qt] - mnew);
+      st.m[qt] = mnew;
+      st.l[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[qt][dt][i] *= alpha;
+    }
+  }
+  bf16x8_t pb[QT][2];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float mref = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], sl, -mref));
+      s[qt][i] = p;
+      rs += p;
+    }
+    st.l[qt] += rs;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t w;
+      w[0] = pack_bf16x2(s[qt][8 * h + 0], s[qt][8 * h + 1]);
+      w[1] = pack_bf16x2(s[qt][8 * h + 2], s[qt][8 * h + 3]);
+      w[2] = pack_bf16x2(s[qt][8 * h + 4], s[qt][8 * h + 5]);
+      w[3] = pack_bf16x2(s[qt][8 * h + 6], s[qt][8 * h + 7]);
+      pb[qt][h] = as_bf16x8(w);
+    }
+  }
+  // P^T for MFMA k-step (2*kk + h) is the score registers 8h .. 8h+7 of this half
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t a = as_bf16x8(
-          *reinterpret_cast<const u32x4_t*>(lv + v_lds_off(dt * 32 + n, 2 * ks + hf)));
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+          lv + v_lds_off(dt * 32 + n, 2 * (2 * kk + h) + hf)));
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][ks], st.o[qt][dt]);
+      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][h], st.o[qt][dt]);
     }
   }
+}
+
+// Subtiles [i0, i1) of the key range starting at key_begin, staged through two LDS
+// buffers: the next subtile's global loads are in flight while the current one is
+// computed, then written to the other buffer; one barrier per subtile.  On entry the
+// subtile i0 is already in buffer i0 & 1.
+template <int D, int QT, bool MASK>
+__device__ __forceinline__ void attend_subtiles(WaveState<D, QT>& st, char* lds,
+                                                KVRegs<D>& r, const uint16_t* __restrict__ kbase,
+                                                const uint16_t* __restrict__ vbase, size_t rs,
+                                                int key_begin, int key_end, int i0, int i1,
+                                                int nsub, float sl, bool active,
+                                                const int (&tpos)[QT]) {
+  constexpr int TILE = KN * D * 2;  // bytes of one K (or V) subtile
+  for (int i = i0; i < i1; ++i) {
+    const int kb = key_begin + i * KN;
+    const bool more = i + 1 < nsub;
+    if (more)
+      kv_load<D>(r, kbase + (size_t)(kb + KN) * rs, vbase + (size_t)(kb + KN) * rs, rs,
+                 min(KN, key_end - kb - KN));
+    const char* cur = lds + (i & 1) * 2 * TILE;
+    if (active) {
+      const int nvalid = min(KN, key_end - kb);
+      attend_half<D, QT, MASK>(st, cur, cur + TILE, 0, sl, nvalid, kb, tpos);
+      attend_half<D, QT, MASK>(st, cur, cur + TILE, 1, sl, nvalid, kb, tpos);
+    }
+    if (more) {
+      char* nxt = lds + ((i + 1) & 1) * 2 * TILE;
+      kv_store<D>(r, nxt, nxt + TILE);
+    }
+    __syncthreads();
+  }
+}
+
+// The wave's rows over keys [key_begin, key_end) of one kv-head.  Subtiles whose last
+// key exceeds diag_from (the smallest query position of the workgroup) or key_end need
+// the mask; they come last and run in their own loop.
+template <int D, int QT>
+__device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
+                                             const uint16_t* __restrict__ kbase,
+                                             const uint16_t* __restrict__ vbase, size_t rs,
+                                             int key_begin, int key_end, float sl,
+                                             bool active, int diag_from, const int (&tpos)[QT]) {
+  constexpr int TILE = KN * D * 2;
+  KVRegs<D> r;
+  const int nsub = (key_end - key_begin + KN - 1) / KN;
+  // subtile i is mask-free iff key_begin + (i+1)*KN <= min(key_end, diag_from + 1)
+  const int lim = min(key_end, diag_from == 0x7fffffff ? key_end : diag_from + 1);
+  const int nplain = max(0, min(nsub, (lim - key_begin) / KN));
+  kv_load<D>(r, kbase + (size_t)key_begin * rs, vbase + (size_t)key_begin * rs, rs,
+             min(KN, key_end - key_begin));
+  kv_store<D>(r, lds, lds + TILE);
+  __syncthreads();
+  attend_subtiles<D, QT, false>(st, lds, r, kbase, vbase, rs, key_begin, key_end, 0, nplain,
+                                nsub, sl, active, tpos);
+  attend_subtiles<D, QT, true>(st, lds, r, kbase, vbase, rs, key_begin, key_end, nplain, nsub,
+                               nsub, sl, active, tpos);
 }
 
 // normalise and store one query tile's partial (o fp32 [D], lse natural log)
@@ -216,15 +310,15 @@ __device__ __forceinline__ void load_q(WaveState<D, QT>& st, int qt, const uint1
 }
 
 // ---------------------------------------------------------------- history (a4)
+// One workgroup = one tile of up to 4 * 32 * QT gathered rows of one list (b, g, j).
 template <int D, int QT>
-__global__ __launch_bounds__(kThreads) void attn_history_kernel(
+__global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_history_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char lk[KN * D * 2];
-  __shared__ __attribute__((aligned(16))) char lv[D * KN * 2];
+  __shared__ __attribute__((aligned(16))) char lds[4 * KN * D * 2];
   const int tile_id = blockIdx.x;
   if (tile_id >= *tile_count) return;
   const int4 tl = tiles[tile_id];
@@ -234,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void attn_history_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
 
   WaveState<D, QT> st;
-  int tq[QT], hlq[QT], slq[QT];
+  int tq[QT], hlq[QT], slq[QT], tpos[QT];
   bool vq[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -245,22 +339,17 @@ __global__ __launch_bounds__(kThreads) void attn_history_kernel(
     const int rr = (int)(ent >> 5);
     tq[qt] = rr / G;
     hlq[qt] = rr % G;
+    tpos[qt] = 0x7fffffff;    // history keys all precede the query
     const uint16_t* qrow = q + ((size_t)((size_t)b * T + tq[qt]) * hq + g * G + hlq[qt]) * D;
     load_q(st, qt, qrow, vq[qt]);
   }
   state_init(st);
   const size_t rs = (size_t)hkv * D;
-  const int key_begin = j * block, key_end = key_begin + block;
   const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
-  const int dummy[QT] = {};
-  for (int kb = key_begin; kb < key_end; kb += KN) {
-    const int nvalid = min(KN, key_end - kb);
-    __syncthreads();
-    stage_kv<D>(lk, lv, kbase + (size_t)kb * rs, vbase + (size_t)kb * rs, rs, nvalid);
-    __syncthreads();
-    attend_subtile<D, QT>(st, lk, lv, sl, nvalid, false, kb, dummy);
-  }
+  const int key_begin = j * block;
+  attend_range<D, QT>(st, lds, kbase, vbase, rs, key_begin, key_begin + block, sl, true,
+                      0x7fffffff, tpos);
   const int ngq = ng * G;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -270,26 +359,27 @@ __global__ __launch_bounds__(kThreads) void attn_history_kernel(
 }
 
 // ---------------------------------------------------------------- current (a5)
-// workgroup: 32*QT consecutive tokens of block c, waves = query heads of kv-head g
+// One workgroup = 32*QT consecutive tokens of block c; its waves are the query heads
+// of kv-head g (in rounds of four), so all four share every staged K/V subtile.
+// Tiles run from the end of the block backwards: the longest ones start first.
 template <int D, int QT>
-__global__ __launch_bounds__(kThreads) void attn_current_kernel(
+__global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_current_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char lk[KN * D * 2];
-  __shared__ __attribute__((aligned(16))) char lv[D * KN * 2];
+  __shared__ __attribute__((aligned(16))) char lds[4 * KN * D * 2];
   constexpr int TT = 32 * QT;
   const int c = blockIdx.y;
   const int gi = blockIdx.z % ng, b = blockIdx.z / ng;
   const int G = hq / hkv, g = g0 + gi;
-  const int t0 = c * block + blockIdx.x * TT;
+  const int x = gridDim.x - 1 - blockIdx.x;
+  const int t0 = c * block + x * TT;
   const int t_end = min(t0 + TT, (c + 1) * block);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
   const size_t rs = (size_t)hkv * D;
   const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
   const int ngq = ng * G;
-  const int key_begin = c * block;
   for (int round = 0; round * 4 < G; ++round) {
     const int hl = round * 4 + wave;
     const bool active = hl < G;
@@ -300,21 +390,12 @@ __global__ __launch_bounds__(kThreads) void attn_current_kernel(
     for (int qt = 0; qt < QT; ++qt) {
       tpos[qt] = t0 + qt * 32 + n;
       vq[qt] = active && tpos[qt] < t_end;
-      const uint16_t* qrow =
-          q + ((size_t)((size_t)b * T + (vq[qt] ? tpos[qt] : 0)) * hq + g * G + (active ? hl : 0)) * D;
+      const uint16_t* qrow = q + ((size_t)((size_t)b * T + (vq[qt] ? tpos[qt] : 0)) * hq +
+                                  g * G + (active ? hl : 0)) * D;
       load_q(st, qt, qrow, vq[qt]);
     }
     state_init(st);
-    for (int kb = key_begin; kb < t_end; kb += KN) {
-      const int nvalid = min(KN, t_end - kb);
-      __syncthreads();
-      stage_kv<D>(lk, lv, kbase + (size_t)kb * rs, vbase + (size_t)kb * rs, rs, nvalid);
-      __syncthreads();
-      if (active) {
-        const bool diag = kb + KN - 1 > t0;
-        attend_subtile<D, QT>(st, lk, lv, sl, nvalid, diag, kb, tpos);
-      }
-    }
+    attend_range<D, QT>(st, lds, kbase, vbase, rs, c * block, t_end, sl, active, t0, tpos);
     if (active) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
@@ -373,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-constexpr int kQT = 1;
+constexpr int kQT = MOBA_ATTN_QT;
 int history_tile_rows() { return 4 * 32 * kQT; }
 
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
