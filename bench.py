@@ -127,6 +127,9 @@ def main(argv=None):
                     help="extra steps timed per stage (default: --steps)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one elementwise copy (torch.neg) of this many MiB "
+                         "of bf16, a kernel of known traffic for scaling HBM counters")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +178,17 @@ def main(argv=None):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
+
+    if a.calibration_copy_mib:
+        n = a.calibration_copy_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)          # reads n*2 bytes, writes n*2 bytes
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {n * 2} bytes read, {n * 2} bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     n_prof = a.steps if a.profile_steps is None else a.profile_steps
     stage = {s: 0.0 for s in moba.STAGES}

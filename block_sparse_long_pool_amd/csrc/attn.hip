@@ -15,9 +15,13 @@
 //            each 32-key half, so the softmax of a query lives in two lanes
 //            (l, l^32) and its running max/sum/scale are per-lane scalars.
 //   output   O^T[dim][query] = V^T P^T: B = P^T straight from the score registers
-//            (converted to bf16), A = V^T from LDS.  V is transposed while it is
-//            staged, with the keys of each 16-key group stored in the order the
-//            score registers hold them, so no register shuffle is needed.
+//            (converted to bf16), A = V^T read from the row-major V tile with the
+//            gfx950 LDS transpose read (ds_read_b64_tr_b16), whose key order is
+//            chosen to match the order the score registers hold the keys in, so no
+//            register shuffle and no transpose while staging are needed.
+// K and V tiles are row-major in LDS with padded rows (K: +16 B, V: +32 B), which
+// spreads the MFMA operand reads over all banks and lets every read use a per-lane
+// base address plus an immediate offset.
 // Online softmax in the log2 domain (scale * log2(e) folded into one FMA).
 #include "moba_internal.h"
 
@@ -35,12 +39,13 @@ constexpr int KN = 64;          // keys per LDS subtile
 constexpr float kTau = 8.f;     // lazy rescale: the reference max may lag by 2^8
 
 template <int D>
-__device__ __forceinline__ int k_lds_off(int key, int chunk) {
-  return key * (D * 2) + ((chunk ^ (key & 7)) << 4);
-}
-__device__ __forceinline__ int v_lds_off(int dim, int chunk) {
-  return dim * (KN * 2) + ((chunk ^ ((dim ^ (dim >> 3)) & 7)) << 4);
-}
+struct Lds {
+  static constexpr int KS = D * 2 + 16;          // K row stride (bytes)
+  static constexpr int VS = D * 2 + 32;          // V row stride (bytes)
+  static constexpr int KBYTES = KN * KS;
+  static constexpr int VBYTES = KN * VS;
+  static constexpr int STAGE = KBYTES + VBYTES;  // one K + V subtile
+};
 
 template <int D, int QT>
 struct WaveState {
@@ -53,71 +58,99 @@ struct WaveState {
 template <int D>
 struct KVRegs {
   static constexpr int CPR = D / 8;                                  // 16 B chunks per row
-  static constexpr int NKC = (KN * CPR + kThreads - 1) / kThreads;   // K chunks per thread
-  static constexpr int NVC = ((KN / 4) * CPR + kThreads - 1) / kThreads;
-  u32x4_t k[NKC];
-  u32x4_t v[NVC][4];
+  static constexpr int NC = (KN * CPR + kThreads - 1) / kThreads;    // chunks per thread
+  u32x4_t k[NC];
+  u32x4_t v[NC];
 };
 
-// keys [0, nvalid) of a subtile; kp/vp point at its first key, rs = row stride.
-// Rows past nvalid re-read row nvalid-1: those keys are masked (score -inf, p = 0), so
-// their values only need to be finite, and the loads stay branch-free.
+// Per-thread element offsets of the 16-byte chunks a thread stages, relative to the
+// subtile's first key (row stride rs); computed once per kernel.
 template <int D>
-__device__ __forceinline__ void kv_load(KVRegs<D>& r, const uint16_t* __restrict__ kp,
-                                        const uint16_t* __restrict__ vp, size_t rs,
-                                        int nvalid) {
-  using R = KVRegs<D>;
-  const int tid = threadIdx.x;
+struct KVOffsets {
+  uint32_t off[KVRegs<D>::NC];
+  __device__ __forceinline__ void init(size_t rs) {
+    using R = KVRegs<D>;
 #pragma unroll
-  for (int i = 0; i < R::NKC; ++i) {
-    const int ci = min(tid + i * kThreads, KN * R::CPR - 1);
+    for (int i = 0; i < R::NC; ++i) {
+      const int ci = min((int)threadIdx.x + i * kThreads, KN * R::CPR - 1);
+      off[i] = (uint32_t)((ci / R::CPR) * rs + (ci % R::CPR) * 8);
+    }
+  }
+};
+
+// A full subtile: kp/vp point at its first key.
+template <int D>
+__device__ __forceinline__ void kv_load(KVRegs<D>& r, const KVOffsets<D>& o,
+                                        const uint16_t* __restrict__ kp,
+                                        const uint16_t* __restrict__ vp) {
+#pragma unroll
+  for (int i = 0; i < KVRegs<D>::NC; ++i) {
+    r.k[i] = *reinterpret_cast<const u32x4_t*>(kp + o.off[i]);
+    r.v[i] = *reinterpret_cast<const u32x4_t*>(vp + o.off[i]);
+  }
+}
+
+// A partial subtile of nvalid keys.  Rows past nvalid re-read row nvalid-1: those keys
+// are masked (score -inf, p = 0), so their values only need to be finite.
+template <int D>
+__device__ __forceinline__ void kv_load_partial(KVRegs<D>& r, const uint16_t* __restrict__ kp,
+                                                const uint16_t* __restrict__ vp, size_t rs,
+                                                int nvalid) {
+  using R = KVRegs<D>;
+#pragma unroll
+  for (int i = 0; i < R::NC; ++i) {
+    const int ci = min((int)threadIdx.x + i * kThreads, KN * R::CPR - 1);
     const int key = min(ci / R::CPR, nvalid - 1), ch = ci % R::CPR;
     r.k[i] = *reinterpret_cast<const u32x4_t*>(kp + key * rs + ch * 8);
+    r.v[i] = *reinterpret_cast<const u32x4_t*>(vp + key * rs + ch * 8);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void kv_fetch(KVRegs<D>& r, const KVOffsets<D>& o,
+                                         const uint16_t* __restrict__ kp,
+                                         const uint16_t* __restrict__ vp, size_t rs,
+                                         int nvalid) {
+  if (nvalid == KN) kv_load<D>(r, o, kp, vp);
+  else kv_load_partial<D>(r, kp, vp, rs, nvalid);
+}
+
+// K and V rows as they are, into padded rows
+template <int D>
+__device__ __forceinline__ void kv_store(const KVRegs<D>& r, char* lk, char* lv) {
+  using R = KVRegs<D>;
+  using L = Lds<D>;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < R::NVC; ++i) {
-    const int combo = min(tid + i * kThreads, (KN / 4) * R::CPR - 1);
-    const int kq = combo / R::CPR, dc = combo % R::CPR;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = min(4 * kq + e, nvalid - 1);
-      r.v[i][e] = *reinterpret_cast<const u32x4_t*>(vp + key * rs + dc * 8);
+  for (int i = 0; i < R::NC; ++i) {
+    const int ci = tid + i * kThreads;
+    const int key = ci / R::CPR, ch = ci % R::CPR;
+    if (ci < KN * R::CPR) {
+      *reinterpret_cast<u32x4_t*>(lk + key * L::KS + ch * 16) = r.k[i];
+      *reinterpret_cast<u32x4_t*>(lv + key * L::VS + ch * 16) = r.v[i];
     }
   }
 }
 
-// K rows as they are (16-byte chunks XOR-swizzled by key); V transposed to [dim][key]
-// with each 16-key group stored in the order 0-3, 8-11, 4-7, 12-15, which is the
-// order the score registers hold the keys in (so P^T needs no shuffle).
-template <int D>
-__device__ __forceinline__ void kv_store(const KVRegs<D>& r, char* lk, char* lv) {
-  using R = KVRegs<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < R::NKC; ++i) {
-    const int ci = tid + i * kThreads;
-    const int key = ci / R::CPR, ch = ci % R::CPR;
-    if (ci < KN * R::CPR) *reinterpret_cast<u32x4_t*>(lk + k_lds_off<D>(key, ch)) = r.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < R::NVC; ++i) {
-    const int combo = tid + i * kThreads;
-    if (combo >= (KN / 4) * R::CPR) continue;
-    const int kq = combo / R::CPR, dc = combo % R::CPR;
-    const int grp = kq & 3;
-    const int pos = (kq >> 2) * 16 + (((grp & 1) << 1) | (grp >> 1)) * 4;
-    const int chunk = pos >> 3, sub = (pos & 7) * 2;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x07060302u);
-      const int dim = dc * 8 + 2 * w;
-      *reinterpret_cast<u32x2_t*>(lv + v_lds_off(dim, chunk) + sub) = u32x2_t{lo01, lo23};
-      *reinterpret_cast<u32x2_t*>(lv + v_lds_off(dim + 1, chunk) + sub) = u32x2_t{hi01, hi23};
-    }
-  }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i%4 of
+// the 8 bytes addressed by lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, int QT>
@@ -147,10 +180,11 @@ __device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[qt][i] = 0.f;
+  // A = K rows kk*32 + n, dims 16*ks + 8*hf .. +7
+  const char* kp = lk + (kk * 32 + n) * Lds<D>::KS + hf * 16;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8_t a = as_bf16x8(
-        *reinterpret_cast<const u32x4_t*>(lk + k_lds_off<D>(kk * 32 + n, 2 * ks + hf)));
+    const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + ks * 32));
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) s[qt] = mfma32x32x16(a, st.q[qt][ks], s[qt]);
   }
@@ -168,7 +202,7 @@ __device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk
     float mx = s[qt][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qt][i]);
-    mx = fmaxf(mx, xor32_f32(mx));
+    mx = pair_max(mx);
     mxs[qt] = mx * sl;
     need |= mxs[qt] > st.m[qt] + kTau;
   }
@@ -189,6 +223,8 @@ __device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float mref = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
+    // the row sum stays float32: summing the bf16-rounded p would cost up to 2^-9
+    // relative in lse for rows that attend only a few keys
     float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -199,21 +235,27 @@ __device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk
     st.l[qt] += rs;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      u32x4_t w;
-      w[0] = pack_bf16x2(s[qt][8 * h + 0], s[qt][8 * h + 1]);
-      w[1] = pack_bf16x2(s[qt][8 * h + 2], s[qt][8 * h + 3]);
-      w[2] = pack_bf16x2(s[qt][8 * h + 4], s[qt][8 * h + 5]);
-      w[3] = pack_bf16x2(s[qt][8 * h + 6], s[qt][8 * h + 7]);
-      pb[qt][h] = as_bf16x8(w);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qt][8 * h + 2 * e], s[qt][8 * h + 2 * e + 1]);
+      pb[qt][h] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
     }
   }
-  // P^T for MFMA k-step (2*kk + h) is the score registers 8h .. 8h+7 of this half
+  // P^T for MFMA k-step ks = 2*kk + h is the score registers 8h .. 8h+7 of this half:
+  // lane (n, hf) holds keys 16ks + 8(e/4) + 4hf + e%4, e < 8.  The matching V^T operand
+  // is two transpose reads: lanes 4j+q of each 16-lane group address row
+  // 16ks + 4hf + j (+8 for the second read), dims d0 + 4q .. +3, where d0 = dt*32 +
+  // 16*((lane/16)&1); lane i of the group then holds dim d0 + i of those four keys.
+  const char* vp = lv + (4 * hf + ((lane & 15) >> 2)) * Lds<D>::VS +
+                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-          lv + v_lds_off(dt * 32 + n, 2 * (2 * kk + h) + hf)));
+      const int ks = 2 * kk + h;
+      const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * Lds<D>::VS + dt * 64);
+      const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * Lds<D>::VS + dt * 64);
+      const bf16x8_t a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][h], st.o[qt][dt]);
     }
@@ -226,27 +268,29 @@ __device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk
 // subtile i0 is already in buffer i0 & 1.
 template <int D, int QT, bool MASK>
 __device__ __forceinline__ void attend_subtiles(WaveState<D, QT>& st, char* lds,
-                                                KVRegs<D>& r, const uint16_t* __restrict__ kbase,
+                                                KVRegs<D>& r, const KVOffsets<D>& ko,
+                                                const uint16_t* __restrict__ kbase,
                                                 const uint16_t* __restrict__ vbase, size_t rs,
                                                 int key_begin, int key_end, int i0, int i1,
                                                 int nsub, float sl, bool active,
                                                 const int (&tpos)[QT]) {
-  constexpr int TILE = KN * D * 2;  // bytes of one K (or V) subtile
+  constexpr int STAGE = Lds<D>::STAGE;
+  constexpr int KB = Lds<D>::KBYTES;
   for (int i = i0; i < i1; ++i) {
     const int kb = key_begin + i * KN;
     const bool more = i + 1 < nsub;
     if (more)
-      kv_load<D>(r, kbase + (size_t)(kb + KN) * rs, vbase + (size_t)(kb + KN) * rs, rs,
-                 min(KN, key_end - kb - KN));
-    const char* cur = lds + (i & 1) * 2 * TILE;
+      kv_fetch<D>(r, ko, kbase + (size_t)(kb + KN) * rs, vbase + (size_t)(kb + KN) * rs, rs,
+                  min(KN, key_end - kb - KN));
+    const char* cur = lds + (i & 1) * STAGE;
     if (active) {
       const int nvalid = min(KN, key_end - kb);
-      attend_half<D, QT, MASK>(st, cur, cur + TILE, 0, sl, nvalid, kb, tpos);
-      attend_half<D, QT, MASK>(st, cur, cur + TILE, 1, sl, nvalid, kb, tpos);
+      attend_half<D, QT, MASK>(st, cur, cur + KB, 0, sl, nvalid, kb, tpos);
+      attend_half<D, QT, MASK>(st, cur, cur + KB, 1, sl, nvalid, kb, tpos);
     }
     if (more) {
-      char* nxt = lds + ((i + 1) & 1) * 2 * TILE;
-      kv_store<D>(r, nxt, nxt + TILE);
+      char* nxt = lds + ((i + 1) & 1) * STAGE;
+      kv_store<D>(r, nxt, nxt + KB);
     }
     __syncthreads();
   }
@@ -261,20 +305,21 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
                                              const uint16_t* __restrict__ vbase, size_t rs,
                                              int key_begin, int key_end, float sl,
                                              bool active, int diag_from, const int (&tpos)[QT]) {
-  constexpr int TILE = KN * D * 2;
   KVRegs<D> r;
+  KVOffsets<D> ko;
+  ko.init(rs);
   const int nsub = (key_end - key_begin + KN - 1) / KN;
   // subtile i is mask-free iff key_begin + (i+1)*KN <= min(key_end, diag_from + 1)
   const int lim = min(key_end, diag_from == 0x7fffffff ? key_end : diag_from + 1);
   const int nplain = max(0, min(nsub, (lim - key_begin) / KN));
-  kv_load<D>(r, kbase + (size_t)key_begin * rs, vbase + (size_t)key_begin * rs, rs,
-             min(KN, key_end - key_begin));
-  kv_store<D>(r, lds, lds + TILE);
+  kv_fetch<D>(r, ko, kbase + (size_t)key_begin * rs, vbase + (size_t)key_begin * rs, rs,
+              min(KN, key_end - key_begin));
+  kv_store<D>(r, lds, lds + Lds<D>::KBYTES);
   __syncthreads();
-  attend_subtiles<D, QT, false>(st, lds, r, kbase, vbase, rs, key_begin, key_end, 0, nplain,
-                                nsub, sl, active, tpos);
-  attend_subtiles<D, QT, true>(st, lds, r, kbase, vbase, rs, key_begin, key_end, nplain, nsub,
-                               nsub, sl, active, tpos);
+  attend_subtiles<D, QT, false>(st, lds, r, ko, kbase, vbase, rs, key_begin, key_end, 0,
+                                nplain, nsub, sl, active, tpos);
+  attend_subtiles<D, QT, true>(st, lds, r, ko, kbase, vbase, rs, key_begin, key_end, nplain,
+                               nsub, nsub, sl, active, tpos);
 }
 
 // normalise and store one query tile's partial (o fp32 [D], lse natural log)
@@ -282,7 +327,7 @@ template <int D, int QT>
 __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt, bool valid,
                                               float* __restrict__ po, float* __restrict__ pl) {
   const int lane = threadIdx.x & 63, hf = lane >> 5;
-  const float ltot = st.l[qt] + xor32_f32(st.l[qt]);
+  const float ltot = pair_sum(st.l[qt]);
   if (!valid) return;
   const float inv = 1.f / ltot;
 #pragma unroll
@@ -318,7 +363,7 @@ __global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_history_kernel(
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * KN * D * 2];
+  __shared__ __attribute__((aligned(16))) char lds[2 * Lds<D>::STAGE];
   const int tile_id = blockIdx.x;
   if (tile_id >= *tile_count) return;
   const int4 tl = tiles[tile_id];
@@ -367,7 +412,7 @@ __global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_current_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * KN * D * 2];
+  __shared__ __attribute__((aligned(16))) char lds[2 * Lds<D>::STAGE];
   constexpr int TT = 32 * QT;
   const int c = blockIdx.y;
   const int gi = blockIdx.z % ng, b = blockIdx.z / ng;
