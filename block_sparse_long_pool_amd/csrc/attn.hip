@@ -19,7 +19,7 @@
 //            gfx950 LDS transpose read (ds_read_b64_tr_b16), whose key order is
 //            chosen to match the order the score registers hold the keys in, so no
 //            register shuffle and no transpose while staging are needed.
-// K and V tiles are row-major in LDS with padded rows (K: +16 B, V: +32 B), which
+// K and V tiles are row-major in LDS with padded rows (K: +16 B, V: +64 B), which
 // spreads the MFMA operand reads over all banks and lets every read use a per-lane
 // base address plus an immediate offset.
 // Online softmax in the log2 domain (scale * log2(e) folded into one FMA).
@@ -34,6 +34,12 @@ namespace moba {
 #ifndef MOBA_ATTN_WPE
 #define MOBA_ATTN_WPE 2
 #endif
+// wavefronts per attention workgroup; every staged K/V subtile serves all of them
+#ifndef MOBA_ATTN_NW
+#define MOBA_ATTN_NW 8
+#endif
+constexpr int kAttnWaves = MOBA_ATTN_NW;
+constexpr int kAttnThreads = 64 * kAttnWaves;
 
 constexpr int KN = 64;          // keys per LDS subtile
 constexpr float kTau = 8.f;     // lazy rescale: the reference max may lag by 2^8
@@ -41,10 +47,12 @@ constexpr float kTau = 8.f;     // lazy rescale: the reference max may lag by 2^
 template <int D>
 struct Lds {
   static constexpr int KS = D * 2 + 16;          // K row stride (bytes)
-  static constexpr int VS = D * 2 + 32;          // V row stride (bytes)
+  // V row stride: a transpose read serves 32 lanes = 4 key rows x 64 bytes per pass;
+  // a stride of 16 dwords (mod 64 banks) puts those rows on disjoint banks
+  static constexpr int VS = D * 2 + 64;          // V row stride (bytes)
   static constexpr int KBYTES = KN * KS;
   static constexpr int VBYTES = KN * VS;
-  static constexpr int STAGE = KBYTES + VBYTES;  // one K + V subtile
+  static constexpr int TOTAL = 2 * (KBYTES + VBYTES);  // two K and two V buffers
 };
 
 template <int D, int QT>
@@ -54,81 +62,60 @@ struct WaveState {
   float m[QT], l[QT];
 };
 
-// one subtile of K and V in flight through registers (global -> regs -> LDS)
+// One 64-key subtile of K (or V) in flight through registers (global -> regs -> LDS).
 template <int D>
-struct KVRegs {
+struct TileRegs {
   static constexpr int CPR = D / 8;                                  // 16 B chunks per row
-  static constexpr int NC = (KN * CPR + kThreads - 1) / kThreads;    // chunks per thread
-  u32x4_t k[NC];
-  u32x4_t v[NC];
+  static constexpr int NC = (KN * CPR + kAttnThreads - 1) / kAttnThreads;    // chunks per thread
+  u32x4_t c[NC];
 };
 
-// Per-thread element offsets of the 16-byte chunks a thread stages, relative to the
-// subtile's first key (row stride rs); computed once per kernel.
+// Per-thread element offsets of the chunks a thread stages, relative to the subtile's
+// first key (row stride rs); computed once per kernel.
 template <int D>
-struct KVOffsets {
-  uint32_t off[KVRegs<D>::NC];
+struct TileOffsets {
+  uint32_t off[TileRegs<D>::NC];
   __device__ __forceinline__ void init(size_t rs) {
-    using R = KVRegs<D>;
+    using R = TileRegs<D>;
 #pragma unroll
     for (int i = 0; i < R::NC; ++i) {
-      const int ci = min((int)threadIdx.x + i * kThreads, KN * R::CPR - 1);
+      const int ci = min((int)threadIdx.x + i * kAttnThreads, KN * R::CPR - 1);
       off[i] = (uint32_t)((ci / R::CPR) * rs + (ci % R::CPR) * 8);
     }
   }
 };
 
-// A full subtile: kp/vp point at its first key.
+// p points at the subtile's first key.  A partial subtile (nvalid < KN) re-reads row
+// nvalid-1 for the rows past its end: those keys are masked (score -inf, p = 0), so
+// their values only need to be finite.
 template <int D>
-__device__ __forceinline__ void kv_load(KVRegs<D>& r, const KVOffsets<D>& o,
-                                        const uint16_t* __restrict__ kp,
-                                        const uint16_t* __restrict__ vp) {
+__device__ __forceinline__ void tile_load(TileRegs<D>& r, const TileOffsets<D>& o,
+                                          const uint16_t* __restrict__ p, size_t rs,
+                                          int nvalid) {
+  using R = TileRegs<D>;
+  if (nvalid == KN) {
 #pragma unroll
-  for (int i = 0; i < KVRegs<D>::NC; ++i) {
-    r.k[i] = *reinterpret_cast<const u32x4_t*>(kp + o.off[i]);
-    r.v[i] = *reinterpret_cast<const u32x4_t*>(vp + o.off[i]);
-  }
-}
-
-// A partial subtile of nvalid keys.  Rows past nvalid re-read row nvalid-1: those keys
-// are masked (score -inf, p = 0), so their values only need to be finite.
-template <int D>
-__device__ __forceinline__ void kv_load_partial(KVRegs<D>& r, const uint16_t* __restrict__ kp,
-                                                const uint16_t* __restrict__ vp, size_t rs,
-                                                int nvalid) {
-  using R = KVRegs<D>;
+    for (int i = 0; i < R::NC; ++i) r.c[i] = *reinterpret_cast<const u32x4_t*>(p + o.off[i]);
+  } else {
 #pragma unroll
-  for (int i = 0; i < R::NC; ++i) {
-    const int ci = min((int)threadIdx.x + i * kThreads, KN * R::CPR - 1);
-    const int key = min(ci / R::CPR, nvalid - 1), ch = ci % R::CPR;
-    r.k[i] = *reinterpret_cast<const u32x4_t*>(kp + key * rs + ch * 8);
-    r.v[i] = *reinterpret_cast<const u32x4_t*>(vp + key * rs + ch * 8);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void kv_fetch(KVRegs<D>& r, const KVOffsets<D>& o,
-                                         const uint16_t* __restrict__ kp,
-                                         const uint16_t* __restrict__ vp, size_t rs,
-                                         int nvalid) {
-  if (nvalid == KN) kv_load<D>(r, o, kp, vp);
-  else kv_load_partial<D>(r, kp, vp, rs, nvalid);
-}
-
-// K and V rows as they are, into padded rows
-template <int D>
-__device__ __forceinline__ void kv_store(const KVRegs<D>& r, char* lk, char* lv) {
-  using R = KVRegs<D>;
-  using L = Lds<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < R::NC; ++i) {
-    const int ci = tid + i * kThreads;
-    const int key = ci / R::CPR, ch = ci % R::CPR;
-    if (ci < KN * R::CPR) {
-      *reinterpret_cast<u32x4_t*>(lk + key * L::KS + ch * 16) = r.k[i];
-      *reinterpret_cast<u32x4_t*>(lv + key * L::VS + ch * 16) = r.v[i];
+    for (int i = 0; i < R::NC; ++i) {
+      const int ci = min((int)threadIdx.x + i * kAttnThreads, KN * R::CPR - 1);
+      const int key = min(ci / R::CPR, nvalid - 1), ch = ci % R::CPR;
+      r.c[i] = *reinterpret_cast<const u32x4_t*>(p + key * rs + ch * 8);
     }
+  }
+}
+
+// rows as they are, into padded LDS rows of STRIDE bytes
+template <int D, int STRIDE>
+__device__ __forceinline__ void tile_store(const TileRegs<D>& r, char* dst) {
+  using R = TileRegs<D>;
+  constexpr bool kAllThreads = (KN * R::CPR) % kAttnThreads == 0;
+#pragma unroll
+  for (int i = 0; i < R::NC; ++i) {
+    const int ci = threadIdx.x + i * kAttnThreads;
+    if (kAllThreads || ci < KN * R::CPR)
+      *reinterpret_cast<u32x4_t*>(dst + (ci / R::CPR) * STRIDE + (ci % R::CPR) * 16) = r.c[i];
   }
 }
 
@@ -166,44 +153,60 @@ __device__ __forceinline__ void state_init(WaveState<D, QT>& st) {
   }
 }
 
-// 32 keys (half kk of a 64-key subtile staged in LDS) for every query row of the wave.
-// MASK: key rows >= nkeys and keys > tpos (causal) score -inf.  Lazy rescale: the
-// reference max m moves only when a row's max exceeds it by more than kTau (O and l are
-// rescaled then), so p = exp2(s * scale * log2e - m) <= 2^kTau.
-template <int D, int QT, bool MASK>
-__device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk,
-                                            const char* lv, int kk, float sl, int nkeys,
-                                            int kb, const int (&tpos)[QT]) {
+// Scores of one 64-key subtile: S^T = K Q^T, two 32-key halves.  Lane (n, hf) ends up
+// with query n and keys kk*32 + (i/4)*8 + hf*4 + i%4 of half kk.
+template <int D, int QT>
+__device__ __forceinline__ void qk_subtile(f32x16_t (&s)[2][QT], const WaveState<D, QT>& st,
+                                           const char* lk) {
   const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  f32x16_t s[QT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[qt][i] = 0.f;
-  // A = K rows kk*32 + n, dims 16*ks + 8*hf .. +7
-  const char* kp = lk + (kk * 32 + n) * Lds<D>::KS + hf * 16;
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + ks * 32));
+      for (int i = 0; i < 16; ++i) s[kk][qt][i] = 0.f;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) s[qt] = mfma32x32x16(a, st.q[qt][ks], s[qt]);
+  for (int kk = 0; kk < 2; ++kk) {
+    // A = K rows kk*32 + n, dims 16*ks + 8*hf .. +7
+    const char* kp = lk + (kk * 32 + n) * Lds<D>::KS + hf * 16;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + ks * 32));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[kk][qt] = mfma32x32x16(a, st.q[qt][ks], s[kk][qt]);
+    }
+  }
+}
+
+// Masks (keys >= nkeys, keys > tpos), takes the row max and applies the lazy rescale:
+// the reference max m moves only when a row's max exceeds it by more than kTau (O and
+// l are rescaled then), so later p = exp2(s * scale * log2e - m) <= 2^kTau.
+template <int D, int QT>
+__device__ __forceinline__ void softmax_max(WaveState<D, QT>& st, f32x16_t (&s)[2][QT],
+                                            float sl, bool mask, int nkeys, int kb,
+                                            const int (&tpos)[QT]) {
+  const int hf = (threadIdx.x & 63) >> 5;
+  if (mask) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int lim = min(nkeys - 1, tpos[qt] - kb) - kk * 32 - hf * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i >> 2) * 8 + (i & 3) > lim) s[kk][qt][i] = -INFINITY;
+      }
   }
   float mxs[QT];
   bool need = false;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    if (MASK) {
-      // key kb + kk*32 + (i/4)*8 + hf*4 + i%4 is live iff its row < nkeys and key <= tpos
-      const int lim = min(nkeys - 1, tpos[qt] - kb) - kk * 32 - hf * 4;
+    float mx = s[0][qt][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i >> 2) * 8 + (i & 3) > lim) s[qt][i] = -INFINITY;
-    }
-    float mx = s[qt][0];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qt][i]);
-    mx = pair_max(mx);
-    mxs[qt] = mx * sl;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][qt][i]);
+    mxs[qt] = pair_max(mx) * sl;
     need |= mxs[qt] > st.m[qt] + kTau;
   }
   if (__ballot(need) != 0ull) {
@@ -219,107 +222,357 @@ __device__ __forceinline__ void attend_half(WaveState<D, QT>& st, const char* lk
         for (int i = 0; i < 16; ++i) st.o[qt][dt][i] *= alpha;
     }
   }
-  bf16x8_t pb[QT][2];
+}
+
+// p = exp2(s * sl - m), float32 row sum, and P^T packed as bf16 MFMA operands: k-step
+// ks (keys 16ks .. 16ks+15) is score registers 8*(ks%2) .. +7 of half ks/2.
+template <int D, int QT>
+__device__ __forceinline__ void softmax_exp(WaveState<D, QT>& st, const f32x16_t (&s)[2][QT],
+                                            float sl, bf16x8_t (&pb)[QT][4]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float mref = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
-    // the row sum stays float32: summing the bf16-rounded p would cost up to 2^-9
-    // relative in lse for rows that attend only a few keys
     float rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][i], sl, -mref));
-      s[qt][i] = p;
-      rs += p;
+    for (int kk = 0; kk < 2; ++kk) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s[kk][qt][i], sl, -mref));
+        rs += p[i];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+        pb[qt][2 * kk + h] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+      }
     }
     st.l[qt] += rs;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qt][8 * h + 2 * e], s[qt][8 * h + 2 * e + 1]);
-      pb[qt][h] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
-    }
   }
-  // P^T for MFMA k-step ks = 2*kk + h is the score registers 8h .. 8h+7 of this half:
-  // lane (n, hf) holds keys 16ks + 8(e/4) + 4hf + e%4, e < 8.  The matching V^T operand
-  // is two transpose reads: lanes 4j+q of each 16-lane group address row
-  // 16ks + 4hf + j (+8 for the second read), dims d0 + 4q .. +3, where d0 = dt*32 +
-  // 16*((lane/16)&1); lane i of the group then holds dim d0 + i of those four keys.
+}
+
+// O^T += V^T P^T for one subtile.  Lane (n, hf) holds keys 16ks + 8(e/4) + 4hf + e%4,
+// e < 8, of k-step ks; the matching V^T operand is two transpose reads: lanes 4j+q of
+// each 16-lane group address row 16ks + 4hf + j (+8 for the second read), dims
+// d0 + 4q .. +3, d0 = dt*32 + 16*((lane/16)&1); lane i of the group then holds dim d0+i.
+template <int D, int QT>
+__device__ __forceinline__ void pv_subtile(WaveState<D, QT>& st, const bf16x8_t (&pb)[QT][4],
+                                           const char* lv) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
   const char* vp = lv + (4 * hf + ((lane & 15) >> 2)) * Lds<D>::VS +
                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ks = 2 * kk + h;
+    for (int ks = 0; ks < 4; ++ks) {
       const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * Lds<D>::VS + dt * 64);
       const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * Lds<D>::VS + dt * 64);
       const bf16x8_t a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][h], st.o[qt][dt]);
+      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][ks], st.o[qt][dt]);
     }
   }
 }
 
-// Subtiles [i0, i1) of the key range starting at key_begin, staged through two LDS
-// buffers: the next subtile's global loads are in flight while the current one is
-// computed, then written to the other buffer; one barrier per subtile.  On entry the
-// subtile i0 is already in buffer i0 & 1.
-template <int D, int QT, bool MASK>
-__device__ __forceinline__ void attend_subtiles(WaveState<D, QT>& st, char* lds,
-                                                KVRegs<D>& r, const KVOffsets<D>& ko,
-                                                const uint16_t* __restrict__ kbase,
-                                                const uint16_t* __restrict__ vbase, size_t rs,
-                                                int key_begin, int key_end, int i0, int i1,
-                                                int nsub, float sl, bool active,
-                                                const int (&tpos)[QT]) {
-  constexpr int STAGE = Lds<D>::STAGE;
-  constexpr int KB = Lds<D>::KBYTES;
-  for (int i = i0; i < i1; ++i) {
-    const int kb = key_begin + i * KN;
-    const bool more = i + 1 < nsub;
-    if (more)
-      kv_fetch<D>(r, ko, kbase + (size_t)(kb + KN) * rs, vbase + (size_t)(kb + KN) * rs, rs,
-                  min(KN, key_end - kb - KN));
-    const char* cur = lds + (i & 1) * STAGE;
-    if (active) {
-      const int nvalid = min(KN, key_end - kb);
-      attend_half<D, QT, MASK>(st, cur, cur + KB, 0, sl, nvalid, kb, tpos);
-      attend_half<D, QT, MASK>(st, cur, cur + KB, 1, sl, nvalid, kb, tpos);
+// Key-range walker.  LDS holds two K buffers and two V buffers; K runs one subtile
+// ahead of V.  Before step i the scores of subtile i are in registers and the lazy
+// rescale for them is done.  Step i:
+//   region A  the MFMAs of QK^T for subtile i+1 (K buffer (i+1)&1), each next to the
+//             operand read three slots ahead and a slice of the exp/sum work of
+//             subtile i;
+//   region B  the PV MFMAs of subtile i (V buffer i&1), each next to its transpose
+//             reads two slots ahead, a slice of the mask/max work on subtile i+1,
+//             and one staging operation: K(i+2) -> K buffer i&1, V(i+1) -> V buffer
+//             (i+1)&1, then the global loads of K(i+3) and V(i+2);
+//   then the rescale decision for subtile i+1 and one barrier.
+// The order inside the regions is fixed by sched_barrier fences.  Staging past the
+// last subtile re-reads the last subtile into a buffer nobody reads again, so the
+// steady state has no branches.
+template <int D, int QT>
+struct Walker {
+  using L = Lds<D>;
+  static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
+  static constexpr int NQK = 2 * KSTEPS;           // QK^T MFMAs per query tile
+  static constexpr int NPV = 4 * (D / 32);         // PV MFMAs per query tile
+  static constexpr int PFK = 3, PFV = 2;           // operand reads in flight
+  static constexpr int NC = TileRegs<D>::NC;
+  char* lds;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  size_t rs;
+  int key_begin, key_end, nsub, diag_from;
+  float sl;
+  bool active;
+  TileOffsets<D> to;
+  TileRegs<D> rk, rv;
+
+  __device__ __forceinline__ char* kbuf(int i) const { return lds + (i & 1) * L::KBYTES; }
+  __device__ __forceinline__ char* vbuf(int i) const {
+    return lds + 2 * L::KBYTES + (i & 1) * L::VBYTES;
+  }
+  __device__ __forceinline__ int kb(int i) const { return key_begin + i * KN; }
+  __device__ __forceinline__ int nvalid(int i) const { return min(KN, key_end - kb(i)); }
+  __device__ __forceinline__ bool masked(int i) const {
+    return kb(i) + KN > key_end || kb(i) + KN - 1 > diag_from;
+  }
+  __device__ __forceinline__ void load_k(int i) {
+    i = min(i, nsub - 1);
+    tile_load<D>(rk, to, kbase + (size_t)kb(i) * rs, rs, nvalid(i));
+  }
+  __device__ __forceinline__ void load_v(int i) {
+    i = min(i, nsub - 1);
+    tile_load<D>(rv, to, vbase + (size_t)kb(i) * rs, rs, nvalid(i));
+  }
+  // staging chunk c of the current registers: c < NC is K, else V
+  __device__ __forceinline__ void store_chunk(int c, int i) {
+    constexpr bool kAllThreads = (KN * TileRegs<D>::CPR) % kAttnThreads == 0;
+    const int ci = threadIdx.x + (c % NC) * kAttnThreads;
+    if (kAllThreads || ci < KN * TileRegs<D>::CPR) {
+      const int row = ci / TileRegs<D>::CPR, col = (ci % TileRegs<D>::CPR) * 16;
+      if (c < NC)
+        *reinterpret_cast<u32x4_t*>(kbuf(i) + row * L::KS + col) = rk.c[c];
+      else
+        *reinterpret_cast<u32x4_t*>(vbuf(i + 1) + row * L::VS + col) = rv.c[c - NC];
     }
-    if (more) {
-      char* nxt = lds + ((i + 1) & 1) * STAGE;
-      kv_store<D>(r, nxt, nxt + KB);
+  }
+
+  __device__ __forceinline__ static int k_off(int j) {
+    return (j / KSTEPS) * 32 * L::KS + (j % KSTEPS) * 32;
+  }
+
+  // the mask and row max of a subtile's scores; returns scaled maxima in mxs
+  __device__ __forceinline__ void mask_scores(f32x16_t (&s)[2][QT], int i,
+                                              const int (&tpos)[QT]) const {
+    const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int lim = min(nvalid(i) - 1, tpos[qt] - kb(i)) - kk * 32 - hf * 4;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((e >> 2) * 8 + (e & 3) > lim) s[kk][qt][e] = -INFINITY;
+      }
+  }
+
+  __device__ __forceinline__ void rescale(WaveState<D, QT>& st, const float (&mxs)[QT]) {
+    bool need = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) need |= mxs[qt] > st.m[qt] + kTau;
+    if (__ballot(need) != 0ull) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mnew = fmaxf(st.m[qt], mxs[qt]);
+        const float alpha =
+            (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(st.m[qt] - mnew);
+        st.m[qt] = mnew;
+        st.l[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) st.o[qt][dt][e] *= alpha;
+      }
+    }
+  }
+
+  template <bool NEXT, bool MASKN>
+  __device__ __forceinline__ void step(WaveState<D, QT>& st, f32x16_t (&cur)[2][QT],
+                                       f32x16_t (&nxt)[2][QT], int i, const int (&tpos)[QT]) {
+    const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+    if (active) {
+      // ---------------- region A: QK^T(i+1) || exp(i)
+      constexpr int EPS = 32 / NQK;  // exp elements per slot and query tile
+      const char* kp = kbuf(i + 1) + n * L::KS + hf * 16;
+      bf16x8_t ka[NQK];
+      if (NEXT) {
+#pragma unroll
+        for (int j = 0; j < PFK; ++j)
+          ka[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
+      }
+      float mref[QT], rsum[QT], p[QT][32];
+      bf16x8_t pb[QT][4];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        mref[qt] = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
+        rsum[qt] = 0.f;
+      }
+      const f32x16_t zero = {};
+#pragma unroll
+      for (int j = 0; j < NQK; ++j) {
+        if (NEXT) {
+          if (j + PFK < NQK)
+            ka[j + PFK] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j + PFK)));
+          const int kk = j / KSTEPS, ks = j % KSTEPS;
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            nxt[kk][qt] = mfma32x32x16(ka[j], st.q[qt][ks], ks == 0 ? zero : nxt[kk][qt]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int x = j * EPS + e;
+            p[qt][x] = __builtin_amdgcn_exp2f(fmaf(cur[x >> 4][qt][x & 15], sl, -mref[qt]));
+            rsum[qt] += p[qt][x];
+          }
+          // P^T operand of k-step ks = score registers 8*(ks%2) .. +7 of half ks/2,
+          // packed as soon as its 8 values exist
+          if (((j + 1) * EPS) % 8 == 0) {
+            const int ks = (j + 1) * EPS / 8 - 1;
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] = pack_bf16x2(p[qt][8 * ks + 2 * e], p[qt][8 * ks + 2 * e + 1]);
+            pb[qt][ks] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) st.l[qt] += rsum[qt];
+      // ---------------- region B: PV(i) || max(i+1) || staging
+      if (NEXT && MASKN) mask_scores(nxt, i + 1, tpos);
+      const char* vp = vbuf(i) + (4 * hf + ((lane & 15) >> 2)) * L::VS +
+                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+      u32x4_t va[NPV];
+      auto vread = [&](int j) {
+        const int ks = j / (D / 32), dt = j % (D / 32);
+        const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * L::VS + dt * 64);
+        const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * L::VS + dt * 64);
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      };
+#pragma unroll
+      for (int j = 0; j < PFV; ++j) va[j] = vread(j);
+      constexpr int MPS = 32 / NPV;  // max elements per slot and query tile
+      float mx[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mx[qt] = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        if (j + PFV < NPV) va[j + PFV] = vread(j + PFV);
+        const int ks = j / (D / 32), dt = j % (D / 32);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          st.o[qt][dt] = mfma32x32x16(as_bf16x8(va[j]), pb[qt][ks], st.o[qt][dt]);
+        if (NEXT) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int e = 0; e < MPS; ++e) {
+              const int x = j * MPS + e;
+              mx[qt] = fmaxf(mx[qt], nxt[x >> 4][qt][x & 15]);
+            }
+        }
+        if (j < 2 * NC) store_chunk(j, i);
+        else if (j == 2 * NC) load_k(i + 3);
+        else if (j == 2 * NC + 1) load_v(i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (2 * NC >= NPV) {   // more staging than MFMA slots (not the case for d = 64, 128)
+#pragma unroll
+        for (int c = NPV; c < 2 * NC; ++c) store_chunk(c, i);
+        load_k(i + 3);
+        load_v(i + 2);
+      }
+      if (NEXT) {
+        float mxs[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mxs[qt] = pair_max(mx[qt]) * sl;
+        rescale(st, mxs);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2 * NC; ++c) store_chunk(c, i);
+      load_k(i + 3);
+      load_v(i + 2);
     }
     __syncthreads();
   }
-}
 
-// The wave's rows over keys [key_begin, key_end) of one kv-head.  Subtiles whose last
-// key exceeds diag_from (the smallest query position of the workgroup) or key_end need
-// the mask; they come last and run in their own loop.
+  __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT]) {
+    to.init(rs);
+    nsub = (key_end - key_begin + KN - 1) / KN;
+    // prologue: K(0), V(0), K(1) into LDS; K(2), V(1) into registers
+    load_k(0);
+    load_v(0);
+    tile_store<D, L::KS>(rk, kbuf(0));
+    tile_store<D, L::VS>(rv, vbuf(0));
+    load_k(1);
+    tile_store<D, L::KS>(rk, kbuf(1));   // duplicate of K(0) when nsub == 1, unused
+    load_v(1);
+    load_k(2);
+    __syncthreads();
+    f32x16_t sa[2][QT], sb[2][QT];
+    if (active) {
+      const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+      const char* kp = kbuf(0) + n * L::KS + hf * 16;
+      const f32x16_t zero = {};
+#pragma unroll
+      for (int j = 0; j < NQK; ++j) {
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
+        const int kk = j / KSTEPS, ks = j % KSTEPS;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          sa[kk][qt] = mfma32x32x16(a, st.q[qt][ks], ks == 0 ? zero : sa[kk][qt]);
+      }
+      if (masked(0)) mask_scores(sa, 0, tpos);
+      float mxs[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[kk][qt][e]);
+        mxs[qt] = pair_max(mx) * sl;
+      }
+      rescale(st, mxs);
+    }
+    __syncthreads();   // K buffer 0 is rewritten in step 0
+    // subtiles needing the mask are a suffix: [nplain, nsub)
+    int nplain = 0;
+    while (nplain < nsub && !masked(nplain)) ++nplain;
+    int i = 0;
+    for (; i + 1 < min(nplain, nsub); ++i) {
+      step<true, false>(st, sa, sb, i, tpos);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sa[kk][qt] = sb[kk][qt];
+    }
+    for (; i + 1 < nsub; ++i) {
+      step<true, true>(st, sa, sb, i, tpos);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sa[kk][qt] = sb[kk][qt];
+    }
+    step<false, false>(st, sa, sb, nsub - 1, tpos);
+  }
+};
+
+// The wave's rows over keys [key_begin, key_end) of one kv-head; subtiles whose last
+// key exceeds diag_from (the smallest query position of the workgroup) or key_end are
+// masked.
 template <int D, int QT>
 __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
                                              const uint16_t* __restrict__ kbase,
                                              const uint16_t* __restrict__ vbase, size_t rs,
                                              int key_begin, int key_end, float sl,
                                              bool active, int diag_from, const int (&tpos)[QT]) {
-  KVRegs<D> r;
-  KVOffsets<D> ko;
-  ko.init(rs);
-  const int nsub = (key_end - key_begin + KN - 1) / KN;
-  // subtile i is mask-free iff key_begin + (i+1)*KN <= min(key_end, diag_from + 1)
-  const int lim = min(key_end, diag_from == 0x7fffffff ? key_end : diag_from + 1);
-  const int nplain = max(0, min(nsub, (lim - key_begin) / KN));
-  kv_fetch<D>(r, ko, kbase + (size_t)key_begin * rs, vbase + (size_t)key_begin * rs, rs,
-              min(KN, key_end - key_begin));
-  kv_store<D>(r, lds, lds + Lds<D>::KBYTES);
-  __syncthreads();
-  attend_subtiles<D, QT, false>(st, lds, r, ko, kbase, vbase, rs, key_begin, key_end, 0,
-                                nplain, nsub, sl, active, tpos);
-  attend_subtiles<D, QT, true>(st, lds, r, ko, kbase, vbase, rs, key_begin, key_end, nplain,
-                               nsub, nsub, sl, active, tpos);
+  Walker<D, QT> w;
+  w.lds = lds;
+  w.kbase = kbase;
+  w.vbase = vbase;
+  w.rs = rs;
+  w.key_begin = key_begin;
+  w.key_end = key_end;
+  w.diag_from = diag_from;
+  w.sl = sl;
+  w.active = active;
+  w.run(st, tpos);
 }
 
 // normalise and store one query tile's partial (o fp32 [D], lse natural log)
@@ -355,15 +608,16 @@ __device__ __forceinline__ void load_q(WaveState<D, QT>& st, int qt, const uint1
 }
 
 // ---------------------------------------------------------------- history (a4)
-// One workgroup = one tile of up to 4 * 32 * QT gathered rows of one list (b, g, j).
+// One workgroup = one tile of up to kAttnWaves * 32 * QT gathered rows of one list
+// (b, g, j).
 template <int D, int QT>
-__global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_history_kernel(
+__global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * Lds<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int tile_id = blockIdx.x;
   if (tile_id >= *tile_count) return;
   const int4 tl = tiles[tile_id];
@@ -404,36 +658,46 @@ __global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_history_kernel(
 }
 
 // ---------------------------------------------------------------- current (a5)
-// One workgroup = 32*QT consecutive tokens of block c; its waves are the query heads
-// of kv-head g (in rounds of four), so all four share every staged K/V subtile.
-// Tiles run from the end of the block backwards: the longest ones start first.
+// One workgroup = a run of consecutive tokens of block c for the query heads of
+// kv-head g; all its waves share every staged K/V subtile.  With G heads per kv-head
+// dividing the wave count, wave w takes head w % G and 32*QT-token sub-tile w / G;
+// otherwise one sub-tile and the heads in rounds.  Tiles run from the end of the
+// block backwards, so the longest ones start first.
+__host__ __device__ __forceinline__ int current_subtiles(int G) {
+  return (G <= kAttnWaves && kAttnWaves % G == 0) ? kAttnWaves / G : 1;
+}
+
 template <int D, int QT>
-__global__ __launch_bounds__(kThreads, MOBA_ATTN_WPE) void attn_current_kernel(
+__global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * Lds<D>::STAGE];
-  constexpr int TT = 32 * QT;
+  __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int c = blockIdx.y;
   const int gi = blockIdx.z % ng, b = blockIdx.z / ng;
   const int G = hq / hkv, g = g0 + gi;
+  const int TS = current_subtiles(G);
+  const int TT = 32 * QT * TS;
   const int x = gridDim.x - 1 - blockIdx.x;
   const int t0 = c * block + x * TT;
   const int t_end = min(t0 + TT, (c + 1) * block);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
+  const int hw = TS > 1 ? wave % G : wave;      // head of this wave within a round
+  const int tsub = TS > 1 ? wave / G : 0;
+  const int hstep = TS > 1 ? G : kAttnWaves;     // heads covered per round
   const size_t rs = (size_t)hkv * D;
   const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
   const int ngq = ng * G;
-  for (int round = 0; round * 4 < G; ++round) {
-    const int hl = round * 4 + wave;
+  for (int round = 0; round * hstep < G; ++round) {
+    const int hl = round * hstep + hw;
     const bool active = hl < G;
     WaveState<D, QT> st;
     int tpos[QT];
     bool vq[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      tpos[qt] = t0 + qt * 32 + n;
+      tpos[qt] = t0 + (tsub * QT + qt) * 32 + n;
       vq[qt] = active && tpos[qt] < t_end;
       const uint16_t* qrow = q + ((size_t)((size_t)b * T + (vq[qt] ? tpos[qt] : 0)) * hq +
                                   g * G + (active ? hl : 0)) * D;
@@ -500,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 
 // ---------------------------------------------------------------- launchers
 constexpr int kQT = MOBA_ATTN_QT;
-int history_tile_rows() { return 4 * 32 * kQT; }
+int history_tile_rows() { return kAttnWaves * 32 * kQT; }
 
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
@@ -510,11 +774,11 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
   if (max_tiles <= 0) return hipSuccess;
   const float sl = scale * 1.4426950408889634f;
   if (s.d == 128)
-    hipLaunchKernelGGL((attn_history_kernel<128, kQT>), dim3(max_tiles), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_history_kernel<128, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
                        st, q, k, v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, s.nb(),
                        tiles, tile_count, entries, part_o, part_lse);
   else
-    hipLaunchKernelGGL((attn_history_kernel<64, kQT>), dim3(max_tiles), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_history_kernel<64, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
                        st, q, k, v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, s.nb(),
                        tiles, tile_count, entries, part_o, part_lse);
   return hipGetLastError();
@@ -524,13 +788,13 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
                                const uint16_t* v, float scale, int g0, int ng,
                                float* part_o, float* part_lse, hipStream_t st) {
   const float sl = scale * 1.4426950408889634f;
-  constexpr int TT = 32 * kQT;
+  const int TT = 32 * kQT * current_subtiles(s.G());
   dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng);
   if (s.d == 128)
-    hipLaunchKernelGGL((attn_current_kernel<128, kQT>), grid, dim3(kThreads), 0, st, q, k,
+    hipLaunchKernelGGL((attn_current_kernel<128, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
                        v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse);
   else
-    hipLaunchKernelGGL((attn_current_kernel<64, kQT>), grid, dim3(kThreads), 0, st, q, k,
+    hipLaunchKernelGGL((attn_current_kernel<64, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
                        v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse);
   return hipGetLastError();
 }
