@@ -85,24 +85,21 @@ struct TileOffsets {
   }
 };
 
-// p points at the subtile's first key.  A partial subtile (nvalid < KN) re-reads row
-// nvalid-1 for the rows past its end: those keys are masked (score -inf, p = 0), so
-// their values only need to be finite.
+// p points at the subtile's first key (a wave-uniform address).  The loads go through
+// a buffer descriptor covering exactly the nvalid rows of the subtile: the 32-bit
+// offsets need no 64-bit address arithmetic, and the rows past a partial subtile's
+// end read as zeros (those keys are masked, so any finite value would do).
 template <int D>
 __device__ __forceinline__ void tile_load(TileRegs<D>& r, const TileOffsets<D>& o,
                                           const uint16_t* __restrict__ p, size_t rs,
                                           int nvalid) {
   using R = TileRegs<D>;
-  if (nvalid == KN) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p), (short)0, (int)(nvalid * rs * sizeof(uint16_t)), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < R::NC; ++i) r.c[i] = *reinterpret_cast<const u32x4_t*>(p + o.off[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < R::NC; ++i) {
-      const int ci = min((int)threadIdx.x + i * kAttnThreads, KN * R::CPR - 1);
-      const int key = min(ci / R::CPR, nvalid - 1), ch = ci % R::CPR;
-      r.c[i] = *reinterpret_cast<const u32x4_t*>(p + key * rs + ch * 8);
-    }
+  for (int i = 0; i < R::NC; ++i) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(o.off[i] * 2), 0, 0);
+    r.c[i] = __builtin_bit_cast(u32x4_t, x);
   }
 }
 
@@ -296,7 +293,7 @@ struct Walker {
   static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int NQK = 2 * KSTEPS;           // QK^T MFMAs per query tile
   static constexpr int NPV = 4 * (D / 32);         // PV MFMAs per query tile
-  static constexpr int PFK = 3, PFV = 2;           // operand reads in flight
+  static constexpr int PFK = 3, PFV = 4;           // operand reads in flight
   static constexpr int NC = TileRegs<D>::NC;
   char* lds;
   const uint16_t* kbase;
