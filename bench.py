@@ -5,7 +5,7 @@ CPU oracle baseline, printed as one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload llama8b_128k] [--gpus 1]
 
 A step is one whole moba_forward (centroid pool, gate + top-k, inverted index,
-history attention, current-block attention, merge) over one batch of seeded synthetic
+history attention, current-block attention fused with the merge) over one batch of seeded synthetic
 inputs already resident in HBM.  `value` is effective TFLOP/s: 4 * head_dim * (keys
 each query head attends) summed over query heads and tokens, divided by the step time.
 The per-step times come from HIP events the library records on the launch stream
@@ -204,7 +204,7 @@ def main(argv=None):
     flop_cur = 4 * w.head_dim * heads * cur
     flop = flop_hist + flop_cur
     tflops = flop / (ms * 1e-3) / 1e12
-    attn_ms = stage["history"] + stage["current"] + stage["merge"]
+    attn_ms = stage["history"] + stage["current"]
     hist_tflops = flop_hist / (stage["history"] * 1e-3) / 1e12 if stage["history"] else None
     gbytes = gate_bytes(w)
     gate_gbs = gbytes / (stage["gate"] * 1e-3) / 1e9 if stage["gate"] else None

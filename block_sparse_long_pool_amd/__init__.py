@@ -24,7 +24,7 @@ __all__ = [
 ]
 
 # names of the steps timed by profile=True, in the library's order
-STAGES = ("pool", "gate", "index", "history", "current", "merge")
+STAGES = ("pool", "gate", "index", "history", "current")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoba.so")

@@ -1,5 +1,6 @@
-// Block-sparse attention: history blocks (gather-and-densify) and the causal current
-// block, each producing (o, lse) partials, then the log-sum-exp merge.
+// Block-sparse attention: history blocks (gather-and-densify) write (o, lse) partials;
+// the causal current block is computed last and its epilogue merges the partials by
+// log-sum-exp into the output.
 //
 // The method: each query attends the keys of its selected blocks only, the current
 // block causally ("MoBA: Mixture of Block Attention for Long-Context LLMs", paper
@@ -592,6 +593,57 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
   if (hf == 0) *pl = (st.m[qt] + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
+// Log-sum-exp merge of a row's current-block result (in registers) with its nh history
+// partials, written as the final output: L = ln(e^lse_c + sum_s e^lse_s), out =
+// e^(lse_c - L) o_c + sum_s e^(lse_s - L) o_s (bf16, round to nearest even), lse = L.
+// Lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row.
+template <int D, int QT>
+__device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, bool valid,
+                                            int nh, const float* __restrict__ po,
+                                            const float* __restrict__ pl,
+                                            uint16_t* __restrict__ orow, float* __restrict__ lrow) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const float lc = pair_sum(st.l[qt]);
+  if (!valid) return;
+  const float ln2 = 0.69314718055994530942f;
+  const float lse_c = (st.m[qt] + __log2f(lc)) * ln2;
+  float mx = lse_c;
+  for (int s = 0; s < nh; ++s) mx = fmaxf(mx, pl[s]);
+  float den = expf(lse_c - mx);
+  for (int s = 0; s < nh; ++s) den += expf(pl[s] - mx);
+  const float L = mx + logf(den);
+  const float wc = expf(lse_c - L) / lc;
+  f32x4_t acc[D / 32][4];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dt][ii][r] = st.o[qt][dt][ii * 4 + r] * wc;
+  for (int s = 0; s < nh; ++s) {
+    const float w = expf(pl[s] - L);
+    const float* ps = po + (size_t)s * D + hf * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(ps + dt * 32 + ii * 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w, x[r], acc[dt][ii][r]);
+      }
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      u32x2_t pk;
+      pk[0] = f32_to_bf16_rne(acc[dt][ii][0]) | (f32_to_bf16_rne(acc[dt][ii][1]) << 16);
+      pk[1] = f32_to_bf16_rne(acc[dt][ii][2]) | (f32_to_bf16_rne(acc[dt][ii][3]) << 16);
+      *reinterpret_cast<u32x2_t*>(orow + dt * 32 + ii * 8 + hf * 4) = pk;
+    }
+  if (hf == 0) *lrow = L;
+}
+
 template <int D, int QT>
 __device__ __forceinline__ void load_q(WaveState<D, QT>& st, int qt, const uint16_t* qrow,
                                        bool valid) {
@@ -649,7 +701,8 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
   const int ngq = ng * G;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const size_t prow = ((size_t)(b * ngq + gi * G + hlq[qt]) * T + tq[qt]) * topk + slq[qt];
+    const size_t prow =
+        ((size_t)(b * ngq + gi * G + hlq[qt]) * T + tq[qt]) * (topk - 1) + slq[qt];
     store_partial(st, qt, vq[qt], part_o + prow * D, part_lse + prow);
   }
 }
@@ -668,7 +721,8 @@ template <int D, int QT>
 __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
-    float sl, int g0, int ng, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float sl, int g0, int ng, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int c = blockIdx.y;
   const int gi = blockIdx.z % ng, b = blockIdx.z / ng;
@@ -703,60 +757,17 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
     state_init(st);
     attend_range<D, QT>(st, lds, kbase, vbase, rs, c * block, t_end, sl, active, t0, tpos);
     if (active) {
+      const int nh = min(c, topk - 1);   // history slots of every row of this block
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const size_t prow =
-            ((size_t)(b * ngq + gi * G + hl) * T + (vq[qt] ? tpos[qt] : 0)) * topk + (topk - 1);
-        store_partial(st, qt, vq[qt], part_o + prow * D, part_lse + prow);
+        const int t = vq[qt] ? tpos[qt] : 0;
+        const size_t prow = ((size_t)(b * ngq + gi * G + hl) * T + t) * (topk - 1);
+        merge_store(st, qt, vq[qt], nh, part_o + prow * D, part_lse + prow,
+                    out + ((size_t)((size_t)b * T + t) * hq + g * G + hl) * D,
+                    lse + ((size_t)b * hq + g * G + hl) * T + t);
       }
     }
   }
-}
-
-// ---------------------------------------------------------------- merge (a5)
-template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int bsz, int T,
-    int hq, int hkv, int block, int topk, int g0, int ng, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
-  constexpr int TPR = D / 4;
-  constexpr int RPB = kThreads / TPR;
-  const int G = hq / hkv, ngq = ng * G;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / TPR;
-  const size_t nrows = (size_t)bsz * ngq * T;
-  if (row >= nrows) return;
-  const int sub = threadIdx.x % TPR;
-  const int t = (int)(row % T);
-  const int hc = (int)((row / T) % ngq);
-  const int b = (int)(row / ((size_t)T * ngq));
-  const int h = g0 * G + hc;
-  const int KH = topk - 1;
-  const int nh = min(t / block, KH);
-  const float* pl = part_lse + row * topk;
-  const float* po = part_o + row * topk * D + 4 * sub;
-  float mx = pl[KH];
-  for (int s = 0; s < nh; ++s) mx = fmaxf(mx, pl[s]);
-  float den = expf(pl[KH] - mx);
-  for (int s = 0; s < nh; ++s) den += expf(pl[s] - mx);
-  const float L = mx + logf(den);
-  f32x4_t acc;
-  {
-    const float w = expf(pl[KH] - L);
-    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(po + (size_t)KH * D);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = w * x[r];
-  }
-  for (int s = 0; s < nh; ++s) {
-    const float w = expf(pl[s] - L);
-    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(po + (size_t)s * D);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += w * x[r];
-  }
-  u32x2_t pk;
-  pk[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  pk[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-  *reinterpret_cast<u32x2_t*>(out + ((size_t)((size_t)b * T + t) * hq + h) * D + 4 * sub) = pk;
-  if (sub == 0) lse[((size_t)b * hq + h) * T + t] = L;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -783,30 +794,19 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
 
 hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
-                               float* part_o, float* part_lse, hipStream_t st) {
+                               const float* part_o, const float* part_lse, uint16_t* out,
+                               float* lse, hipStream_t st) {
   const float sl = scale * 1.4426950408889634f;
   const int TT = 32 * kQT * current_subtiles(s.G());
   dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng);
   if (s.d == 128)
     hipLaunchKernelGGL((attn_current_kernel<128, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
-                       v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse);
+                       v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse,
+                       out, lse);
   else
     hipLaunchKernelGGL((attn_current_kernel<64, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
-                       v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge(const Shape& s, int g0, int ng, const float* part_o,
-                        const float* part_lse, uint16_t* out, float* lse, hipStream_t st) {
-  const size_t rows = (size_t)s.b * ng * s.G() * s.T;
-  const int rpb = kThreads / (s.d / 4);
-  dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  if (s.d == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kThreads), 0, st, part_o, part_lse,
-                       s.b, s.T, s.hq, s.hkv, s.block, s.topk, g0, ng, out, lse);
-  else
-    hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kThreads), 0, st, part_o, part_lse,
-                       s.b, s.T, s.hq, s.hkv, s.block, s.topk, g0, ng, out, lse);
+                       v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse,
+                       out, lse);
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ Layout make_layout(const Shape& s, int ng) {
   L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
-  const size_t prow = (size_t)s.b * ng * s.G() * s.T * s.topk;
+  const size_t prow = (size_t)s.b * ng * s.G() * s.T * s.KH();   // history slots only
   L.part_o = take(prow * s.d * sizeof(float));
   L.part_lse = take(prow * sizeof(float));
   L.total = off;
@@ -225,10 +225,9 @@ int forward_impl(const void* q, const void* k, const void* v, int batch, int seq
                                          po, pl, hs));
       MOBA_TRY(clock.mark(3));
     }
-    MOBA_TRY(moba::launch_attn_current(s, qb, kb, vb, scale, g0, ngc, po, pl, hs));
+    MOBA_TRY(moba::launch_attn_current(s, qb, kb, vb, scale, g0, ngc, po, pl,
+                                       static_cast<uint16_t*>(out), lse, hs));
     MOBA_TRY(clock.mark(4));
-    MOBA_TRY(moba::launch_merge(s, g0, ngc, po, pl, static_cast<uint16_t*>(out), lse, hs));
-    MOBA_TRY(clock.mark(5));
   }
   return clock.finish(stage_ms);
 }

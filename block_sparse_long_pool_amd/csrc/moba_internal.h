@@ -89,18 +89,17 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
                         int32_t* list_offsets, int32_t* tile_offsets,
                         int4* tiles, uint32_t* entries, long long cap,
                         hipStream_t st);
-// (a4) history attention partials, (a5) current block + merge
+// (a4) history attention partials, (a5) current block fused with the merge
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
                                const int4* tiles, const int32_t* tile_count,
                                int max_tiles, const uint32_t* entries, float* part_o,
                                float* part_lse, hipStream_t st);
+// the current-block kernel also merges the history partials and writes out and lse
 hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
-                               float* part_o, float* part_lse, hipStream_t st);
-hipError_t launch_merge(const Shape& s, int g0, int ng, const float* part_o,
-                        const float* part_lse, uint16_t* out, float* lse,
-                        hipStream_t st);
+                               const float* part_o, const float* part_lse, uint16_t* out,
+                               float* lse, hipStream_t st);
 int history_tile_rows();
 
 }  // namespace moba

@@ -9,7 +9,8 @@
  * LLMs", paper summary page on atlas.scime.ai, section "Approach"; MoBA README,
  * intro bullets "Trainable Block Sparse Attention" and "Parameter-less Gating
  * Mechanism").  The library splits that attention into the history blocks and the
- * causal current block and merges the two by log-sum-exp.
+ * causal current block; the current-block kernel merges the two by log-sum-exp as it
+ * writes the output.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -72,7 +73,7 @@ size_t moba_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim
 
 /* The whole prefill forward pass (paper summary page, "Approach"):
  * centroids -> gate and top-k -> inverted index -> history attention ->
- * current-block causal attention -> log-sum-exp merge.
+ * current-block causal attention fused with the log-sum-exp merge.
  * Writes out, lse and idx.  `workspace` must hold at least the minimum of
  * moba_workspace_bytes and be 256-byte aligned. */
 int moba_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
@@ -84,10 +85,10 @@ int moba_forward(const void* q, const void* k, const void* v, int batch, int seq
  * HIP events recorded on `stream` between the steps, in milliseconds, summed over
  * kv-head groups:
  *   stage_ms[0] centroid pool   [1] gate + top-k   [2] inverted index
- *   stage_ms[3] history attention   [4] current-block attention   [5] merge
+ *   stage_ms[3] history attention   [4] current-block attention + merge
  * stage_ms is a HOST array of MOBA_NUM_STAGES floats.  Meant for measurement: it
  * synchronises, unlike moba_forward. */
-#define MOBA_NUM_STAGES 6
+#define MOBA_NUM_STAGES 5
 int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
                          int seqlen, int hq, int hkv, int head_dim, int block, int topk,
                          float scale, void* out, float* lse, int32_t* idx,
