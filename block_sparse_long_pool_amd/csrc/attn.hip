@@ -40,6 +40,7 @@ namespace moba {
 #define MOBA_ATTN_NW 8
 #endif
 constexpr int kAttnWaves = MOBA_ATTN_NW;
+static_assert(kAttnWaves % 2 == 0, "the walker runs two wave groups");
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
 constexpr int KN = 64;          // keys per LDS subtile
@@ -274,20 +275,22 @@ __device__ __forceinline__ void pv_subtile(WaveState<D, QT>& st, const bf16x8_t 
   }
 }
 
-// Key-range walker.  LDS holds two K buffers and two V buffers; K runs one subtile
-// ahead of V.  Before step i the scores of subtile i are in registers and the lazy
-// rescale for them is done.  Step i:
-//   region A  the MFMAs of QK^T for subtile i+1 (K buffer (i+1)&1), each next to the
-//             operand read three slots ahead and a slice of the exp/sum work of
-//             subtile i;
-//   region B  the PV MFMAs of subtile i (V buffer i&1), each next to its transpose
-//             reads two slots ahead, a slice of the mask/max work on subtile i+1,
-//             and one staging operation: K(i+2) -> K buffer i&1, V(i+1) -> V buffer
-//             (i+1)&1, then the global loads of K(i+3) and V(i+2);
-//   then the rescale decision for subtile i+1 and one barrier.
-// The order inside the regions is fixed by sched_barrier fences.  Staging past the
-// last subtile re-reads the last subtile into a buffer nobody reads again, so the
-// steady state has no branches.
+// Key-range walker, two wave groups in ping-pong.  The workgroup's waves form two
+// groups (the two waves that share a SIMD are in different groups).  Every wave runs
+// the same sequence of phases, separated by barriers:
+//   P      QK^T of subtile 0, its mask and row max;
+//   A(i)   the MFMAs of QK^T for subtile i+1 next to the exp/sum/pack of subtile i;
+//   B(i)   the PV MFMAs of subtile i next to the mask and row max of subtile i+1,
+//          then the lazy-rescale decision for subtile i+1;
+// but group 1 starts one barrier later, so at every half-step h one wave of a SIMD is
+// in an exp-heavy A phase while the other is in an MFMA/LDS-heavy phase.  Phase
+// number f = 0 (P), 2i+1 (A(i)), 2i+2 (B(i)) runs at half-step h = f + group.
+// LDS holds two K and two V buffers.  At half-step h all threads stage one slice
+// each of one subtile, K(h/2 + 1) for even h and V(h/2) for odd h, from registers
+// loaded two half-steps before.  K(j) is read at half-steps 2j-1 and 2j (K(0) at 0
+// and 1) and V(i) at 2i+2 and 2i+3, so every buffer is rewritten only after both
+// groups are done with its previous subtile.  Staging past the last subtile
+// re-stages the last subtile into a buffer nobody reads again.
 template <int D, int QT>
 struct Walker {
   using L = Lds<D>;
@@ -296,15 +299,17 @@ struct Walker {
   static constexpr int NPV = 4 * (D / 32);         // PV MFMAs per query tile
   static constexpr int PFK = 3, PFV = 4;           // operand reads in flight
   static constexpr int NC = TileRegs<D>::NC;
+  using Scores = f32x16_t[2][QT];
+  using POps = bf16x8_t[QT][4];
   char* lds;
   const uint16_t* kbase;
   const uint16_t* vbase;
   size_t rs;
   int key_begin, key_end, nsub, diag_from;
   float sl;
-  bool active;
+  int grp;                     // 0 leads, 1 trails by one half-step
   TileOffsets<D> to;
-  TileRegs<D> rk, rv;
+  TileRegs<D> bank[2];         // staging registers of even / odd phases
 
   __device__ __forceinline__ char* kbuf(int i) const { return lds + (i & 1) * L::KBYTES; }
   __device__ __forceinline__ char* vbuf(int i) const {
@@ -315,34 +320,36 @@ struct Walker {
   __device__ __forceinline__ bool masked(int i) const {
     return kb(i) + KN > key_end || kb(i) + KN - 1 > diag_from;
   }
-  __device__ __forceinline__ void load_k(int i) {
-    i = min(i, nsub - 1);
-    tile_load<D>(rk, to, kbase + (size_t)kb(i) * rs, rs, nvalid(i));
+  // global -> registers: the subtile staged at half-step h
+  __device__ __forceinline__ void stage_load(TileRegs<D>& r, int h) {
+    const bool isv = h & 1;
+    const int t = min(isv ? h / 2 : h / 2 + 1, nsub - 1);
+    tile_load<D>(r, to, (isv ? vbase : kbase) + (size_t)kb(t) * rs, rs, nvalid(t));
   }
-  __device__ __forceinline__ void load_v(int i) {
-    i = min(i, nsub - 1);
-    tile_load<D>(rv, to, vbase + (size_t)kb(i) * rs, rs, nvalid(i));
-  }
-  // staging chunk c of the current registers: c < NC is K, else V
-  __device__ __forceinline__ void store_chunk(int c, int i) {
+  // registers -> LDS: chunk c of the subtile staged at half-step h
+  __device__ __forceinline__ void stage_store(const TileRegs<D>& r, int c, int h) {
     constexpr bool kAllThreads = (KN * TileRegs<D>::CPR) % kAttnThreads == 0;
-    const int ci = threadIdx.x + (c % NC) * kAttnThreads;
+    const int ci = threadIdx.x + c * kAttnThreads;
     if (kAllThreads || ci < KN * TileRegs<D>::CPR) {
       const int row = ci / TileRegs<D>::CPR, col = (ci % TileRegs<D>::CPR) * 16;
-      if (c < NC)
-        *reinterpret_cast<u32x4_t*>(kbuf(i) + row * L::KS + col) = rk.c[c];
-      else
-        *reinterpret_cast<u32x4_t*>(vbuf(i + 1) + row * L::VS + col) = rv.c[c - NC];
+      const bool isv = h & 1;
+      char* dst = isv ? vbuf(h / 2) + row * L::VS : kbuf(h / 2 + 1) + row * L::KS;
+      *reinterpret_cast<u32x4_t*>(dst + col) = r.c[c];
     }
+  }
+  // the staging work of a phase, spread over its MFMA slots: the stores of the
+  // subtile for half-step h, then the loads for half-step h + 2 into the same registers
+  template <int BANK>
+  __device__ __forceinline__ void stage_slot(int j, int h) {
+    if (j < NC) stage_store(bank[BANK], j, h);
+    else if (j == NC) stage_load(bank[BANK], h + 2);
   }
 
   __device__ __forceinline__ static int k_off(int j) {
     return (j / KSTEPS) * 32 * L::KS + (j % KSTEPS) * 32;
   }
 
-  // the mask and row max of a subtile's scores; returns scaled maxima in mxs
-  __device__ __forceinline__ void mask_scores(f32x16_t (&s)[2][QT], int i,
-                                              const int (&tpos)[QT]) const {
+  __device__ __forceinline__ void mask_scores(Scores& s, int i, const int (&tpos)[QT]) const {
     const int hf = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
@@ -375,38 +382,55 @@ struct Walker {
     }
   }
 
-  template <bool NEXT, bool MASKN>
-  __device__ __forceinline__ void step(WaveState<D, QT>& st, f32x16_t (&cur)[2][QT],
-                                       f32x16_t (&nxt)[2][QT], int i, const int (&tpos)[QT]) {
+  // mask, row max and rescale of subtile i's scores, all at once (after phase P)
+  __device__ __forceinline__ void max_all(WaveState<D, QT>& st, Scores& s, int i,
+                                          const int (&tpos)[QT]) {
+    if (masked(i)) mask_scores(s, i, tpos);
+    float mxs[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kk][qt][e]);
+      mxs[qt] = pair_max(mx) * sl;
+    }
+    rescale(st, mxs);
+  }
+
+  // Phase A(i) (EXP) or P (!EXP, i = -1): QK^T of subtile i+1 into nxt (when NEXT) and
+  // exp/sum/pack of cur into pb, next to the staging of half-step h.
+  template <bool NEXT, bool EXP, int BANK>
+  __device__ __forceinline__ void phase_a(WaveState<D, QT>& st, const Scores& cur,
+                                          Scores& nxt, POps& pb, int i, int h) {
     const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-    if (active) {
-      // ---------------- region A: QK^T(i+1) || exp(i)
-      constexpr int EPS = 32 / NQK;  // exp elements per slot and query tile
-      const char* kp = kbuf(i + 1) + n * L::KS + hf * 16;
-      bf16x8_t ka[NQK];
+    constexpr int EPS = 32 / NQK;  // exp elements per slot and query tile
+    const char* kp = kbuf(i + 1) + n * L::KS + hf * 16;
+    bf16x8_t ka[NQK];
+    if (NEXT) {
+#pragma unroll
+      for (int j = 0; j < PFK; ++j)
+        ka[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
+    }
+    float mref[QT], rsum[QT], p[QT][32];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      mref[qt] = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
+      rsum[qt] = 0.f;
+    }
+    const f32x16_t zero = {};
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
       if (NEXT) {
+        if (j + PFK < NQK)
+          ka[j + PFK] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j + PFK)));
+        const int kk = j / KSTEPS, ks = j % KSTEPS;
 #pragma unroll
-        for (int j = 0; j < PFK; ++j)
-          ka[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
+        for (int qt = 0; qt < QT; ++qt)
+          nxt[kk][qt] = mfma32x32x16(ka[j], st.q[qt][ks], ks == 0 ? zero : nxt[kk][qt]);
       }
-      float mref[QT], rsum[QT], p[QT][32];
-      bf16x8_t pb[QT][4];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        mref[qt] = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
-        rsum[qt] = 0.f;
-      }
-      const f32x16_t zero = {};
-#pragma unroll
-      for (int j = 0; j < NQK; ++j) {
-        if (NEXT) {
-          if (j + PFK < NQK)
-            ka[j + PFK] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j + PFK)));
-          const int kk = j / KSTEPS, ks = j % KSTEPS;
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            nxt[kk][qt] = mfma32x32x16(ka[j], st.q[qt][ks], ks == 0 ? zero : nxt[kk][qt]);
-        }
+      if (EXP) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
@@ -426,128 +450,108 @@ struct Walker {
             pb[qt][ks] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      stage_slot<BANK>(j, h);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (EXP) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) st.l[qt] += rsum[qt];
-      // ---------------- region B: PV(i) || max(i+1) || staging
-      if (NEXT && MASKN) mask_scores(nxt, i + 1, tpos);
-      const char* vp = vbuf(i) + (4 * hf + ((lane & 15) >> 2)) * L::VS +
-                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-      u32x4_t va[NPV];
-      auto vread = [&](int j) {
-        const int ks = j / (D / 32), dt = j % (D / 32);
-        const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * L::VS + dt * 64);
-        const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * L::VS + dt * 64);
-        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      };
+    }
+  }
+
+  // Phase B(i): O^T += V^T P^T for subtile i next to the mask and row max of nxt
+  // (subtile i+1, when NEXT), then the rescale decision; staging of half-step h.
+  template <bool NEXT, int BANK>
+  __device__ __forceinline__ void phase_b(WaveState<D, QT>& st, Scores& nxt, const POps& pb,
+                                          int i, int h, const int (&tpos)[QT]) {
+    const int lane = threadIdx.x & 63, hf = lane >> 5;
+    if (NEXT && masked(i + 1)) mask_scores(nxt, i + 1, tpos);
+    const char* vp = vbuf(i) + (4 * hf + ((lane & 15) >> 2)) * L::VS +
+                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    u32x4_t va[NPV];
+    auto vread = [&](int j) {
+      const int ks = j / (D / 32), dt = j % (D / 32);
+      const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * L::VS + dt * 64);
+      const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * L::VS + dt * 64);
+      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
 #pragma unroll
-      for (int j = 0; j < PFV; ++j) va[j] = vread(j);
-      constexpr int MPS = 32 / NPV;  // max elements per slot and query tile
-      float mx[QT];
+    for (int j = 0; j < PFV; ++j) va[j] = vread(j);
+    constexpr int MPS = 32 / NPV;  // max elements per slot and query tile
+    float mx[QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) mx[qt] = -INFINITY;
+    for (int qt = 0; qt < QT; ++qt) mx[qt] = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        if (j + PFV < NPV) va[j + PFV] = vread(j + PFV);
-        const int ks = j / (D / 32), dt = j % (D / 32);
+    for (int j = 0; j < NPV; ++j) {
+      if (j + PFV < NPV) va[j + PFV] = vread(j + PFV);
+      const int ks = j / (D / 32), dt = j % (D / 32);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        st.o[qt][dt] = mfma32x32x16(as_bf16x8(va[j]), pb[qt][ks], st.o[qt][dt]);
+      if (NEXT) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          st.o[qt][dt] = mfma32x32x16(as_bf16x8(va[j]), pb[qt][ks], st.o[qt][dt]);
-        if (NEXT) {
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-            for (int e = 0; e < MPS; ++e) {
-              const int x = j * MPS + e;
-              mx[qt] = fmaxf(mx[qt], nxt[x >> 4][qt][x & 15]);
-            }
-        }
-        if (j < 2 * NC) store_chunk(j, i);
-        else if (j == 2 * NC) load_k(i + 3);
-        else if (j == 2 * NC + 1) load_v(i + 2);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < MPS; ++e) {
+            const int x = j * MPS + e;
+            mx[qt] = fmaxf(mx[qt], nxt[x >> 4][qt][x & 15]);
+          }
       }
-      if (2 * NC >= NPV) {   // more staging than MFMA slots (not the case for d = 64, 128)
-#pragma unroll
-        for (int c = NPV; c < 2 * NC; ++c) store_chunk(c, i);
-        load_k(i + 3);
-        load_v(i + 2);
-      }
-      if (NEXT) {
-        float mxs[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) mxs[qt] = pair_max(mx[qt]) * sl;
-        rescale(st, mxs);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2 * NC; ++c) store_chunk(c, i);
-      load_k(i + 3);
-      load_v(i + 2);
+      stage_slot<BANK>(j, h);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (NEXT) {
+      float mxs[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mxs[qt] = pair_max(mx[qt]) * sl;
+      rescale(st, mxs);
+    }
+  }
+
+  // A(i) then B(i), cur = S(i), nxt = S(i+1); phases 2i+1 and 2i+2
+  template <bool NEXT>
+  __device__ __forceinline__ void step(WaveState<D, QT>& st, const Scores& cur, Scores& nxt,
+                                       POps& pb, int i, const int (&tpos)[QT]) {
+    phase_a<NEXT, true, 1>(st, cur, nxt, pb, i, 2 * i + 1 + grp);
+    __syncthreads();
+    phase_b<NEXT, 0>(st, nxt, pb, i, 2 * i + 2 + grp, tpos);
     __syncthreads();
   }
 
   __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT]) {
     to.init(rs);
     nsub = (key_end - key_begin + KN - 1) / KN;
-    // prologue: K(0), V(0), K(1) into LDS; K(2), V(1) into registers
-    load_k(0);
-    load_v(0);
-    tile_store<D, L::KS>(rk, kbuf(0));
-    tile_store<D, L::VS>(rv, vbuf(0));
-    load_k(1);
-    tile_store<D, L::KS>(rk, kbuf(1));   // duplicate of K(0) when nsub == 1, unused
-    load_v(1);
-    load_k(2);
+    // prologue: K(0) into LDS.  Group 1 waits out half-step 0, so it stages its slices
+    // of that half-step's subtile (K(1)) now.  Then the registers for the first two
+    // phases: the subtiles of half-steps grp and grp + 1.
+    tile_load<D>(bank[0], to, kbase + (size_t)kb(0) * rs, rs, nvalid(0));
+    tile_store<D, L::KS>(bank[0], kbuf(0));
+    if (grp) {
+      stage_load(bank[0], 0);
+      for (int c = 0; c < NC; ++c) stage_store(bank[0], c, 0);
+    }
+    stage_load(bank[0], grp);
+    stage_load(bank[1], grp + 1);
     __syncthreads();
-    f32x16_t sa[2][QT], sb[2][QT];
-    if (active) {
-      const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-      const char* kp = kbuf(0) + n * L::KS + hf * 16;
-      const f32x16_t zero = {};
-#pragma unroll
-      for (int j = 0; j < NQK; ++j) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
-        const int kk = j / KSTEPS, ks = j % KSTEPS;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          sa[kk][qt] = mfma32x32x16(a, st.q[qt][ks], ks == 0 ? zero : sa[kk][qt]);
-      }
-      if (masked(0)) mask_scores(sa, 0, tpos);
-      float mxs[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[kk][qt][e]);
-        mxs[qt] = pair_max(mx) * sl;
-      }
-      rescale(st, mxs);
-    }
-    __syncthreads();   // K buffer 0 is rewritten in step 0
-    // subtiles needing the mask are a suffix: [nplain, nsub)
-    int nplain = 0;
-    while (nplain < nsub && !masked(nplain)) ++nplain;
+    if (grp) __syncthreads();            // group 1 trails by one half-step
+    Scores sa, sb;
+    POps pb;
+    phase_a<true, false, 0>(st, sa, sa, pb, -1, grp);   // P
+    max_all(st, sa, 0, tpos);
+    __syncthreads();
     int i = 0;
-    for (; i + 1 < min(nplain, nsub); ++i) {
-      step<true, false>(st, sa, sb, i, tpos);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) sa[kk][qt] = sb[kk][qt];
+    for (; i + 2 < nsub; i += 2) {
+      step<true>(st, sa, sb, pb, i, tpos);
+      step<true>(st, sb, sa, pb, i + 1, tpos);
     }
-    for (; i + 1 < nsub; ++i) {
-      step<true, true>(st, sa, sb, i, tpos);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) sa[kk][qt] = sb[kk][qt];
+    if (i + 1 < nsub) {
+      step<true>(st, sa, sb, pb, i, tpos);
+      step<false>(st, sb, sa, pb, i + 1, tpos);
+    } else {
+      step<false>(st, sa, sb, pb, i, tpos);
     }
-    step<false, false>(st, sa, sb, nsub - 1, tpos);
+    if (!grp) __syncthreads();           // group 0's share of the last half-step
   }
 };
 
@@ -559,7 +563,7 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
                                              const uint16_t* __restrict__ kbase,
                                              const uint16_t* __restrict__ vbase, size_t rs,
                                              int key_begin, int key_end, float sl,
-                                             bool active, int diag_from, const int (&tpos)[QT]) {
+                                             int diag_from, const int (&tpos)[QT]) {
   Walker<D, QT> w;
   w.lds = lds;
   w.kbase = kbase;
@@ -569,7 +573,14 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
   w.key_end = key_end;
   w.diag_from = diag_from;
   w.sl = sl;
-  w.active = active;
+  // waves w and w + kAttnWaves/2 share a SIMD (waves are dealt to SIMDs in turn), so
+  // the halves of the workgroup are the two groups
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#if MOBA_ATTN_GROUP_BY_PARITY
+  w.grp = wave & 1;
+#else
+  w.grp = wave / (kAttnWaves / 2);
+#endif
   w.run(st, tpos);
 }
 
@@ -696,7 +707,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
   const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
   const int key_begin = j * block;
-  attend_range<D, QT>(st, lds, kbase, vbase, rs, key_begin, key_begin + block, sl, true,
+  attend_range<D, QT>(st, lds, kbase, vbase, rs, key_begin, key_begin + block, sl,
                       0x7fffffff, tpos);
   const int ngq = ng * G;
 #pragma unroll
@@ -755,7 +766,9 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
       load_q(st, qt, qrow, vq[qt]);
     }
     state_init(st);
-    attend_range<D, QT>(st, lds, kbase, vbase, rs, c * block, t_end, sl, active, t0, tpos);
+    // waves without a head this round run on zero queries: every wave takes part in
+    // every phase and barrier of the walker
+    attend_range<D, QT>(st, lds, kbase, vbase, rs, c * block, t_end, sl, t0, tpos);
     if (active) {
       const int nh = min(c, topk - 1);   // history slots of every row of this block
 #pragma unroll
