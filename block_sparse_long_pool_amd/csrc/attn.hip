@@ -584,10 +584,11 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
   w.run(st, tpos);
 }
 
-// normalise and store one query tile's partial (o fp32 [D], lse natural log)
+// normalise and store one query tile's partial: o rounded to bf16 (nearest even) [D],
+// lse (natural log) in fp32
 template <int D, int QT>
 __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt, bool valid,
-                                              float* __restrict__ po, float* __restrict__ pl) {
+                                              uint16_t* __restrict__ po, float* __restrict__ pl) {
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const float ltot = pair_sum(st.l[qt]);
   if (!valid) return;
@@ -596,10 +597,10 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      f32x4_t w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = st.o[qt][dt][ii * 4 + r] * inv;
-      *reinterpret_cast<f32x4_t*>(po + dt * 32 + ii * 8 + hf * 4) = w;
+      const f32x16_t& o = st.o[qt][dt];
+      const u32x2_t w = {pack_bf16x2(o[ii * 4] * inv, o[ii * 4 + 1] * inv),
+                         pack_bf16x2(o[ii * 4 + 2] * inv, o[ii * 4 + 3] * inv)};
+      *reinterpret_cast<u32x2_t*>(po + dt * 32 + ii * 8 + hf * 4) = w;
     }
   if (hf == 0) *pl = (st.m[qt] + __log2f(ltot)) * 0.69314718055994530942f;
 }
@@ -610,7 +611,7 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
 // Lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row.
 template <int D, int QT>
 __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, bool valid,
-                                            int nh, const float* __restrict__ po,
+                                            int nh, const uint16_t* __restrict__ po,
                                             const float* __restrict__ pl,
                                             uint16_t* __restrict__ orow, float* __restrict__ lrow) {
   const int lane = threadIdx.x & 63, hf = lane >> 5;
@@ -633,14 +634,16 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
       for (int r = 0; r < 4; ++r) acc[dt][ii][r] = st.o[qt][dt][ii * 4 + r] * wc;
   for (int s = 0; s < nh; ++s) {
     const float w = expf(pl[s] - L);
-    const float* ps = po + (size_t)s * D + hf * 4;
+    const uint16_t* ps = po + (size_t)s * D + hf * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(ps + dt * 32 + ii * 8);
+        const u32x2_t x = *reinterpret_cast<const u32x2_t*>(ps + dt * 32 + ii * 8);
+        const float xf[4] = {__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                             __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w, x[r], acc[dt][ii][r]);
+        for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w, xf[r], acc[dt][ii][r]);
       }
   }
 #pragma unroll
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int tile_id = blockIdx.x;
   if (tile_id >= *tile_count) return;
@@ -732,7 +735,7 @@ template <int D, int QT>
 __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
-    float sl, int g0, int ng, const float* __restrict__ part_o,
+    float sl, int g0, int ng, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int c = blockIdx.y;
@@ -790,7 +793,7 @@ int history_tile_rows() { return kAttnWaves * 32 * kQT; }
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
                                const int4* tiles, const int32_t* tile_count,
-                               int max_tiles, const uint32_t* entries, float* part_o,
+                               int max_tiles, const uint32_t* entries, uint16_t* part_o,
                                float* part_lse, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const float sl = scale * 1.4426950408889634f;
@@ -807,7 +810,7 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
 
 hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
-                               const float* part_o, const float* part_lse, uint16_t* out,
+                               const uint16_t* part_o, const float* part_lse, uint16_t* out,
                                float* lse, hipStream_t st) {
   const float sl = scale * 1.4426950408889634f;
   const int TT = 32 * kQT * current_subtiles(s.G());

@@ -79,7 +79,7 @@ Layout make_layout(const Shape& s, int ng) {
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
   const size_t prow = (size_t)s.b * ng * s.G() * s.T * s.KH();   // history slots only
-  L.part_o = take(prow * s.d * sizeof(float));
+  L.part_o = take(prow * s.d * sizeof(uint16_t));   // bf16 partial outputs
   L.part_lse = take(prow * sizeof(float));
   L.total = off;
   return L;
@@ -207,7 +207,7 @@ int forward_impl(const void* q, const void* k, const void* v, int batch, int seq
   for (int g0 = 0; g0 < hkv; g0 += ng) {
     const int ngc = ng < hkv - g0 ? ng : hkv - g0;
     const int nlc = s.b * ngc * s.nb();
-    float* po = reinterpret_cast<float*>(ws + L.part_o);
+    uint16_t* po = reinterpret_cast<uint16_t*>(ws + L.part_o);
     float* pl = reinterpret_cast<float*>(ws + L.part_lse);
     if (s.KH() > 0) {
       int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);

@@ -93,12 +93,12 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
                                const int4* tiles, const int32_t* tile_count,
-                               int max_tiles, const uint32_t* entries, float* part_o,
+                               int max_tiles, const uint32_t* entries, uint16_t* part_o,
                                float* part_lse, hipStream_t st);
 // the current-block kernel also merges the history partials and writes out and lse
 hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
-                               const float* part_o, const float* part_lse, uint16_t* out,
+                               const uint16_t* part_o, const float* part_lse, uint16_t* out,
                                float* lse, hipStream_t st);
 int history_tile_rows();
 

@@ -57,8 +57,8 @@ def test_check_args_codes(moba):
 def test_workspace_sizes(moba):
     full, mn = moba.workspace_bytes(1, 131072, 32, 8, 128, 4096, 12)
     assert 0 < mn < full
-    # history partials dominate: [Hq, T, topk - 1, d] float32 for all heads
-    assert full > 32 * 131072 * 11 * 128 * 4
+    # history partials dominate: [Hq, T, topk - 1, d] bf16 for all heads
+    assert full > 32 * 131072 * 11 * 128 * 2
     assert mn < full / 4
     assert moba.workspace_bytes(1, 130, 1, 1, 64, 16, 2) == (0, 0)
 
