@@ -9,30 +9,33 @@
 // blocks j < c = t / block compete; ties go to the lower block index; rows with
 // c <= topk-1 take every block 0..c without scoring (their queries are never read).
 //
-// Mapping.  A wavefront owns 32 query rows r = t*G + h%G of one kv-head g and
-// computes S^T = C Q^T on MFMA 32x32x16 (rows = 32 blocks, columns = 32 queries).
-// The centroid is float32; it enters the MFMA as bf16 hi + bf16 lo (two products
-// into one float32 accumulator), the query is bf16 already.  Lane l then holds 16
-// scores of query l%32 (blocks (i/4)*8 + (l/32)*4 + i%4).
+// Mapping.  A wavefront owns 64 consecutive tokens of one query head h (kv-head g)
+// and computes S^T = C Q^T on MFMA 32x32x16 for two tiles of 32 queries (rows = 32
+// blocks, columns = 32 queries).  The centroid is float32; it enters the MFMA as bf16
+// hi + bf16 lo (two products into one float32 accumulator), the query is bf16 already.
+// In each tile lane l holds 16 scores of query l%32 (blocks (i/4)*8 + (l/32)*4 + i%4);
+// one lane-half swap per accumulator register then gives lane l all 32 scores of
+// query t0 + l, so every lane ranks one row on its own and the wavefront's idx rows
+// are one contiguous run.
 //
 // Ranking.  Each score becomes a 32-bit key whose high bits order like the float and
 // whose low nbits hold (mask - j), so larger key = better, and exactly equal scores
 // rank the lower block first.  Scores closer than ~2^-(23-nbits) relative compare
-// as equal (well inside the 1e-3-relative near-tie band).  Each lane sorts its 16
-// keys with a bitonic network and merges them into a running sorted top-KHMAX list;
-// the two lanes of a query merge their lists at the end.  No branch depends on the
-// data, so the wavefront never diverges.
+// as equal (well inside the 1e-3-relative near-tie band).  Per 32-block tile a lane
+// sorts its keys with bitonic networks and merges them into a running sorted
+// top-KHMAX list.  No branch depends on the data, so the wavefront never diverges.
 #include "moba_internal.h"
 
 namespace moba {
 
 namespace {
 
-__device__ __forceinline__ uint32_t gate_key(float s, int j, uint32_t mask) {
-  uint32_t u = __float_as_uint(s);
-  if (u == 0x80000000u) u = 0u;  // -0 ranks like +0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (u & ~mask) | (mask - (uint32_t)j);
+// jbits = mask - j: the block's rank bits
+__device__ __forceinline__ uint32_t gate_key(float s, uint32_t jbits, uint32_t mask) {
+  const uint32_t u = __float_as_uint(s + 0.f);  // -0 + 0 = +0: ranks like +0
+  // negative: all bits flipped; non-negative: sign bit set -> unsigned order = float order
+  const uint32_t m = (uint32_t)((int32_t)u >> 31) | 0x80000000u;
+  return ((u ^ m) & ~mask) | jbits;
 }
 
 template <int N>
@@ -97,110 +100,201 @@ __device__ __forceinline__ void bitonic_sort_asc(int (&a)[N]) {
 
 }  // namespace
 
-// KHMAX: list length (16 or 32) >= topk-1.  D: head_dim.
+// Query operands of one chunk (64 tokens t0 .. t0+63 of head h, batch b): tile qt,
+// k-step s holds dims 16*s + 8*hf .. +7 of token t0 + 32*qt + n.  Loads go through a
+// buffer descriptor of the chunk's rows (zero size when not needed), so rows past T
+// read as zeros.
+template <int D>
+__device__ __forceinline__ void gate_load_q(bf16x8_t (&bq)[2][D / 16],
+                                            const uint16_t* __restrict__ q, int T, int hq,
+                                            int b, int h, int t0, bool needed) {
+  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  const uint16_t* base = q + ((size_t)((size_t)b * T + t0) * hq + h) * D;
+  const int rows = min(64, T - t0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0,
+      needed ? (int)(rows * hq * D * sizeof(uint16_t)) : 0, 0x00020000);
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int off = ((32 * qt + n) * hq * D + 16 * s + 8 * hf) * (int)sizeof(uint16_t);
+      bq[qt][s] = as_bf16x8(__builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0)));
+    }
+}
+
+struct GateChunk {
+  int b, h, t0;
+  bool compete;  // some row has more causal history blocks than slots
+};
+
+__device__ __forceinline__ GateChunk gate_chunk_of(int cid, int T, int hq, int block, int KH) {
+  const int nct = (T + 63) / 64;
+  GateChunk k;
+  k.t0 = (cid % nct) * 64;
+  k.h = (cid / nct) % hq;
+  k.b = cid / (nct * hq);
+  k.compete = min(k.t0 + 63, T - 1) / block > KH;
+  return k;
+}
+
+// Rank one chunk (its rows compete) with its query operands bq.
 template <int D, int KHMAX>
-__global__ __launch_bounds__(kThreads) void gate_topk_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
-    const uint16_t* __restrict__ clo, int T, int hq, int hkv, int block, int nb,
-    int topk, int nbits, int32_t* __restrict__ idx) {
+__device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], const GateChunk& k,
+                                           const uint16_t* __restrict__ chi,
+                                           const uint16_t* __restrict__ clo, int T, int hq,
+                                           int hkv, int block, int nb, int topk, int nbits,
+                                           int32_t* __restrict__ idx) {
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
-  const int G = hq / hkv;
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 31, hf = lane >> 5;
-  const int r = (blockIdx.x * 4 + wave) * 32 + n;
-  const int t = r / G, hl = r % G, h = g * G + hl;
+  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  const int G = hq / hkv, g = k.h / G;
+  const int t = k.t0 + lane;  // the row this lane ranks and writes
   const bool valid = t < T;
   const int c = valid ? t / block : 0;
   const int KH = topk - 1;
-  // does any row of this wavefront have more candidates than slots?
-  const bool compete = valid && c > KH;
-  const bool wave_compete = __ballot(compete) != 0ull;
+  int32_t* row = idx + ((size_t)(k.b * hq + k.h) * T + (valid ? t : 0)) * topk;
 
-  int32_t* row = idx + ((size_t)(b * hq + h) * T + (valid ? t : 0)) * topk;
-
-  if (!wave_compete) {
-    // every causal block is selected: 0..c, then -1
-    if (valid && hf == 0) {
-      for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
-    }
-    return;
-  }
-
-  // query operand: dims 16*s + 8*hf .. +7 of row (t, h)
-  bf16x8_t bq[KS];
-  {
-    const uint16_t* qp = q + ((size_t)((size_t)b * T + (valid ? t : 0)) * hq + h) * D + 8 * hf;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
-      if (!valid) v = u32x4_t{0u, 0u, 0u, 0u};
-      bq[s] = as_bf16x8(v);
-    }
-  }
   const uint32_t mask = (1u << nbits) - 1u;
   uint32_t L[KHMAX];
 #pragma unroll
   for (int p = 0; p < KHMAX; ++p) L[p] = 0u;
 
   const int cmax = wave_max_i32(c);
-  const size_t cbase = (size_t)(b * hkv + g) * nb;
+  const size_t cbase = (size_t)(k.b * hkv + g) * nb;
   for (int jt = 0; jt * 32 < cmax; ++jt) {
     const int jrow = min(jt * 32 + n, nb - 1);
     const uint16_t* ph = chi + (cbase + jrow) * D + 8 * hf;
     const uint16_t* pl = clo + (cbase + jrow) * D + 8 * hf;
-    f32x16_t acc;
+    f32x16_t acc0, acc1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ph + 16 * s));
       const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pl + 16 * s));
-      acc = mfma32x32x16(ah, bq[s], acc);
-      acc = mfma32x32x16(al, bq[s], acc);
+      acc0 = mfma32x32x16(ah, bq[0][s], acc0);
+      acc1 = mfma32x32x16(ah, bq[1][s], acc1);
+      acc0 = mfma32x32x16(al, bq[0][s], acc0);
+      acc1 = mfma32x32x16(al, bq[1][s], acc1);
     }
-    uint32_t N16[16];
+    // Lane halves swap: lane l < 32 keeps tile 0's scores of query l and receives the
+    // other half of them from lane l + 32; lane l >= 32 receives tile 1's first half of
+    // query l from lane l - 32 and keeps the second.  A[i] then holds block
+    // (i/4)*8 + i%4 and B[i] block (i/4)*8 + 4 + i%4 of this tile, for query t0 + lane.
+    uint32_t A[16], B[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int j = jt * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-      N16[i] = (j < c) ? gate_key(acc[i], j, mask) : 0u;
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[i]),
+                                                      __float_as_uint(acc1[i]), false, false);
+      const int ja = jt * 32 + (i >> 2) * 8 + (i & 3), jb = ja + 4;
+      A[i] = ja < c ? gate_key(__uint_as_float(r[0]), mask - ja, mask) : 0u;
+      B[i] = jb < c ? gate_key(__uint_as_float(r[1]), mask - jb, mask) : 0u;
     }
-    bitonic_sort_desc(N16);
-    // running list (descending) + reversed new sorted run -> bitonic top-KHMAX
+    bitonic_sort_desc(A);
+    bitonic_sort_desc(B);
+    if (KHMAX == 16) {
+      // top 16 of the tile: A descending + B reversed is bitonic after the max
 #pragma unroll
-    for (int p = KHMAX - 16; p < KHMAX; ++p) L[p] = max(L[p], N16[KHMAX - 1 - p]);
+      for (int p = 0; p < 16; ++p) A[p] = max(A[p], B[15 - p]);
+      bitonic_merge_desc(A);
+      if (jt == 0) {
+#pragma unroll
+        for (int p = 0; p < 16; ++p) L[KHMAX - 16 + p] = A[p];
+        continue;
+      }
+#pragma unroll
+      for (int p = 0; p < 16; ++p) L[KHMAX - 16 + p] = max(L[KHMAX - 16 + p], A[15 - p]);
+    } else {
+      // all 32 keys of the tile, sorted: merge A and reversed B (a bitonic sequence)
+      uint32_t M[32];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        M[p] = A[p];
+        M[16 + p] = B[15 - p];
+      }
+      bitonic_merge_desc(M);
+      if (jt == 0) {
+#pragma unroll
+        for (int p = 0; p < 32; ++p) L[KHMAX - 32 + p] = M[p];
+        continue;
+      }
+#pragma unroll
+      for (int p = 0; p < 32; ++p) L[KHMAX - 32 + p] = max(L[KHMAX - 32 + p], M[31 - p]);
+    }
+    // running list (descending) + reversed sorted tile list -> bitonic -> sorted
     bitonic_merge_desc(L);
   }
-  // merge with the other half of the query's blocks (lane ^ 32)
-#pragma unroll
-  for (int p = 0; p < KHMAX; ++p) {
-    const uint32_t other = xor32_u32(L[KHMAX - 1 - p]);
-    L[p] = max(L[p], other);
-  }
-  bitonic_merge_desc(L);
 
   if (!valid) return;
-  // the best KH keys -> block ids, ascending; empty slots sort last
+  // the best KH keys -> block ids, ascending
   int J[KHMAX];
+  if (nb <= 32) {
+    // a bit per selected block, then the set bits from the lowest up
+    uint32_t sel = 0u;
 #pragma unroll
-  for (int p = 0; p < KHMAX; ++p) {
-    const bool keep = p < KH && L[p] != 0u;
-    J[p] = keep ? (int)(mask - (L[p] & mask)) : 0x7fffffff;
-  }
-  bitonic_sort_asc(J);
-  const int nh = min(c, KH);
-  // lanes hf = 0 / 1 write the first / second half of the row
-  const int half = (topk + 1) >> 1;
-  const int p0 = hf ? half : 0, p1 = hf ? topk : half;
+    for (int p = 0; p < KHMAX; ++p)
+      if (p < KH && L[p] != 0u) sel |= 1u << (mask - (L[p] & mask));
 #pragma unroll
-  for (int p = 0; p <= KHMAX; ++p) {
-    if (p >= p0 && p < p1) {
-      int val;
-      if (p < nh) val = J[p < KHMAX ? p : 0];
-      else val = (p == nh) ? c : -1;
-      row[p] = val;
+    for (int p = 0; p < KHMAX; ++p) {
+      J[p] = (int)__builtin_ctz(sel | 0x80000000u);
+      sel &= sel - 1u;
     }
+  } else {
+    // empty slots sort last
+#pragma unroll
+    for (int p = 0; p < KHMAX; ++p) {
+      const bool keep = p < KH && L[p] != 0u;
+      J[p] = keep ? (int)(mask - (L[p] & mask)) : 0x7fffffff;
+    }
+    bitonic_sort_asc(J);
   }
+  const int nh = min(c, KH);
+  // the row: nh history blocks ascending, the current block, then -1
+  if ((topk & 3) == 0) {
+#pragma unroll
+    for (int p4 = 0; p4 * 4 <= KHMAX; ++p4) {
+      if (p4 * 4 < topk) {
+        int v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = p4 * 4 + e;
+          v[e] = p < nh ? J[p < KHMAX ? p : 0] : (p == nh ? c : -1);
+        }
+        *reinterpret_cast<int4*>(row + p4 * 4) = make_int4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p <= KHMAX; ++p)
+      if (p < topk) row[p] = p < nh ? J[p < KHMAX ? p : 0] : (p == nh ? c : -1);
+  }
+}
+
+// KHMAX: list length (16 or 32) >= topk-1.  D: head_dim.  One wavefront per chunk.
+// three wavefronts per SIMD: the loads of one chunk hide behind the ranking of others
+template <int D, int KHMAX>
+__global__ __launch_bounds__(kThreads, 3) void gate_topk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
+    const uint16_t* __restrict__ clo, int batch, int T, int hq, int hkv, int block, int nb,
+    int topk, int nbits, int32_t* __restrict__ idx) {
+  const int nchunks = batch * hq * ((T + 63) / 64);
+  const int cid = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (cid >= nchunks) return;
+  const GateChunk k = gate_chunk_of(cid, T, hq, block, topk - 1);
+  if (!k.compete) {
+    // every causal block is selected: 0..c, then -1
+    const int t = k.t0 + (threadIdx.x & 63);
+    if (t < T) {
+      const int c = t / block;
+      int32_t* row = idx + ((size_t)(k.b * hq + k.h) * T + t) * topk;
+      for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
+    }
+    return;
+  }
+  bf16x8_t bq[2][D / 16];
+  gate_load_q<D>(bq, q, T, hq, k.b, k.h, k.t0, true);
+  gate_chunk<D, KHMAX>(bq, k, chi, clo, T, hq, hkv, block, nb, topk, nbits, idx);
 }
 
 hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
@@ -208,12 +302,14 @@ hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
   const int nb = s.nb();
   int nbits = 1;
   while ((1 << nbits) < nb) ++nbits;
-  const long rows = (long)s.T * s.G();
-  dim3 grid((unsigned)((rows + 127) / 128), s.hkv, s.b);
+  // a wavefront per 64-token chunk of one query head
+  const long nchunks = (long)s.b * s.hq * ((s.T + 63) / 64);
+  const int per_block = kThreads / 64;
+  dim3 grid((unsigned)((nchunks + per_block - 1) / per_block));
   const int KH = s.KH();
 #define MOBA_GATE(DD, KK)                                                            \
   hipLaunchKernelGGL((gate_topk_kernel<DD, KK>), grid, dim3(kThreads), 0, st, q, chi, \
-                     clo, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits, idx)
+                     clo, s.b, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits, idx)
   if (s.d == 128) {
     if (KH <= 16) MOBA_GATE(128, 16);
     else MOBA_GATE(128, 32);
