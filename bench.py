@@ -5,11 +5,12 @@ CPU oracle baseline, printed as one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload llama8b_128k] [--gpus 1]
 
 A step is one whole moba_forward (centroid pool, gate + top-k, inverted index,
-history attention, current-block attention fused with the merge) over one batch of seeded synthetic
-inputs already resident in HBM.  `value` is effective TFLOP/s: 4 * head_dim * (keys
-each query head attends) summed over query heads and tokens, divided by the step time.
-The per-step times come from HIP events the library records on the launch stream
-(moba_forward_profile) in extra profiled steps after the timed ones.
+history attention, current-block attention fused with the merge) over one batch of
+seeded synthetic inputs already resident in HBM.  `value` is effective TFLOP/s:
+4 * head_dim * (keys each query head attends) summed over query heads and tokens,
+divided by the step time.  The per-stage times (and so the roofline of the history
+attention kernel) come from HIP events that the library records on the launch stream
+at the stage boundaries of every timed step (moba_forward_timed, no synchronisation).
 """
 from __future__ import annotations
 
@@ -42,13 +43,18 @@ def pair_counts(T: int, B: int, k: int):
     return hist, cur
 
 
-def gate_bytes(w) -> int:
-    """Bytes the gate must move: query rows that have more causal history blocks than
-    slots (the others select every causal block without a score), the idx rows, and
-    the bf16 hi/lo centroids."""
+def gate_bytes(w, needed_only: bool) -> int:
+    """Bytes of the gate step: every query row read once, the idx rows written, and the
+    centroids (read as bf16 hi + lo, the size of fp32).  With needed_only, only the
+    query rows that have more causal history blocks than slots are counted: the others
+    select every causal block without a score, and the kernel never reads them."""
     nb = w.seqlen // w.block
-    competing_rows = w.batch * w.hq * w.block * sum(1 for c in range(nb) if c > w.topk - 1)
-    q = competing_rows * w.head_dim * 2
+    rows_per_block = w.batch * w.hq * w.block
+    if needed_only:
+        q_rows = rows_per_block * sum(1 for c in range(nb) if c > w.topk - 1)
+    else:
+        q_rows = rows_per_block * nb
+    q = q_rows * w.head_dim * 2
     idx = w.batch * w.hq * w.seqlen * w.topk * 4
     cent = w.batch * w.hkv * nb * w.head_dim * 2 * 2
     return q + idx + cent
@@ -123,8 +129,6 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_128k")
-    ap.add_argument("--profile-steps", type=int, default=None,
-                    help="extra steps timed per stage (default: --steps)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -159,9 +163,9 @@ def main(argv=None):
     full_ws, _ = moba.workspace_bytes(w.batch, w.seqlen, w.hq, w.hkv, w.head_dim, w.block,
                                       w.topk)
 
-    def step(profile=False):
+    def step(events=None):
         return moba.forward(q, k, v, w.block, w.topk, w.sm_scale, workspace=ws, out=out,
-                            lse=lse, idx=idx, profile=profile)
+                            lse=lse, idx=idx, events=events)
 
     print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
@@ -170,11 +174,17 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    # stage-boundary events for every timed step; one record each creates the HIP event
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(moba.STAGES) + 1)]
+           for _ in range(a.steps)]
+    for evs in sev:
+        for e in evs:
+            e.record(stream)
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(a.steps):
-        step()
+    for i in range(a.steps):
+        step(events=sev[i])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
@@ -190,12 +200,8 @@ def main(argv=None):
               file=sys.stderr, flush=True)
         del src, dst
 
-    n_prof = a.steps if a.profile_steps is None else a.profile_steps
-    stage = {s: 0.0 for s in moba.STAGES}
-    for _ in range(n_prof):
-        *_, st = step(profile=True)
-        for s_ in stage:
-            stage[s_] += st[s_] / n_prof
+    stage = {s_: sum(sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(a.steps)) / a.steps
+             for j, s_ in enumerate(moba.STAGES)}
     print(f"[bench] {ms:.3f} ms/step; stages {stage}", file=sys.stderr, flush=True)
 
     hist, cur = pair_counts(w.seqlen, w.block, w.topk)
@@ -206,8 +212,11 @@ def main(argv=None):
     tflops = flop / (ms * 1e-3) / 1e12
     attn_ms = stage["history"] + stage["current"]
     hist_tflops = flop_hist / (stage["history"] * 1e-3) / 1e12 if stage["history"] else None
-    gbytes = gate_bytes(w)
-    gate_gbs = gbytes / (stage["gate"] * 1e-3) / 1e9 if stage["gate"] else None
+    gbytes = gate_bytes(w, needed_only=False)
+    gbytes_needed = gate_bytes(w, needed_only=True)
+    gate_s = stage["gate"] * 1e-3
+    gate_gbs = gbytes / gate_s / 1e9 if gate_s else None
+    gate_gbs_needed = gbytes_needed / gate_s / 1e9 if gate_s else None
     # history attention runs once per kv-head group; one launch covers all of them when
     # the workspace holds every head (it does for this workload)
     one_launch = ws.numel() >= full_ws
@@ -246,6 +255,10 @@ def main(argv=None):
         "gate_gbs": gate_gbs,
         "gate_frac_of_hbm_peak": gate_gbs / PEAK_HBM_GBS if gate_gbs else None,
         "gate_algorithmic_bytes": gbytes,
+        "gate_needed_bytes": gbytes_needed,
+        "gate_needed_gbs": gate_gbs_needed,
+        "gate_needed_frac_of_hbm_peak": (gate_gbs_needed / PEAK_HBM_GBS
+                                         if gate_gbs_needed else None),
         "roofline": roofline,
         "cpu_baseline": None,
     }

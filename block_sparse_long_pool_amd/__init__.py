@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_PKG, "libmoba.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_pool_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python block_sparse_long_pool_amd/build.py` "
         "(hipcc --offload-arch=gfx950).  There is no fallback implementation.")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -44,6 +44,8 @@ _SIGS = {
                           _vp, _sz, _vp]),
     "moba_forward_profile": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                   _vp, _vp, _sz, _vp, ctypes.POINTER(_f)]),
+    "moba_forward_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
+                                _vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "moba_strerror": (ctypes.c_char_p, [_i]),
     "moba_stage_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moba_pool_centroids": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -148,10 +150,13 @@ def alloc_workspace(q, k, block: int, topk: int, max_workspace_bytes: int | None
 
 def forward(q, k, v, block: int, topk: int, scale: float | None = None, workspace=None,
             max_workspace_bytes: int | None = None, out=None, lse=None, idx=None,
-            profile: bool = False):
+            profile: bool = False, events=None):
     """MoBA prefill forward.  Returns (out bf16, lse fp32, idx int32), and with
     ``profile=True`` also a dict of per-step GPU milliseconds (HIP events on the
-    current stream; the call then synchronises).
+    current stream; the call then synchronises).  ``events``: len(STAGES) + 1
+    torch.cuda.Event(enable_timing=True), each recorded once before (so that its HIP
+    event exists); the library records them at the step boundaries on the current
+    stream without synchronising.
 
     Outputs and the workspace are allocated with torch unless given."""
     torch = _torch()
@@ -189,6 +194,11 @@ def forward(q, k, v, block: int, topk: int, scale: float | None = None, workspac
         if profile:
             ms = (ctypes.c_float * len(STAGES))()
             st = lib.moba_forward_profile(*args, ms)
+        elif events is not None:
+            if len(events) != len(STAGES) + 1:
+                raise ValueError(f"events: need {len(STAGES) + 1} events")
+            handles = (_vp * len(events))(*[e.cuda_event for e in events])
+            st = lib.moba_forward_timed(*args, handles)
         else:
             st = lib.moba_forward(*args)
     _raise(st, "moba_forward")

@@ -1,6 +1,6 @@
 """Compile libmoba.so for gfx950 in-tree: one hipcc job per source, then a link.
 
-    python -m block_sparse_long_pool_amd.build [--jobs N] [--verbose]
+    python block_sparse_long_pool_amd/build.py [--jobs N] [--verbose]
 """
 from __future__ import annotations
 

@@ -137,14 +137,23 @@ const char* moba_strerror(int status) {
 namespace {
 
 // Records HIP events at stage boundaries on the launch stream when profiling.
+// Stage boundaries as HIP events on the launch stream.  Either the clock owns its
+// events and sums the stage times at the end (synchronising), or the caller gives
+// MOBA_NUM_STAGES + 1 events that are only recorded: ext[0] at the start and
+// ext[i + 1] after stage i (the last kv-head group's boundaries when there are several).
 struct StageClock {
   hipStream_t st;
-  bool on;
+  bool on = false;
+  hipEvent_t const* ext = nullptr;
   int n = 0;
   int stage[64];
   hipEvent_t ev[65];
-  bool begin(hipStream_t s, bool enable) {
+  bool begin(hipStream_t s, bool enable, void* const* external) {
     st = s;
+    if (external) {
+      ext = reinterpret_cast<hipEvent_t const*>(external);
+      return hipEventRecord(ext[0], st) == hipSuccess;
+    }
     on = enable;
     if (!on) return true;
     for (int i = 0; i < 65; ++i)
@@ -152,6 +161,7 @@ struct StageClock {
     return hipEventRecord(ev[0], st) == hipSuccess;
   }
   hipError_t mark(int which) {
+    if (ext) return hipEventRecord(ext[which + 1], st);
     if (!on || n >= 64) return hipSuccess;
     stage[n] = which;
     return hipEventRecord(ev[++n], st);
@@ -174,7 +184,8 @@ struct StageClock {
 int forward_impl(const void* q, const void* k, const void* v, int batch, int seqlen,
                  int hq, int hkv, int head_dim, int block, int topk, float scale,
                  void* out, float* lse, int32_t* idx, void* workspace,
-                 size_t workspace_bytes, void* stream, float* stage_ms) {
+                 size_t workspace_bytes, void* stream, float* stage_ms,
+                 void* const* stage_events) {
   int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
   if (st != MOBA_OK) return st;
   if (!q || !k || !v || !out || !lse || !idx || !workspace) return MOBA_ERR_INVALID_ARG;
@@ -196,7 +207,7 @@ int forward_impl(const void* q, const void* k, const void* v, int batch, int seq
   uint16_t* chi = reinterpret_cast<uint16_t*>(ws + L.chi);
   uint16_t* clo = reinterpret_cast<uint16_t*>(ws + L.clo);
   StageClock clock;
-  if (!clock.begin(hs, stage_ms != nullptr)) return MOBA_ERR_HIP;
+  if (!clock.begin(hs, stage_ms != nullptr, stage_events)) return MOBA_ERR_HIP;
 
   MOBA_TRY(moba::launch_pool(s, kb, reinterpret_cast<float*>(ws + L.pool_partial), cent, hs));
   MOBA_TRY(moba::launch_centroid_split(s, cent, chi, clo, hs));
@@ -241,7 +252,7 @@ int moba_forward(const void* q, const void* k, const void* v, int batch, int seq
                  void* out, float* lse, int32_t* idx, void* workspace,
                  size_t workspace_bytes, void* stream) {
   return forward_impl(q, k, v, batch, seqlen, hq, hkv, head_dim, block, topk, scale, out,
-                      lse, idx, workspace, workspace_bytes, stream, nullptr);
+                      lse, idx, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
@@ -251,7 +262,18 @@ int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
                          float* stage_ms) {
   if (!stage_ms) return MOBA_ERR_INVALID_ARG;
   return forward_impl(q, k, v, batch, seqlen, hq, hkv, head_dim, block, topk, scale, out,
-                      lse, idx, workspace, workspace_bytes, stream, stage_ms);
+                      lse, idx, workspace, workspace_bytes, stream, stage_ms, nullptr);
+}
+
+int moba_forward_timed(const void* q, const void* k, const void* v, int batch, int seqlen,
+                       int hq, int hkv, int head_dim, int block, int topk, float scale,
+                       void* out, float* lse, int32_t* idx, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (!stage_events) return MOBA_ERR_INVALID_ARG;
+  for (int i = 0; i <= MOBA_NUM_STAGES; ++i)
+    if (!stage_events[i]) return MOBA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, batch, seqlen, hq, hkv, head_dim, block, topk, scale, out,
+                      lse, idx, workspace, workspace_bytes, stream, nullptr, stage_events);
 }
 
 // ------------------------------------------------------------------- stages

@@ -95,6 +95,19 @@ int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
                          void* workspace, size_t workspace_bytes, void* stream,
                          float* stage_ms);
 
+/* moba_forward that also records HIP events at the step boundaries, on `stream`,
+ * without synchronising: stage_events is a HOST array of MOBA_NUM_STAGES + 1 hipEvent_t
+ * handles created by the caller (timing enabled); stage_events[0] is recorded before
+ * the first step and stage_events[i + 1] after step i (numbered as for
+ * moba_forward_profile).  When the workspace makes the call loop over several kv-head
+ * groups, the events mark the boundaries of the last group.  The caller reads the
+ * times with hipEventElapsedTime once the stream has passed them.  Returns
+ * MOBA_ERR_INVALID_ARG when stage_events or one of its handles is NULL. */
+int moba_forward_timed(const void* q, const void* k, const void* v, int batch, int seqlen,
+                       int hq, int hkv, int head_dim, int block, int topk, float scale,
+                       void* out, float* lse, int32_t* idx, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* stage_events);
+
 /* A static, human-readable message for a status code. */
 const char* moba_strerror(int status);
 

@@ -86,3 +86,8 @@ def test_forward_rejects_bad_args_before_any_launch(moba):
     st = lib.moba_forward(None, None, None, 1, 130, 1, 1, 64, 16, 2, 0.125, None, None,
                           None, None, 0, None)
     assert st == -2
+    # the timed variant needs MOBA_NUM_STAGES + 1 non-null event handles
+    args = (None, None, None, 1, 128, 1, 1, 64, 16, 2, 0.125, None, None, None, None, 0, None)
+    assert lib.moba_forward_timed(*args, None) == -1
+    ev = (ctypes.c_void_p * (len(moba.STAGES) + 1))(*([1] * len(moba.STAGES) + [None]))
+    assert lib.moba_forward_timed(*args, ev) == -1

@@ -298,6 +298,28 @@ def test_forward_deterministic_and_chunked(moba):
         assert torch.equal(x, y) and torch.equal(x, z)
 
 
+def test_forward_timed_events(moba):
+    """moba_forward_timed gives the same results as moba_forward, and its stage events,
+    recorded on the stream without a synchronisation, bracket the whole call."""
+    w = small_workload("timed", 1, 8, 2, 128, 4096, 256, 5, "offset", 21)
+    inp = make_inputs(w)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    a = moba.forward(q, k, v, w.block, w.topk)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(moba.STAGES) + 1)]
+    for e in evs:
+        e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    b = moba.forward(q, k, v, w.block, w.topk, events=evs)
+    end.record()
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    stages = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(moba.STAGES))]
+    assert all(t >= 0.0 for t in stages) and stages[3] > 0.0   # history ran
+    assert sum(stages) <= start.elapsed_time(end) + 0.05
+
+
 def test_forward_rejects_small_workspace(moba):
     w = small_workload("ws", 1, 4, 2, 64, 1024, 128, 3, "iid", 20)
     inp = make_inputs(w)
