@@ -43,7 +43,12 @@ constexpr int kAttnWaves = MOBA_ATTN_NW;
 static_assert(kAttnWaves % 2 == 0, "the walker runs two wave groups");
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
-constexpr int KN = 64;          // keys per LDS subtile
+#ifndef MOBA_ATTN_KN
+#define MOBA_ATTN_KN 64
+#endif
+constexpr int KN = MOBA_ATTN_KN;  // keys per LDS subtile (a multiple of 32)
+constexpr int NH = KN / 32;       // 32-key halves of a subtile (one MFMA row block each)
+static_assert(KN % 32 == 0, "subtiles hold whole 32-key MFMA blocks");
 constexpr float kTau = 8.f;     // lazy rescale: the reference max may lag by 2^8
 
 template <int D>
@@ -64,7 +69,7 @@ struct WaveState {
   float m[QT], l[QT];
 };
 
-// One 64-key subtile of K (or V) in flight through registers (global -> regs -> LDS).
+// One KN-key subtile of K (or V) in flight through registers (global -> regs -> LDS).
 template <int D>
 struct TileRegs {
   static constexpr int CPR = D / 8;                                  // 16 B chunks per row
@@ -152,129 +157,6 @@ __device__ __forceinline__ void state_init(WaveState<D, QT>& st) {
   }
 }
 
-// Scores of one 64-key subtile: S^T = K Q^T, two 32-key halves.  Lane (n, hf) ends up
-// with query n and keys kk*32 + (i/4)*8 + hf*4 + i%4 of half kk.
-template <int D, int QT>
-__device__ __forceinline__ void qk_subtile(f32x16_t (&s)[2][QT], const WaveState<D, QT>& st,
-                                           const char* lk) {
-  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kk][qt][i] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    // A = K rows kk*32 + n, dims 16*ks + 8*hf .. +7
-    const char* kp = lk + (kk * 32 + n) * Lds<D>::KS + hf * 16;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + ks * 32));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[kk][qt] = mfma32x32x16(a, st.q[qt][ks], s[kk][qt]);
-    }
-  }
-}
-
-// Masks (keys >= nkeys, keys > tpos), takes the row max and applies the lazy rescale:
-// the reference max m moves only when a row's max exceeds it by more than kTau (O and
-// l are rescaled then), so later p = exp2(s * scale * log2e - m) <= 2^kTau.
-template <int D, int QT>
-__device__ __forceinline__ void softmax_max(WaveState<D, QT>& st, f32x16_t (&s)[2][QT],
-                                            float sl, bool mask, int nkeys, int kb,
-                                            const int (&tpos)[QT]) {
-  const int hf = (threadIdx.x & 63) >> 5;
-  if (mask) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int lim = min(nkeys - 1, tpos[qt] - kb) - kk * 32 - hf * 4;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((i >> 2) * 8 + (i & 3) > lim) s[kk][qt][i] = -INFINITY;
-      }
-  }
-  float mxs[QT];
-  bool need = false;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float mx = s[0][qt][0];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][qt][i]);
-    mxs[qt] = pair_max(mx) * sl;
-    need |= mxs[qt] > st.m[qt] + kTau;
-  }
-  if (__ballot(need) != 0ull) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mnew = fmaxf(st.m[qt], mxs[qt]);
-      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(st.m[qt] - mnew);
-      st.m[qt] = mnew;
-      st.l[qt] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.o[qt][dt][i] *= alpha;
-    }
-  }
-}
-
-// p = exp2(s * sl - m), float32 row sum, and P^T packed as bf16 MFMA operands: k-step
-// ks (keys 16ks .. 16ks+15) is score registers 8*(ks%2) .. +7 of half ks/2.
-template <int D, int QT>
-__device__ __forceinline__ void softmax_exp(WaveState<D, QT>& st, const f32x16_t (&s)[2][QT],
-                                            float sl, bf16x8_t (&pb)[QT][4]) {
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float mref = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
-    float rs = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(s[kk][qt][i], sl, -mref));
-        rs += p[i];
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
-        pb[qt][2 * kk + h] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
-      }
-    }
-    st.l[qt] += rs;
-  }
-}
-
-// O^T += V^T P^T for one subtile.  Lane (n, hf) holds keys 16ks + 8(e/4) + 4hf + e%4,
-// e < 8, of k-step ks; the matching V^T operand is two transpose reads: lanes 4j+q of
-// each 16-lane group address row 16ks + 4hf + j (+8 for the second read), dims
-// d0 + 4q .. +3, d0 = dt*32 + 16*((lane/16)&1); lane i of the group then holds dim d0+i.
-template <int D, int QT>
-__device__ __forceinline__ void pv_subtile(WaveState<D, QT>& st, const bf16x8_t (&pb)[QT][4],
-                                           const char* lv) {
-  const int lane = threadIdx.x & 63, hf = lane >> 5;
-  const char* vp = lv + (4 * hf + ((lane & 15) >> 2)) * Lds<D>::VS +
-                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * Lds<D>::VS + dt * 64);
-      const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * Lds<D>::VS + dt * 64);
-      const bf16x8_t a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][ks], st.o[qt][dt]);
-    }
-  }
-}
-
 // Key-range walker, two wave groups in ping-pong.  The workgroup's waves form two
 // groups (the two waves that share a SIMD are in different groups).  Every wave runs
 // the same sequence of phases, separated by barriers:
@@ -295,12 +177,12 @@ template <int D, int QT>
 struct Walker {
   using L = Lds<D>;
   static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
-  static constexpr int NQK = 2 * KSTEPS;           // QK^T MFMAs per query tile
-  static constexpr int NPV = 4 * (D / 32);         // PV MFMAs per query tile
+  static constexpr int NQK = NH * KSTEPS;          // QK^T MFMAs per query tile
+  static constexpr int NPV = (KN / 16) * (D / 32); // PV MFMAs per query tile
   static constexpr int PFK = 3, PFV = 4;           // operand reads in flight
   static constexpr int NC = TileRegs<D>::NC;
-  using Scores = f32x16_t[2][QT];
-  using POps = bf16x8_t[QT][4];
+  using Scores = f32x16_t[NH][QT];
+  using POps = bf16x8_t[QT][KN / 16];
   char* lds;
   const uint16_t* kbase;
   const uint16_t* vbase;
@@ -354,7 +236,7 @@ struct Walker {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < NH; ++kk) {
         const int lim = min(nvalid(i) - 1, tpos[qt] - kb(i)) - kk * 32 - hf * 4;
 #pragma unroll
         for (int e = 0; e < 16; ++e)
@@ -391,7 +273,7 @@ struct Walker {
     for (int qt = 0; qt < QT; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < NH; ++kk)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kk][qt][e]);
       mxs[qt] = pair_max(mx) * sl;
@@ -405,7 +287,8 @@ struct Walker {
   __device__ __forceinline__ void phase_a(WaveState<D, QT>& st, const Scores& cur,
                                           Scores& nxt, POps& pb, int i, int h) {
     const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-    constexpr int EPS = 32 / NQK;  // exp elements per slot and query tile
+    constexpr int EPS = 16 * NH / NQK;  // exp elements per slot and query tile
+    static_assert(EPS * NQK == 16 * NH && 8 % EPS == 0, "the exps split evenly over slots");
     const char* kp = kbuf(i + 1) + n * L::KS + hf * 16;
     bf16x8_t ka[NQK];
     if (NEXT) {
@@ -413,7 +296,7 @@ struct Walker {
       for (int j = 0; j < PFK; ++j)
         ka[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
     }
-    float mref[QT], rsum[QT], p[QT][32];
+    float mref[QT], rsum[QT], p[QT][16 * NH];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       mref[qt] = (st.m[qt] == -INFINITY) ? 0.f : st.m[qt];
@@ -478,7 +361,8 @@ struct Walker {
     };
 #pragma unroll
     for (int j = 0; j < PFV; ++j) va[j] = vread(j);
-    constexpr int MPS = 32 / NPV;  // max elements per slot and query tile
+    constexpr int MPS = 16 * NH / NPV;  // max elements per slot and query tile
+    static_assert(MPS * NPV == 16 * NH, "the row max splits evenly over the PV slots");
     float mx[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) mx[qt] = -INFINITY;
@@ -576,7 +460,9 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
   // waves w and w + kAttnWaves/2 share a SIMD (waves are dealt to SIMDs in turn), so
   // the halves of the workgroup are the two groups
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#if MOBA_ATTN_GROUP_BY_PARITY
+#if MOBA_ATTN_NO_PINGPONG
+  w.grp = 0 * wave;
+#elif MOBA_ATTN_GROUP_BY_PARITY
   w.grp = wave & 1;
 #else
   w.grp = wave / (kAttnWaves / 2);
