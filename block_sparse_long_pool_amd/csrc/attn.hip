@@ -179,7 +179,13 @@ struct Walker {
   static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int NQK = NH * KSTEPS;          // QK^T MFMAs per query tile
   static constexpr int NPV = (KN / 16) * (D / 32); // PV MFMAs per query tile
-  static constexpr int PFK = 3, PFV = 4;           // operand reads in flight
+#ifndef MOBA_ATTN_PFK
+#define MOBA_ATTN_PFK 3
+#endif
+#ifndef MOBA_ATTN_PFV
+#define MOBA_ATTN_PFV 4
+#endif
+  static constexpr int PFK = MOBA_ATTN_PFK, PFV = MOBA_ATTN_PFV;  // operand reads in flight
   static constexpr int NC = TileRegs<D>::NC;
   using Scores = f32x16_t[NH][QT];
   using POps = bf16x8_t[QT][KN / 16];
@@ -331,6 +337,9 @@ struct Walker {
             for (int e = 0; e < 4; ++e)
               w[e] = pack_bf16x2(p[qt][8 * ks + 2 * e], p[qt][8 * ks + 2 * e + 1]);
             pb[qt][ks] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+            // keep this slice in this slot: without the pin the compiler sinks the
+            // whole exp/pack work past the barrier into phase B, next to its use
+            asm volatile("" : "+v"(pb[qt][ks]));
           }
         }
       }
@@ -339,7 +348,10 @@ struct Walker {
     }
     if (EXP) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st.l[qt] += rsum[qt];
+      for (int qt = 0; qt < QT; ++qt) {
+        asm volatile("" : "+v"(rsum[qt]));
+        st.l[qt] += rsum[qt];
+      }
     }
   }
 
@@ -505,10 +517,26 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
   if (!valid) return;
   const float ln2 = 0.69314718055994530942f;
   const float lse_c = (st.m[qt] + __log2f(lc)) * ln2;
+  // The parts are read CH at a time so that their loads are in flight together;
+  // indices past nh are clamped to the row's last part and given weight 0.
+  constexpr int CH = 4;
   float mx = lse_c;
-  for (int s = 0; s < nh; ++s) mx = fmaxf(mx, pl[s]);
+  for (int s0 = 0; s0 < nh; s0 += CH) {
+    float v[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) v[u] = pl[min(s0 + u, nh - 1)];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) mx = fmaxf(mx, v[u]);
+  }
   float den = expf(lse_c - mx);
-  for (int s = 0; s < nh; ++s) den += expf(pl[s] - mx);
+  for (int s0 = 0; s0 < nh; s0 += CH) {
+    float v[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) v[u] = pl[min(s0 + u, nh - 1)];
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+      if (s0 + u < nh) den += expf(v[u] - mx);
+  }
   const float L = mx + logf(den);
   const float wc = expf(lse_c - L) / lc;
   f32x4_t acc[D / 32][4];
@@ -518,19 +546,32 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[dt][ii][r] = st.o[qt][dt][ii * 4 + r] * wc;
-  for (int s = 0; s < nh; ++s) {
-    const float w = expf(pl[s] - L);
-    const uint16_t* ps = po + (size_t)s * D + hf * 4;
+  for (int s0 = 0; s0 < nh; s0 += CH) {
+    u32x2_t x[CH][D / 32][4];
+    float w[CH];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int u = 0; u < CH; ++u) {
+      const int sc = min(s0 + u, nh - 1);
+      const uint16_t* ps = po + (size_t)sc * D + hf * 4;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const u32x2_t x = *reinterpret_cast<const u32x2_t*>(ps + dt * 32 + ii * 8);
-        const float xf[4] = {__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
-                             __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w, xf[r], acc[dt][ii][r]);
-      }
+        for (int ii = 0; ii < 4; ++ii)
+          x[u][dt][ii] = *reinterpret_cast<const u32x2_t*>(ps + dt * 32 + ii * 8);
+      w[u] = s0 + u < nh ? expf(pl[sc] - L) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const u32x2_t y = x[u][dt][ii];
+          const float xf[4] = {__uint_as_float(y[0] << 16), __uint_as_float(y[0] & 0xffff0000u),
+                               __uint_as_float(y[1] << 16), __uint_as_float(y[1] & 0xffff0000u)};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w[u], xf[r], acc[dt][ii][r]);
+        }
   }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
