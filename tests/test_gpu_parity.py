@@ -373,3 +373,60 @@ def test_llama8b_128k(moba):
 
 def test_llama8b_64k_b128(moba):
     big_compare(moba, "llama8b_64k_b128", per_block=1, seed=4)
+
+
+class _Bf16Rows:
+    """A bf16 bit array that widens to float64 only what is indexed (the oracle's row
+    functions index single query rows), so a 1M-token Q need not exist in float64."""
+
+    def __init__(self, bits):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, idx):
+        return bf16_to_f64(self.bits[idx])
+
+
+def check_idx_rows(idx, B, topk):
+    """Properties every idx row has, checked on all rows: ascending valid entries,
+    min(k, c+1) of them, the last one the current block c, none in the future, then
+    -1 padding."""
+    b, hq, T, k = idx.shape
+    c = (np.arange(T) // B)[None, None, :]
+    n_valid = np.minimum(topk, c + 1)
+    pos = np.arange(k)[None, None, None, :]
+    valid = pos < n_valid[..., None]
+    assert np.all(np.where(valid, idx >= 0, idx == -1)), "padding"
+    last = np.take_along_axis(idx, (n_valid - 1)[..., None].repeat(b, 0).repeat(hq, 1), -1)
+    assert np.all(last[..., 0] == c), "current block"
+    assert np.all(np.where(valid, idx <= c[..., None], True)), "future block"
+    inc = np.diff(idx, axis=-1) > 0
+    assert np.all(np.where(valid[..., 1:], inc, True)), "ascending"
+
+
+def test_llama8b_1m(moba):
+    """1M tokens, B=4096, k=12: every idx row's properties, and sampled rows against the
+    oracle (selection with the near-tie rule, out and lse)."""
+    w = get_workload("llama8b_1m")
+    say(f"[big] {w.name}: generating inputs")
+    inp = make_inputs(w)
+    say(f"[big] {w.name}: running the GPU path")
+    go_t, gl_t, gi_t = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.block,
+                                    w.topk, w.sm_scale)
+    torch.cuda.synchronize()
+    say(f"[big] {w.name}: checking every idx row")
+    gi = gi_t.cpu().numpy()
+    check_idx_rows(gi, w.block, w.topk)
+    rows = sample_rows(w.batch, w.seqlen, w.hq, w.block, per_block=2, seed=5,
+                       extra=[(0, w.seqlen - 1, w.hq - 1), (0, 0, 0)])
+    say(f"[big] {w.name}: oracle on {len(rows)} sampled rows")
+    K = bf16_to_f64(inp["k"])
+    V = bf16_to_f64(inp["v"])
+    C = oracle.centroids(K, w.block)
+    bi_, t_, h_ = (np.array(x) for x in zip(*rows))
+    ib, it, ih = (torch.as_tensor(x, device="cuda") for x in (bi_, t_, h_))
+    go = go_t[ib, it, ih].float().cpu().numpy()
+    gl = gl_t[ib, ih, it].cpu().numpy()
+    stats = compare_rows(_Bf16Rows(inp["q"]), K, V, w.block, w.topk, w.sm_scale, rows, go,
+                         gl, gi[bi_, h_, t_], C=C)
+    say(f"[big] {w.name}: {stats}")

@@ -321,6 +321,21 @@ def test_generator_is_seeded_and_per_head():
     assert np.array_equal(c["k"], a["k"])
 
 
+def test_parallel_generator_matches_the_plain_draw():
+    """make_inputs draws each head in its own thread; the values equal one plain
+    float32 draw per head stream (+ the key offsets) rounded to bf16."""
+    import workloads as wl
+    w = small_workload("par", 1, 8, 2, 16, 96, 32, 3, "offset", seed=12)
+    inp = make_inputs(w)
+    k32 = wl._normal_heads(w, wl.K_ID, w.hkv)
+    mu = wl._key_offsets(w)
+    for j in range(w.num_blocks):
+        k32[:, j * w.block:(j + 1) * w.block] += mu[:, j][:, None, :, :]
+    assert np.array_equal(inp["k"], f32_to_bf16_bits(k32))
+    assert np.array_equal(inp["v"], f32_to_bf16_bits(wl._normal_heads(w, wl.V_ID, w.hkv)))
+    assert np.array_equal(inp["q"], f32_to_bf16_bits(wl._normal_heads(w, wl.Q_ID, w.hq)))
+
+
 def test_bf16_rounding_is_rne():
     x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.140625, 1e-40], np.float32)
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins;

@@ -19,6 +19,8 @@ is drawn on its own, so any head can be regenerated alone.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, asdict
 
 import numpy as np
@@ -130,6 +132,27 @@ def _normal_heads(w: Workload, tensor_id: int, nheads: int) -> np.ndarray:
     return out
 
 
+def _bf16_heads(w: Workload, tensor_id: int, nheads: int, mu=None) -> np.ndarray:
+    """[batch, T, nheads, d] bf16 bits of N(0,1) draws, one stream per head, the same
+    values as rounding _normal_heads(...) (+ the key offsets mu [b, nb, nheads, d] when
+    given).  Heads are drawn in parallel threads (numpy's generators and array
+    arithmetic run without the interpreter lock), one head's float32 at a time each."""
+    out = np.empty((w.batch, w.seqlen, nheads, w.head_dim), np.uint16)
+
+    def one(h):
+        x = _rng(w.seed, tensor_id, h).standard_normal(
+            (w.batch, w.seqlen, w.head_dim), dtype=np.float32)
+        if mu is not None:
+            for j in range(w.num_blocks):
+                x[:, j * w.block:(j + 1) * w.block] += mu[:, j, h][:, None, :]
+        out[:, :, h, :] = f32_to_bf16_bits(x)
+
+    workers = max(1, min(16, os.cpu_count() or 1, nheads))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(nheads)))
+    return out
+
+
 def _key_offsets(w: Workload) -> np.ndarray:
     """[batch, nb, hkv, d] float32: a per-(kv-head, block) key mean offset, N(0, 0.5^2)."""
     nb = w.num_blocks
@@ -179,21 +202,11 @@ def make_inputs(w: Workload, heads_only=None):
                blocks' mean key (kv-head h's group); q = sqrt(d) m/|m| + N(0, I).
                Rows in block 0 get q = N(0, I).  The routing target P is returned.
     """
-    d = w.head_dim
-    k32 = _normal_heads(w, K_ID, w.hkv)
-    if w.recipe == "offset":
-        mu = _key_offsets(w)
-        nb = w.num_blocks
-        for j in range(nb):
-            k32[:, j * w.block:(j + 1) * w.block] += mu[:, j][:, None, :, :]
-    v32 = _normal_heads(w, V_ID, w.hkv)
-    kb = f32_to_bf16_bits(k32)
-    del k32
-    vb = f32_to_bf16_bits(v32)
-    del v32
+    kb = _bf16_heads(w, K_ID, w.hkv, _key_offsets(w) if w.recipe == "offset" else None)
+    vb = _bf16_heads(w, V_ID, w.hkv)
     out = {"k": kb, "v": vb, "workload": w}
     if w.recipe in ("iid", "offset"):
-        qb = f32_to_bf16_bits(_normal_heads(w, Q_ID, w.hq))
+        qb = _bf16_heads(w, Q_ID, w.hq)
     elif w.recipe == "planted":
         qb, planted = _planted_queries(w, kb)
         out["planted"] = planted
