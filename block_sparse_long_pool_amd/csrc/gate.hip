@@ -139,11 +139,23 @@ __device__ __forceinline__ GateChunk gate_chunk_of(int cid, int T, int hq, int b
   return k;
 }
 
-// Rank one chunk (its rows compete) with its query operands bq.
-template <int D, int KHMAX>
+// LDS image of one kv-head's centroids: the bf16 hi rows then the lo rows, each row
+// padded to CS bytes so that the 32 rows an MFMA operand read touches spread over the
+// banks.
+template <int D>
+struct CentLds {
+  static constexpr int CS = 2 * D + 16;
+  static constexpr int MAX_NB = 96;
+  static constexpr int BYTES = 2 * MAX_NB * CS;
+};
+
+// Rank one chunk (its rows compete) with its query operands bq.  The centroids come
+// from global memory, or from the workgroup's LDS image lds (nb <= CentLds::MAX_NB).
+template <int D, int KHMAX, bool CLDS>
 __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], const GateChunk& k,
                                            const uint16_t* __restrict__ chi,
-                                           const uint16_t* __restrict__ clo, int T, int hq,
+                                           const uint16_t* __restrict__ clo,
+                                           const char* __restrict__ lds, int T, int hq,
                                            int hkv, int block, int nb, int topk, int nbits,
                                            int32_t* __restrict__ idx) {
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
@@ -166,13 +178,17 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
     const int jrow = min(jt * 32 + n, nb - 1);
     const uint16_t* ph = chi + (cbase + jrow) * D + 8 * hf;
     const uint16_t* pl = clo + (cbase + jrow) * D + 8 * hf;
+    const char* lh = lds + jrow * CentLds<D>::CS + 16 * hf;
+    const char* ll = lh + nb * CentLds<D>::CS;
     f32x16_t acc0, acc1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ph + 16 * s));
-      const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u32x4_t*>(pl + 16 * s));
+      const bf16x8_t ah = as_bf16x8(CLDS ? *reinterpret_cast<const u32x4_t*>(lh + 32 * s)
+                                         : *reinterpret_cast<const u32x4_t*>(ph + 16 * s));
+      const bf16x8_t al = as_bf16x8(CLDS ? *reinterpret_cast<const u32x4_t*>(ll + 32 * s)
+                                         : *reinterpret_cast<const u32x4_t*>(pl + 16 * s));
       acc0 = mfma32x32x16(ah, bq[0][s], acc0);
       acc1 = mfma32x32x16(ah, bq[1][s], acc1);
       acc0 = mfma32x32x16(al, bq[0][s], acc0);
@@ -294,7 +310,50 @@ __global__ __launch_bounds__(kThreads, 3) void gate_topk_kernel(
   }
   bf16x8_t bq[2][D / 16];
   gate_load_q<D>(bq, q, T, hq, k.b, k.h, k.t0, true);
-  gate_chunk<D, KHMAX>(bq, k, chi, clo, T, hq, hkv, block, nb, topk, nbits, idx);
+  gate_chunk<D, KHMAX, false>(bq, k, chi, clo, nullptr, T, hq, hkv, block, nb, topk, nbits,
+                              idx);
+}
+
+// The same with the centroids in LDS (nb <= CentLds::MAX_NB): a workgroup takes four
+// chunks of one (batch, kv-head) group, blockIdx.y = b * hkv + g, and first copies that
+// kv-head's hi/lo centroids into LDS.
+template <int D, int KHMAX>
+__global__ __launch_bounds__(kThreads, 3) void gate_topk_lds_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
+    const uint16_t* __restrict__ clo, int batch, int T, int hq, int hkv, int block, int nb,
+    int topk, int nbits, int32_t* __restrict__ idx) {
+  using CL = CentLds<D>;
+  __shared__ __attribute__((aligned(16))) char lds[CL::BYTES];
+  const int G = hq / hkv, nct = (T + 63) / 64;
+  const int b = blockIdx.y / hkv, g = blockIdx.y % hkv;
+  const int ci = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // chunk in group
+  const size_t cbase = (size_t)(b * hkv + g) * nb;
+  constexpr int CPR = D / 8;  // 16-byte chunks per centroid row
+  for (int e = threadIdx.x; e < 2 * nb * CPR; e += kThreads) {
+    const int which = e / (nb * CPR), r = (e / CPR) % nb, cp = e % CPR;
+    const uint16_t* src = (which ? clo : chi) + (cbase + r) * D + cp * 8;
+    *reinterpret_cast<u32x4_t*>(lds + (which * nb + r) * CL::CS + cp * 16) =
+        *reinterpret_cast<const u32x4_t*>(src);
+  }
+  __syncthreads();
+  if (ci >= G * nct) return;
+  GateChunk k;
+  k.b = b;
+  k.h = g * G + ci / nct;
+  k.t0 = (ci % nct) * 64;
+  k.compete = min(k.t0 + 63, T - 1) / block > topk - 1;
+  if (!k.compete) {
+    const int t = k.t0 + (threadIdx.x & 63);
+    if (t < T) {
+      const int c = t / block;
+      int32_t* row = idx + ((size_t)(k.b * hq + k.h) * T + t) * topk;
+      for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
+    }
+    return;
+  }
+  bf16x8_t bq[2][D / 16];
+  gate_load_q<D>(bq, q, T, hq, k.b, k.h, k.t0, true);
+  gate_chunk<D, KHMAX, true>(bq, k, chi, clo, lds, T, hq, hkv, block, nb, topk, nbits, idx);
 }
 
 hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
@@ -307,9 +366,19 @@ hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
   const int per_block = kThreads / 64;
   dim3 grid((unsigned)((nchunks + per_block - 1) / per_block));
   const int KH = s.KH();
-#define MOBA_GATE(DD, KK)                                                            \
-  hipLaunchKernelGGL((gate_topk_kernel<DD, KK>), grid, dim3(kThreads), 0, st, q, chi, \
-                     clo, s.b, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits, idx)
+  const bool clds = nb <= 96;
+  const long group_chunks = (long)s.G() * ((s.T + 63) / 64);
+  const dim3 grid_lds((unsigned)((group_chunks + per_block - 1) / per_block), s.b * s.hkv);
+#define MOBA_GATE(DD, KK)                                                                \
+  do {                                                                                   \
+    if (clds)                                                                            \
+      hipLaunchKernelGGL((gate_topk_lds_kernel<DD, KK>), grid_lds, dim3(kThreads), 0, st, \
+                         q, chi, clo, s.b, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits,  \
+                         idx);                                                           \
+    else                                                                                 \
+      hipLaunchKernelGGL((gate_topk_kernel<DD, KK>), grid, dim3(kThreads), 0, st, q, chi, \
+                         clo, s.b, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits, idx);    \
+  } while (0)
   if (s.d == 128) {
     if (KH <= 16) MOBA_GATE(128, 16);
     else MOBA_GATE(128, 32);

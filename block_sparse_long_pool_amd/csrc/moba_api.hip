@@ -176,7 +176,7 @@ struct StageClock {
       if (hipEventElapsedTime(&t, ev[i], ev[i + 1]) != hipSuccess) status = MOBA_ERR_HIP;
       ms[stage[i]] += t;
     }
-    for (int i = 0; i < 65; ++i) hipEventDestroy(ev[i]);
+    for (int i = 0; i < 65; ++i) (void)hipEventDestroy(ev[i]);
     return status;
   }
 };
