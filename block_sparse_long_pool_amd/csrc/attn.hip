@@ -519,7 +519,10 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
   const float lse_c = (st.m[qt] + __log2f(lc)) * ln2;
   // The parts are read CH at a time so that their loads are in flight together;
   // indices past nh are clamped to the row's last part and given weight 0.
-  constexpr int CH = 4;
+#ifndef MOBA_MERGE_CH
+#define MOBA_MERGE_CH 4
+#endif
+  constexpr int CH = MOBA_MERGE_CH;
   float mx = lse_c;
   for (int s0 = 0; s0 < nh; s0 += CH) {
     float v[CH];
