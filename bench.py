@@ -131,6 +131,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama8b_128k")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing dense causal attention on the same inputs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one elementwise copy (torch.neg) of this many MiB "
                          "of bf16, a kernel of known traffic for scaling HBM counters")
@@ -262,6 +264,29 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if not a.no_dense:
+        # the full-attention layer of a hybrid model on the same inputs: context for the
+        # sparse path (not the metric)
+        out_d = torch.empty_like(q)
+        lse_d = torch.empty_like(lse)
+        moba.dense_forward(q, k, v, w.sm_scale, out=out_d, lse=lse_d)
+        n_dense = 3
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_dense):
+            moba.dense_forward(q, k, v, w.sm_scale, out=out_d, lse=lse_d)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / n_dense
+        dflop = 4 * w.head_dim * heads * w.seqlen * (w.seqlen + 1) // 2
+        result["dense_causal"] = {
+            "ms": dms, "tflops": dflop / (dms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": dflop / (dms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "moba_speedup": dms / ms,
+            "note": "dense causal attention (moba_dense_forward) on the same inputs",
+        }
+        print(f"[bench] dense causal {dms:.2f} ms", file=sys.stderr, flush=True)
+        del out_d, lse_d
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_seconds:.0f} s)", file=sys.stderr,
               flush=True)

@@ -20,7 +20,7 @@ import os
 __all__ = [
     "LIB_PATH", "MobaError", "check_args", "workspace_bytes", "forward",
     "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
-    "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace",
+    "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -46,6 +46,7 @@ _SIGS = {
                                   _vp, _vp, _sz, _vp, ctypes.POINTER(_f)]),
     "moba_forward_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
                                 _vp, _sz, _vp, ctypes.POINTER(_vp)]),
+    "moba_dense_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "moba_strerror": (ctypes.c_char_p, [_i]),
     "moba_stage_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moba_pool_centroids": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -205,6 +206,45 @@ def forward(q, k, v, block: int, topk: int, scale: float | None = None, workspac
     if profile:
         return out, lse, idx, dict(zip(STAGES, (float(x) for x in ms)))
     return out, lse, idx
+
+
+def dense_forward(q, k, v, scale: float | None = None, out=None, lse=None):
+    """Dense causal attention through the library (the full-attention layers of a
+    hybrid model).  Returns (out bf16 [b,T,Hq,d], lse fp32 [b,Hq,T])."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    b, T, hq, d = q.shape
+    if k.shape[0] != b or k.shape[1] != T or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, hq, T), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (b, hq, T):
+        raise ValueError("output shapes do not match the inputs")
+    with torch.cuda.device(q.device):
+        st = lib.moba_dense_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv,
+                                    d, float(scale), out.data_ptr(), lse.data_ptr(),
+                                    _stream_ptr())
+    _raise(st, "moba_dense_forward")
+    return out, lse
+
+
+def attention(q, k, v, block: int, topk: int, scale: float | None = None, dense: bool = False,
+              **kw):
+    """One attention layer of a hybrid model: MoBA (returns out, lse, idx) or, with
+    ``dense=True``, full causal attention (returns out, lse, None)."""
+    if dense:
+        out, lse = dense_forward(q, k, v, scale, kw.get("out"), kw.get("lse"))
+        return out, lse, None
+    return forward(q, k, v, block, topk, scale, **kw)
 
 
 def pool_centroids(k, block: int):

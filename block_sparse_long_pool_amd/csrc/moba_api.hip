@@ -255,6 +255,24 @@ int moba_forward(const void* q, const void* k, const void* v, int batch, int seq
                       lse, idx, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
+int moba_dense_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
+                       int hq, int hkv, int head_dim, float scale, void* out, float* lse,
+                       void* stream) {
+  // one block of seqlen tokens and topk 1: the current-block kernel alone is dense
+  // causal attention, with no history part to merge
+  const int st = check(batch, seqlen, hq, hkv, head_dim, seqlen, 1, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out || !lse) return MOBA_ERR_INVALID_ARG;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, seqlen, 1};
+  if (moba::launch_attn_current(s, static_cast<const uint16_t*>(q),
+                                static_cast<const uint16_t*>(k),
+                                static_cast<const uint16_t*>(v), scale, 0, hkv, nullptr,
+                                nullptr, static_cast<uint16_t*>(out), lse,
+                                static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOBA_ERR_HIP;
+  return MOBA_OK;
+}
+
 int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
                          int seqlen, int hq, int hkv, int head_dim, int block, int topk,
                          float scale, void* out, float* lse, int32_t* idx,

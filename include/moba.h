@@ -95,6 +95,17 @@ int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
                          void* workspace, size_t workspace_bytes, void* stream,
                          float* stage_ms);
 
+/* Dense causal attention, for the layers that stay on full attention (README bullet
+ * "Seamlessly Transition between Full and Sparse Attention": with every block
+ * selected, the layer is full attention).  The same result as moba_forward with
+ * topk >= seqlen / block, without gating or index: out[b,t,h] = softmax over keys
+ * u <= t of scale * q.k_u, times V; lse as for moba_forward.  Layouts, dtypes and
+ * stream semantics as for moba_forward; needs no workspace.  seqlen must be a
+ * multiple of 16; the other shape limits are moba_forward's with block = seqlen. */
+int moba_dense_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
+                       int hq, int hkv, int head_dim, float scale, void* out, float* lse,
+                       void* stream);
+
 /* moba_forward that also records HIP events at the step boundaries, on `stream`,
  * without synchronising: stage_events is a HOST array of MOBA_NUM_STAGES + 1 hipEvent_t
  * handles created by the caller (timing enabled); stage_events[0] is recorded before

@@ -86,6 +86,11 @@ def test_forward_rejects_bad_args_before_any_launch(moba):
     st = lib.moba_forward(None, None, None, 1, 130, 1, 1, 64, 16, 2, 0.125, None, None,
                           None, None, 0, None)
     assert st == -2
+    # dense causal attention: seqlen a multiple of 16, pointers checked on the host
+    assert lib.moba_dense_forward(None, None, None, 1, 130, 1, 1, 64, 0.125, None, None,
+                                  None) == -2
+    assert lib.moba_dense_forward(None, None, None, 1, 128, 1, 1, 64, 0.125, None, None,
+                                  None) == -1
     # the timed variant needs MOBA_NUM_STAGES + 1 non-null event handles
     args = (None, None, None, 1, 128, 1, 1, 64, 16, 2, 0.125, None, None, None, None, 0, None)
     assert lib.moba_forward_timed(*args, None) == -1

@@ -320,6 +320,50 @@ def test_forward_timed_events(moba):
     assert sum(stages) <= start.elapsed_time(end) + 0.05
 
 
+@pytest.mark.parametrize("b,hq,hkv,d,T", [(1, 4, 2, 128, 2048), (2, 2, 1, 64, 1024),
+                                           (1, 8, 8, 128, 784)])
+def test_dense_forward_matches_oracle(moba, b, hq, hkv, d, T):
+    """Dense causal attention (the full-attention layers of a hybrid model) against the
+    oracle with every block selected (pinned to SDPA), all rows."""
+    w = small_workload("dense_causal", b, hq, hkv, d, T, 16, T // 16, "iid", 23)
+    inp = make_inputs(w)
+    say(f"[dense] b={b} T={T} hq={hq} hkv={hkv} d={d}")
+    go, gl = moba.dense_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.sm_scale)
+    torch.cuda.synchronize()
+    Q, K, V = (bf16_to_f64(inp[x]) for x in "qkv")
+    ro, rl, _, _ = oracle.moba_forward(Q, K, V, w.block, w.topk, w.sm_scale)
+    go = go.float().cpu().numpy()
+    gl = gl.cpu().numpy()
+    err = np.abs(go - ro)
+    assert err.max() <= OUT_MAX and err.mean() <= OUT_MEAN, (err.max(), err.mean())
+    assert np.abs(gl - rl).max() <= LSE_MAX
+    # the hybrid dispatcher's dense branch is the same call
+    ho, hl, hi = moba.attention(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.block, w.topk,
+                                w.sm_scale, dense=True)
+    torch.cuda.synchronize()
+    assert hi is None and np.array_equal(ho.float().cpu().numpy(), go)
+
+
+def test_dense_forward_32k_sampled(moba):
+    """Dense causal attention at 32K tokens, 32/8 heads, d=128: sampled rows against the
+    oracle's one-softmax definition over keys 0..t."""
+    w = get_workload("llama8b_32k")
+    inp = make_inputs(w)
+    go_t, gl_t = moba.dense_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.sm_scale)
+    torch.cuda.synchronize()
+    K, V = bf16_to_f64(inp["k"]), bf16_to_f64(inp["v"])
+    r = np.random.default_rng(7)
+    rows = [(0, int(r.integers(w.seqlen)), int(r.integers(w.hq))) for _ in range(160)]
+    rows += [(0, 0, 0), (0, w.seqlen - 1, w.hq - 1)]
+    G = w.hq // w.hkv
+    for bi, t, h in rows:
+        o, l = oracle.attend_row(bf16_to_f64(inp["q"][bi, t, h]), K[bi, :, h // G],
+                                 V[bi, :, h // G], np.arange(t + 1), w.sm_scale)
+        go = go_t[bi, t, h].float().cpu().numpy()
+        assert np.abs(go - o).max() <= OUT_MAX, (t, h)
+        assert abs(float(gl_t[bi, h, t]) - l) <= LSE_MAX, (t, h)
+
+
 def test_forward_rejects_small_workspace(moba):
     w = small_workload("ws", 1, 4, 2, 64, 1024, 128, 3, "iid", 20)
     inp = make_inputs(w)
