@@ -1,4 +1,4 @@
-"""CPU oracle for the MoBA prefill forward pass (float64, NumPy).
+"""CPU oracle for the MoBA prefill forward pass and its backward (float64, NumPy).
 
 TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by
 ``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``, and by
@@ -24,6 +24,6 @@ exact-tie rules, hand-derived routings, brute force).  No function here is
 from .moba_oracle import (  # noqa: F401
     num_blocks, centroids, gate_scores_rows, select_rows, select_blocks,
     attended_keys, attend_row, attend_rows, attend_parts_row, merge_parts,
-    moba_forward, moba_rows, attended_pairs,
+    moba_forward, moba_rows, attended_pairs, attend_row_grad, moba_backward,
 )
 from .bruteforce import moba_bruteforce  # noqa: F401

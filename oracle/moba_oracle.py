@@ -1,4 +1,4 @@
-"""The plain float64 definition of MoBA prefill forward.
+"""The plain float64 definition of MoBA prefill forward (and its gradient).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the product.
 
@@ -220,3 +220,53 @@ def attended_pairs(T: int, B: int, topk: int) -> int:
         hist = min(c, topk - 1)
         total += n * hist * B + n * (n + 1) // 2
     return total
+
+
+# ----------------------------------------------------------------------------- backward
+# The gradient of the layer's output with respect to Q, K and V, for the training use of
+# MoBA ("Trainable Block Sparse Attention", README).  The block selection is a
+# piecewise-constant function of Q and K (a top-k over inner products with mean keys,
+# [Gating]: no parameters), so it contributes no gradient: the selection S of every row
+# is held fixed, and each row's output is ordinary softmax attention over its attended
+# keys N.  With z_u = scale q.k_u, p = softmax(z), o = sum_u p_u v_u and an upstream
+# gradient g = dL/do (the lse output is taken to carry no gradient):
+#   dv_u += p_u g,  dp_u = g.v_u,  dz_u = p_u (dp_u - g.o),
+#   dq = scale sum_u dz_u k_u,  dk_u += scale dz_u q.
+
+def attend_row_grad(q, Kg, Vg, keys, scale: float, g):
+    """(dq [d], dk [len(keys), d], dv [len(keys), d]) of one row's attention."""
+    z = scale * (Kg[keys] @ q)
+    e = np.exp(z - z.max())
+    p = e / e.sum()
+    o = p @ Vg[keys]
+    dp = Vg[keys] @ g
+    dz = p * (dp - g @ o)
+    dq = scale * (dz @ Kg[keys])
+    dk = scale * np.outer(dz, q)
+    dv = np.outer(p, g)
+    return dq, dk, dv
+
+
+def moba_backward(Q, K, V, dO, B: int, topk: int, scale: float, idx=None):
+    """dQ, dK, dV (float64, shapes of Q, K, V) of sum(dO * out) with each row's block set
+    fixed: the oracle's own selection, or ``idx`` [b, Hq, T, topk] when given."""
+    b, T, hq, d = Q.shape
+    hkv = K.shape[2]
+    G = hq // hkv
+    if idx is None:
+        idx = select_blocks(Q, centroids(K, B), B, topk)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for bi in range(b):
+        for h in range(hq):
+            g = h // G
+            Kg, Vg = K[bi, :, g], V[bi, :, g]
+            for t in range(T):
+                S = [int(j) for j in idx[bi, h, t] if j >= 0]
+                keys = attended_keys(S, t, B, T)
+                dq, dk, dv = attend_row_grad(Q[bi, t, h], Kg, Vg, keys, scale, dO[bi, t, h])
+                dQ[bi, t, h] = dq
+                dK[bi, keys, g] += dk
+                dV[bi, keys, g] += dv
+    return dQ, dK, dV
