@@ -21,6 +21,7 @@ __all__ = [
     "LIB_PATH", "MobaError", "check_args", "workspace_bytes", "forward",
     "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
+    "backward", "backward_workspace_bytes",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -47,6 +48,9 @@ _SIGS = {
     "moba_forward_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
                                 _vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "moba_dense_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
+    "moba_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "moba_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                           _vp, _vp, _vp, _vp, _sz, _vp]),
     "moba_strerror": (ctypes.c_char_p, [_i]),
     "moba_stage_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moba_pool_centroids": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -235,6 +239,64 @@ def dense_forward(q, k, v, scale: float | None = None, out=None, lse=None):
                                     _stream_ptr())
     _raise(st, "moba_dense_forward")
     return out, lse
+
+
+def backward_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk):
+    """(all-kv-heads size, one-kv-head size) of the backward workspace; (0, 0) when the
+    backward does not support the shape."""
+    mn = _sz(0)
+    full = lib.moba_backward_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk,
+                                             ctypes.byref(mn))
+    return int(full), int(mn.value)
+
+
+def backward(q, k, v, out, lse, idx, dout, block: int, topk: int, scale: float | None = None,
+             workspace=None, max_workspace_bytes: int | None = None, dq=None, dk=None,
+             dv=None):
+    """Gradients of ``forward`` with its block selection ``idx`` held fixed.  q, k, v,
+    out, lse, idx as given to / returned by ``forward``; dout like out.  Returns
+    (dq like q, dk like k, dv like v), bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(idx, "idx", torch.int32, 4)
+    b, T, hq, d = q.shape
+    hkv = k.shape[2]
+    if (k.shape[0] != b or k.shape[1] != T or k.shape[3] != d or v.shape != k.shape
+            or out.shape != q.shape or dout.shape != q.shape or lse.shape != (b, hq, T)
+            or idx.shape != (b, hq, T, topk)):
+        raise ValueError("shape mismatch between q, k, v, out, lse, idx, dout")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _raise(check_args(b, T, hq, hkv, d, block, topk, scale), "moba_backward")
+    if workspace is None:
+        full, mn = backward_workspace_bytes(b, T, hq, hkv, d, block, topk)
+        if full == 0:
+            _raise(MOBA_ERR_UNSUPPORTED, "moba_backward_workspace_bytes")
+        if max_workspace_bytes is None:
+            free, _ = torch.cuda.mem_get_info(q.device)
+            max_workspace_bytes = int(0.6 * free)
+        workspace = _alloc_workspace(full if full <= max_workspace_bytes
+                                     else max(mn, max_workspace_bytes), q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, 4)
+    _need(dk, "dk", torch.bfloat16, 4)
+    _need(dv, "dv", torch.bfloat16, 4)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shapes do not match the inputs")
+    with torch.cuda.device(q.device):
+        st = lib.moba_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), idx.data_ptr(), dout.data_ptr(), b, T, hq, hkv,
+                               d, block, topk, float(scale), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                               _stream_ptr())
+    _raise(st, "moba_backward")
+    return dq, dk, dv
 
 
 def attention(q, k, v, block: int, topk: int, scale: float | None = None, dense: bool = False,

@@ -1,0 +1,587 @@
+// Backward of the block-sparse attention: dQ, dK, dV for the training use of MoBA
+// ("MoBA: Mixture of Block Attention for Long-Context LLMs", README bullet "Trainable
+// Block Sparse Attention").  The block selection of the forward is held fixed: it is a
+// top-k over inner products with parameter-less mean keys, piecewise constant, so it
+// carries no gradient.  Each row is softmax attention over its attended keys N:
+//   p_u = exp(scale q.k_u - lse),  dp_u = dO.v_u,  dz_u = p_u (dp_u - D),  D = dO.out,
+//   dq = scale sum_u dz_u k_u,  dk_u += scale dz_u q,  dv_u += p_u dO.
+// lse and out come from the forward, so p is recomputed without a running max.
+//
+// Kernels:
+//   bwd_delta_kernel   D = rowsum(dO * out) per (b, h, t)
+//   bwd_dq_kernel      per row tile, over the keys of one block: S^T = K Q^T,
+//                      dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  History
+//                      tiles (the inverted index's gathered rows) write an fp32 partial
+//                      per (row, slot); current-block tiles add the row's partials to
+//                      their own and write dq.
+//   bwd_dkdv_kernel    per 256 keys of one block: every row that attends them (the
+//                      block's history list, then the block's own rows causally) in
+//                      groups of 32: S = Q K^T, dP = dO V^T, P, dS, then
+//                      dV^T += dO^T P and dK^T += Q^T dS; dK and dV stay in registers
+//                      and each key is written by exactly one workgroup.
+// MFMA layouts are those of the forward (v_mfma_f32_32x32x16_bf16): a 32x32 result
+// lane l holds column l%32 and rows (i/4)*8 + (l/32)*4 + i%4, and a transposed operand
+// is read from a row-major LDS tile with ds_read_b64_tr_b16 in the order the result
+// registers hold the summation index.
+#include "moba_internal.h"
+
+namespace moba {
+namespace {
+
+constexpr int kBwdWaves = 8;                // dQ kernel
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kKvWaves = 4;                 // dK/dV kernel: one wave per SIMD, 512 registers
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kBwdKN = 64;                  // keys per subtile in the dQ kernel
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BwdStrides {
+  static constexpr int RS = 2 * D + 16;     // rows read 16 bytes per lane (operand rows)
+  static constexpr int TS = 2 * D + 64;     // rows read with the transpose read
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i%4 of
+// the 8 bytes addressed by lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ u32x2_t tr16(const char* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+// A = X^T for rows 16ks .. 16ks+15 of a row-major tile with TS-byte rows, dims
+// dt*32 .. +31: the order matches result registers (i/4)*8 + hf*4 + i%4.
+template <int D>
+__device__ __forceinline__ bf16x8_t read_t_operand(const char* tile, int ks, int dt) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const char* p = tile + (4 * hf + ((lane & 15) >> 2)) * BwdStrides<D>::TS +
+                  (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2 + dt * 64;
+  const u32x2_t lo = tr16(p + (16 * ks) * BwdStrides<D>::TS);
+  const u32x2_t hi = tr16(p + (16 * ks + 8) * BwdStrides<D>::TS);
+  return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// 16 bytes of global memory through a buffer descriptor covering `bytes` from base
+// (reads past the end return zero)
+__device__ __forceinline__ u32x4_t load16(const void* base, int bytes, int off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// the B operand of one row (k-step s: dims 16s + 8hf .. +7), zero when !valid
+template <int D>
+__device__ __forceinline__ void load_row_operand(bf16x8_t (&x)[D / 16], const uint16_t* row,
+                                                 bool valid) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (valid) v = *reinterpret_cast<const u32x4_t*>(row + 16 * s + 8 * hf);
+    x[s] = as_bf16x8(v);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- D = rowsum(dO*O)
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ out,
+                                                        const uint16_t* __restrict__ dout,
+                                                        int T, int hq, int d, long rows,
+                                                        float* __restrict__ delta) {
+  const long r = (long)blockIdx.x * 256 + threadIdx.x;   // row index b*T*hq + t*hq + h
+  if (r >= rows) return;
+  const uint16_t* o = out + r * d;
+  const uint16_t* g = dout + r * d;
+  float acc = 0.f;
+  for (int c = 0; c < d; c += 8) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(o + c);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(g + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += bf16lo(a[e]) * bf16lo(b[e]) + bf16hi(a[e]) * bf16hi(b[e]);
+  }
+  const long h = r % hq, t = (r / hq) % T, b = r / ((long)hq * T);
+  delta[(b * hq + h) * T + t] = acc;
+}
+
+// ------------------------------------------------------------------------- dQ kernel
+// One workgroup = kBwdWaves * 32 rows against the keys [kbeg, kend) of one kv-head.
+// History: a tile of the inverted index (rows that chose block j; no mask), writing
+// the rows' fp32 partials.  Current: 32-token sub-tiles of block c for the query heads
+// of kv-head g (as the forward), causal, then the sum with the history partials.
+template <int D>
+struct DqLds {
+  using S = BwdStrides<D>;
+  static constexpr int KR = kBwdKN * S::RS;   // K rows for S^T = K Q^T
+  static constexpr int KT = kBwdKN * S::TS;   // K rows for the transpose read (K^T)
+  static constexpr int VR = kBwdKN * S::RS;   // V rows for dP^T = V dO^T
+  static constexpr int BUF = KR + KT + VR;
+  static constexpr int TOTAL = 2 * BUF;
+};
+
+template <int D, bool CUR>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int hkv,
+    int block, int topk, float sl, float scale, int g0, int ng, int nb,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tile_count,
+    const uint32_t* __restrict__ entries, float* __restrict__ dq_part,
+    uint16_t* __restrict__ dq) {
+  using S = BwdStrides<D>;
+  using L = DqLds<D>;
+  constexpr int KS = D / 16, CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
+  const int G = hq / hkv, KH = topk - 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  int b, gi, kbeg, kend, t, hl, slot = 0;
+  bool valid;
+  if (!CUR) {
+    const int tile_id = blockIdx.x;
+    if (tile_id >= *tile_count) return;
+    const int4 tl = tiles[tile_id];
+    const int list = tl.x;
+    const int j = list % nb;
+    gi = (list / nb) % ng;
+    b = list / (nb * ng);
+    kbeg = j * block;
+    kend = kbeg + block;
+    const int e = tl.y + wave * 32 + n;
+    valid = e < tl.z;
+    const uint32_t ent = valid ? entries[e] : 0u;
+    slot = (int)(ent & 31u);
+    t = (int)(ent >> 5) / G;
+    hl = (int)(ent >> 5) % G;
+  } else {
+    // blockIdx.x: 32*kBwdWaves/G-token tile of block blockIdx.y (from the end of the
+    // block, longest first); wave w takes head w % G and token sub-tile w / G
+    const int c = blockIdx.y;
+    gi = blockIdx.z % ng;
+    b = blockIdx.z / ng;
+    const int TS = kBwdWaves / G;                   // G divides kBwdWaves (checked)
+    const int TT = 32 * TS;
+    const int x = gridDim.x - 1 - blockIdx.x;
+    const int t0 = c * block + x * TT;
+    hl = wave % G;
+    t = t0 + (wave / G) * 32 + n;
+    valid = t < min(t0 + TT, (c + 1) * block);
+    kbeg = c * block;
+    kend = min(t0 + TT, (c + 1) * block);
+    if (!valid) t = c * block;
+  }
+  const int g = g0 + gi, h = g * G + hl;
+  const size_t rs = (size_t)hkv * D;
+  const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
+  const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
+  // the row's operands and statistics
+  bf16x8_t bq[KS], bo[KS];
+  const size_t qrow = ((size_t)b * T + t) * hq + h;
+  load_row_operand<D>(bq, q + qrow * D, valid);
+  load_row_operand<D>(bo, dout + qrow * D, valid);
+  const float lse2 = valid ? lse[((size_t)b * hq + h) * T + t] * kLog2e : 0.f;
+  const float dlt = valid ? delta[((size_t)b * hq + h) * T + t] : 0.f;
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  // staging: every thread moves NC 16-byte chunks of the K subtile and of the V subtile
+  constexpr int NC = (kBwdKN * CPR + kBwdThreads - 1) / kBwdThreads;
+  u32x4_t rk[NC], rv[NC];
+  const int nsub = (kend - kbeg + kBwdKN - 1) / kBwdKN;
+  auto load_sub = [&](int i) {
+    const int kb = kbeg + i * kBwdKN;
+    const int nvalid = min(kBwdKN, kend - kb);
+    const int bytes = (int)(nvalid * rs * sizeof(uint16_t));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ci = min((int)threadIdx.x + c * kBwdThreads, kBwdKN * CPR - 1);
+      const int off = (int)(((ci / CPR) * rs + (ci % CPR) * 8) * sizeof(uint16_t));
+      rk[c] = load16(kbase + (size_t)kb * rs, bytes, off);
+      rv[c] = load16(vbase + (size_t)kb * rs, bytes, off);
+    }
+  };
+  auto store_sub = [&](int buf) {
+    char* base = lds + buf * L::BUF;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ci = threadIdx.x + c * kBwdThreads;
+      if ((kBwdKN * CPR) % kBwdThreads == 0 || ci < kBwdKN * CPR) {
+        const int row = ci / CPR, col = (ci % CPR) * 16;
+        *reinterpret_cast<u32x4_t*>(base + row * S::RS + col) = rk[c];
+        *reinterpret_cast<u32x4_t*>(base + L::KR + row * S::TS + col) = rk[c];
+        *reinterpret_cast<u32x4_t*>(base + L::KR + L::KT + row * S::RS + col) = rv[c];
+      }
+    }
+  };
+  load_sub(0);
+  store_sub(0);
+  __syncthreads();
+  for (int i = 0; i < nsub; ++i) {
+    if (i + 1 < nsub) load_sub(i + 1);
+    const char* kr = lds + (i & 1) * L::BUF;
+    const char* kt = kr + L::KR;
+    const char* vr = kt + L::KT;
+    const int kb = kbeg + i * kBwdKN;
+    // S^T and dP^T for the subtile's two 32-key halves
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kk][e] = dp[kk][e] = 0.f;
+      const char* kp = kr + (kk * 32 + n) * S::RS + hf * 16;
+      const char* vp = vr + (kk * 32 + n) * S::RS + hf * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + ks * 32)),
+                             bq[ks], s[kk]);
+        dp[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(vp + ks * 32)),
+                              bo[ks], dp[kk]);
+      }
+    }
+    // P^T and dS^T; keys past kend, and in the current block keys after t, get p = 0
+    bf16x8_t ds[4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int u = kb + kk * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
+        const bool keep = u < kend && (!CUR || u <= t);
+        const float p = keep ? __builtin_amdgcn_exp2f(fmaf(s[kk][e], sl, -lse2)) : 0.f;
+        x[e] = p * (dp[kk][e] - dlt);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
+        ds[2 * kk + hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+      }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = mfma32x32x16(read_t_operand<D>(kt, ks, dt), ds[ks], acc[dt]);
+    if (i + 1 < nsub) store_sub((i + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!valid) return;
+  const int ngq = ng * G;
+  const size_t prow = ((size_t)(b * ngq + gi * G + hl) * T + t) * KH;
+  if (!CUR) {
+    float* po = dq_part + (prow + slot) * D + hf * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        f32x4_t w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = acc[dt][ii * 4 + r] * scale;
+        *reinterpret_cast<f32x4_t*>(po + dt * 32 + ii * 8) = w;
+      }
+    return;
+  }
+  // current block: this part plus the row's history partials
+  const int nh = min(t / block, KH);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] *= scale;
+  for (int sidx = 0; sidx < nh; ++sidx) {
+    const float* pp = dq_part + (prow + sidx) * D + hf * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(pp + dt * 32 + ii * 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][ii * 4 + r] += w[r];
+      }
+  }
+  uint16_t* orow = dq + qrow * D + hf * 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      u32x2_t pk;
+      pk[0] = f32_to_bf16_rne(acc[dt][ii * 4]) | (f32_to_bf16_rne(acc[dt][ii * 4 + 1]) << 16);
+      pk[1] = f32_to_bf16_rne(acc[dt][ii * 4 + 2]) | (f32_to_bf16_rne(acc[dt][ii * 4 + 3]) << 16);
+      *reinterpret_cast<u32x2_t*>(orow + dt * 32 + ii * 8) = pk;
+    }
+}
+
+// ----------------------------------------------------------------------- dK/dV kernel
+// One workgroup = 32 * kKvWaves keys of block j of kv-head g (wave w: keys
+// kc0 + 32w + n).  Rows: the history list of (b, g, j) from the inverted index, then
+// the rows of block j from token kc0 on (causal: key u is attended by token t >= u), G
+// heads each.
+template <int D>
+struct KvLds {
+  using S = BwdStrides<D>;
+  static constexpr int QR = 32 * S::RS;
+  static constexpr int QT = 32 * S::TS;
+  static constexpr int BUF = 2 * (QR + QT) + 3 * 32 * 4;   // Q, dO; lse2, delta, t
+  static constexpr int TOTAL = 2 * BUF;
+};
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int hkv,
+    int block, float sl, float scale, int g0, int ng, int nb,
+    const int32_t* __restrict__ list_offsets, const uint32_t* __restrict__ entries,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  using S = BwdStrides<D>;
+  using L = KvLds<D>;
+  constexpr int KS = D / 16, CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
+  const int G = hq / hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  const int j = blockIdx.y, gi = blockIdx.z % ng, b = blockIdx.z / ng, g = g0 + gi;
+  const int kc0 = j * block + blockIdx.x * 32 * kKvWaves;
+  const int u = kc0 + wave * 32 + n;                  // this lane's key
+  const int kend = (j + 1) * block;
+  const bool kvalid = u < kend;
+  const int list = (b * ng + gi) * nb + j;
+  const int hbeg = list_offsets ? list_offsets[list] : 0;
+  const int nhist = list_offsets ? list_offsets[list + 1] - hbeg : 0;
+  // tokens of block j before kc0 attend none of these keys
+  const int nrows = nhist + (kend - kc0) * G;
+  // K and V rows of this lane's key: B operands (lane = key column)
+  bf16x8_t bk[KS], bv[KS];
+  load_row_operand<D>(bk, k + (((size_t)b * T + (kvalid ? u : 0)) * hkv + g) * D, kvalid);
+  load_row_operand<D>(bv, v + (((size_t)b * T + (kvalid ? u : 0)) * hkv + g) * D, kvalid);
+  f32x16_t ak[D / 32], av[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ak[dt][i] = av[dt][i] = 0.f;
+
+  // staging of a 32-row group: thread x moves 16-byte chunk x % (32*CPR) of Q (x <
+  // 32*CPR) or dO; threads 0..31 also the rows' lse2, delta and t
+  constexpr int CHUNKS = 2 * 32 * CPR;
+  constexpr int NC = (CHUNKS + kKvThreads - 1) / kKvThreads;
+  u32x4_t rg[NC];
+  float meta_f = 0.f, meta_d = 0.f;
+  int meta_t = 0;
+  auto row_of = [&](int r, int& t, int& h) {   // group-relative row -> token, head
+    if (r < nhist) {
+      const uint32_t rr = entries[hbeg + r] >> 5;
+      t = (int)rr / G;
+      h = g * G + (int)rr % G;
+    } else {
+      const int rc = r - nhist;
+      t = kc0 + rc / G;
+      h = g * G + rc % G;
+    }
+  };
+  auto load_group = [&](int r0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int x = min((int)threadIdx.x + c * kKvThreads, CHUNKS - 1);
+      const int which = x / (32 * CPR), y = x % (32 * CPR), r = r0 + y / CPR;
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (r < nrows) {
+        int t, h;
+        row_of(r, t, h);
+        const uint16_t* src = (which ? dout : q) + (((size_t)b * T + t) * hq + h) * D;
+        val = *reinterpret_cast<const u32x4_t*>(src + (y % CPR) * 8);
+      }
+      rg[c] = val;
+    }
+    if (threadIdx.x < 32) {
+      const int r = r0 + threadIdx.x;
+      if (r < nrows) {
+        int t, h;
+        row_of(r, t, h);
+        const size_t at = ((size_t)b * hq + h) * T + t;
+        meta_f = lse[at] * kLog2e;
+        meta_d = delta[at];
+        meta_t = r < nhist ? 0x7fffffff : t;
+      } else {
+        meta_f = INFINITY;   // p = 0
+        meta_d = 0.f;
+        meta_t = 0x7fffffff;
+      }
+    }
+  };
+  auto store_group = [&](int buf) {
+    char* base = lds + buf * L::BUF;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int x = threadIdx.x + c * kKvThreads;
+      if (CHUNKS % kKvThreads == 0 || x < CHUNKS) {
+        const int which = x / (32 * CPR), y = x % (32 * CPR);
+        const int row = y / CPR, col = (y % CPR) * 16;
+        char* t0 = base + which * (L::QR + L::QT);
+        *reinterpret_cast<u32x4_t*>(t0 + row * S::RS + col) = rg[c];
+        *reinterpret_cast<u32x4_t*>(t0 + L::QR + row * S::TS + col) = rg[c];
+      }
+    }
+    if (threadIdx.x < 32) {
+      float* mf = reinterpret_cast<float*>(base + 2 * (L::QR + L::QT));
+      mf[threadIdx.x] = meta_f;
+      mf[32 + threadIdx.x] = meta_d;
+      reinterpret_cast<int*>(mf + 64)[threadIdx.x] = meta_t;
+    }
+  };
+  const int ngroups = (nrows + 31) / 32;
+  load_group(0);
+  store_group(0);
+  __syncthreads();
+  for (int gidx = 0; gidx < ngroups; ++gidx) {
+    if (gidx + 1 < ngroups) load_group((gidx + 1) * 32);
+    const char* base = lds + (gidx & 1) * L::BUF;
+    const char* qr = base;
+    const char* qt = base + L::QR;
+    const char* dr = base + L::QR + L::QT;
+    const char* dtr = dr + L::QR;
+    const float* mf = reinterpret_cast<const float*>(base + 2 * (L::QR + L::QT));
+    // S = Q K^T and dP = dO V^T: rows (registers) x keys (lanes)
+    f32x16_t s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+    const char* qp = qr + n * S::RS + hf * 16;
+    const char* dpp = dr + n * S::RS + hf * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + ks * 32)), bk[ks], s);
+      dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(dpp + ks * 32)), bv[ks],
+                        dp);
+    }
+    // P and dS; register e holds row (e/4)*8 + hf*4 + e%4
+    float p[16], x[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int r0 = q4 * 8 + hf * 4;
+      const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(mf + r0);
+      const f32x4_t ld = *reinterpret_cast<const f32x4_t*>(mf + 32 + r0);
+      const int4 lt = *reinterpret_cast<const int4*>(mf + 64 + r0);
+      const int tt[4] = {lt.x, lt.y, lt.z, lt.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = q4 * 4 + r;
+        const bool keep = kvalid && u <= tt[r];
+        p[e] = keep ? __builtin_amdgcn_exp2f(fmaf(s[e], sl, -lf[r])) : 0.f;
+        x[e] = p[e] * (dp[e] - ld[r]);
+      }
+    }
+    bf16x8_t pp[2], dsp[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint32_t w1[4], w2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w1[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+        w2[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
+      }
+      pp[hh] = as_bf16x8(u32x4_t{w1[0], w1[1], w1[2], w1[3]});
+      dsp[hh] = as_bf16x8(u32x4_t{w2[0], w2[1], w2[2], w2[3]});
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (summed over the group's 32 rows)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        av[dt] = mfma32x32x16(read_t_operand<D>(dtr, ks, dt), pp[ks], av[dt]);
+        ak[dt] = mfma32x32x16(read_t_operand<D>(qt, ks, dt), dsp[ks], ak[dt]);
+      }
+    if (gidx + 1 < ngroups) store_group((gidx + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!kvalid) return;
+  uint16_t* krow = dk + (((size_t)b * T + u) * hkv + g) * D + hf * 4;
+  uint16_t* vrow = dv + (((size_t)b * T + u) * hkv + g) * D + hf * 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      u32x2_t a, c;
+      a[0] = f32_to_bf16_rne(ak[dt][ii * 4] * scale) |
+             (f32_to_bf16_rne(ak[dt][ii * 4 + 1] * scale) << 16);
+      a[1] = f32_to_bf16_rne(ak[dt][ii * 4 + 2] * scale) |
+             (f32_to_bf16_rne(ak[dt][ii * 4 + 3] * scale) << 16);
+      c[0] = f32_to_bf16_rne(av[dt][ii * 4]) | (f32_to_bf16_rne(av[dt][ii * 4 + 1]) << 16);
+      c[1] = f32_to_bf16_rne(av[dt][ii * 4 + 2]) | (f32_to_bf16_rne(av[dt][ii * 4 + 3]) << 16);
+      *reinterpret_cast<u32x2_t*>(krow + dt * 32 + ii * 8) = a;
+      *reinterpret_cast<u32x2_t*>(vrow + dt * 32 + ii * 8) = c;
+    }
+}
+
+// ------------------------------------------------------------------------- launchers
+int bwd_tile_rows() { return kBwdWaves * 32; }
+
+// the current-block dQ tiles put the G heads of a kv-head on different waves
+bool bwd_supported(const Shape& s) { return kBwdWaves % s.G() == 0; }
+
+hipError_t launch_bwd_delta(const Shape& s, const uint16_t* out, const uint16_t* dout,
+                            float* delta, hipStream_t st) {
+  const long rows = (long)s.b * s.T * s.hq;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                     out, dout, s.T, s.hq, s.d, rows, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_history(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* dout, const float* lse,
+                                 const float* delta, float scale, int g0, int ng,
+                                 const int4* tiles, const int32_t* tile_count, int max_tiles,
+                                 const uint32_t* entries, float* dq_part, hipStream_t st) {
+  if (max_tiles <= 0) return hipSuccess;
+  const float sl = scale * kLog2e;
+#define MOBA_DQH(DD)                                                                       \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, false>), dim3(max_tiles), dim3(kBwdThreads), 0, st, \
+                     q, k, v, dout, lse, delta, s.T, s.hq, s.hkv, s.block, s.topk, sl, scale, \
+                     g0, ng, s.nb(), tiles, tile_count, entries, dq_part, nullptr)
+  if (s.d == 128) MOBA_DQH(128);
+  else MOBA_DQH(64);
+#undef MOBA_DQH
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_current(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* dout, const float* lse,
+                                 const float* delta, float scale, int g0, int ng,
+                                 const float* dq_part, uint16_t* dq, hipStream_t st) {
+  const float sl = scale * kLog2e;
+  const int TT = 32 * (kBwdWaves / s.G());
+  dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng);
+#define MOBA_DQC(DD)                                                                       \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, true>), grid, dim3(kBwdThreads), 0, st, q, k, v,     \
+                     dout, lse, delta, s.T, s.hq, s.hkv, s.block, s.topk, sl, scale, g0, ng,  \
+                     s.nb(), nullptr, nullptr, nullptr, const_cast<float*>(dq_part), dq)
+  if (s.d == 128) MOBA_DQC(128);
+  else MOBA_DQC(64);
+#undef MOBA_DQC
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* dout, const float* lse,
+                           const float* delta, float scale, int g0, int ng,
+                           const int32_t* list_offsets, const uint32_t* entries, uint16_t* dk,
+                           uint16_t* dv, hipStream_t st) {
+  const float sl = scale * kLog2e;
+  const int kpw = 32 * kKvWaves;
+  dim3 grid((s.block + kpw - 1) / kpw, s.nb(), s.b * ng);
+#define MOBA_KV(DD)                                                                        \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD>), grid, dim3(kKvThreads), 0, st, q, k, v, dout,    \
+                     lse, delta, s.T, s.hq, s.hkv, s.block, sl, scale, g0, ng, s.nb(),        \
+                     list_offsets, entries, dk, dv)
+  if (s.d == 128) MOBA_KV(128);
+  else MOBA_KV(64);
+#undef MOBA_KV
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -89,6 +89,46 @@ bool layout_ok(const Layout& L) {
   return L.n_entries < (1ll << 31) && L.max_tiles < (1ll << 31);
 }
 
+// Backward workspace: D for the whole problem, then per group of ng kv-heads the
+// inverted index (as in the forward, cut in tiles of the dQ kernel's rows) and the
+// fp32 dQ parts of every (row, history slot).
+struct BwdLayout {
+  size_t delta, chunk_counts, list_count, list_offsets, tile_offsets, tiles, entries,
+      dq_part;
+  size_t total;
+  long long n_entries, max_tiles;
+};
+
+BwdLayout make_bwd_layout(const Shape& s, int ng) {
+  BwdLayout L{};
+  const size_t nb = s.nb();
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.delta = take((size_t)s.b * s.hq * s.T * sizeof(float));
+  const size_t nlists = (size_t)s.b * ng * nb;
+  const size_t nchunks = moba::index_chunks(s);
+  L.n_entries = (long long)s.b * ng * s.G() * entries_per_head(s);
+  const int tm = moba::bwd_tile_rows();
+  L.max_tiles = (L.n_entries + tm - 1) / tm + (long long)nlists;
+  L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
+  L.list_count = take(nlists * sizeof(int32_t));
+  L.list_offsets = take((nlists + 1) * sizeof(int32_t));
+  L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
+  L.tiles = take((size_t)L.max_tiles * sizeof(int4));
+  L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
+  L.dq_part = take((size_t)s.b * ng * s.G() * s.T * s.KH() * s.d * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+bool bwd_layout_ok(const BwdLayout& L) {
+  return L.n_entries < (1ll << 31) && L.max_tiles < (1ll << 31);
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_ERR_HIP; }
 
 #define MOBA_TRY(expr)                        \
@@ -372,6 +412,82 @@ int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
       reinterpret_cast<int32_t*>(ws + cc + lc), nullptr, entries,
       (long long)s.b * kv_count * s.G() * entries_per_head(s),
       static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------- backward
+size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
+                                     int head_dim, int block, int topk,
+                                     size_t* min_bytes) {
+  if (min_bytes) *min_bytes = 0;
+  if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  if (!moba::bwd_supported(s)) return 0;
+  const BwdLayout one = make_bwd_layout(s, 1);
+  if (!bwd_layout_ok(one)) return 0;
+  if (min_bytes) *min_bytes = one.total;
+  for (int ng = hkv; ng >= 1; --ng) {
+    const BwdLayout L = make_bwd_layout(s, ng);
+    if (bwd_layout_ok(L)) return L.total;
+  }
+  return one.total;
+}
+
+int moba_backward(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const int32_t* idx, const void* dout, int batch,
+                  int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+                  float scale, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out || !lse || !idx || !dout || !dq || !dk || !dv || !workspace)
+    return MOBA_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  if (!moba::bwd_supported(s)) return MOBA_ERR_UNSUPPORTED;
+  int ng = hkv;
+  BwdLayout L = make_bwd_layout(s, ng);
+  while (ng > 1 && (L.total > workspace_bytes || !bwd_layout_ok(L)))
+    L = make_bwd_layout(s, --ng);
+  if (L.total > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  if (!bwd_layout_ok(L)) return MOBA_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  const uint16_t* vb = static_cast<const uint16_t*>(v);
+  const uint16_t* gb = static_cast<const uint16_t*>(dout);
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* dq_part = reinterpret_cast<float*>(ws + L.dq_part);
+  MOBA_TRY(moba::launch_bwd_delta(s, static_cast<const uint16_t*>(out), gb, delta, hs));
+  for (int g0 = 0; g0 < hkv; g0 += ng) {
+    const int ngc = ng < hkv - g0 ? ng : hkv - g0;
+    const int nlc = s.b * ngc * s.nb();
+    const int32_t* list_offsets = nullptr;
+    const uint32_t* entries = nullptr;
+    if (s.KH() > 0) {
+      int32_t* lo = reinterpret_cast<int32_t*>(ws + L.list_offsets);
+      int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
+      int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
+      uint32_t* ent = reinterpret_cast<uint32_t*>(ws + L.entries);
+      MOBA_TRY(moba::launch_index(s, idx, g0, ngc, moba::bwd_tile_rows(),
+                                  reinterpret_cast<int32_t*>(ws + L.chunk_counts),
+                                  reinterpret_cast<int32_t*>(ws + L.list_count), lo,
+                                  tile_offsets, tiles, ent, L.n_entries, hs));
+      const BwdLayout Lc = make_bwd_layout(s, ngc);
+      MOBA_TRY(moba::launch_bwd_dq_history(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
+                                           tiles, tile_offsets + nlc, (int)Lc.max_tiles,
+                                           ent, dq_part, hs));
+      list_offsets = lo;
+      entries = ent;
+    }
+    MOBA_TRY(moba::launch_bwd_dq_current(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
+                                         dq_part, static_cast<uint16_t*>(dq), hs));
+    MOBA_TRY(moba::launch_bwd_dkdv(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
+                                   list_offsets, entries, static_cast<uint16_t*>(dk),
+                                   static_cast<uint16_t*>(dv), hs));
+  }
+  return MOBA_OK;
 }
 
 }  // extern "C"

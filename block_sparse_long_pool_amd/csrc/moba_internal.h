@@ -102,4 +102,26 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
                                float* lse, hipStream_t st);
 int history_tile_rows();
 
+// backward with the selection held fixed: D = rowsum(dO * out), dQ over the history
+// tiles (fp32 partials per row and slot) and the current blocks (sum -> dq), and dK/dV
+// per 32*4 keys of a block over the rows that attend them
+bool bwd_supported(const Shape& s);
+int bwd_tile_rows();
+hipError_t launch_bwd_delta(const Shape& s, const uint16_t* out, const uint16_t* dout,
+                            float* delta, hipStream_t st);
+hipError_t launch_bwd_dq_history(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* dout, const float* lse,
+                                 const float* delta, float scale, int g0, int ng,
+                                 const int4* tiles, const int32_t* tile_count, int max_tiles,
+                                 const uint32_t* entries, float* dq_part, hipStream_t st);
+hipError_t launch_bwd_dq_current(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const uint16_t* dout, const float* lse,
+                                 const float* delta, float scale, int g0, int ng,
+                                 const float* dq_part, uint16_t* dq, hipStream_t st);
+hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* dout, const float* lse,
+                           const float* delta, float scale, int g0, int ng,
+                           const int32_t* list_offsets, const uint32_t* entries, uint16_t* dk,
+                           uint16_t* dv, hipStream_t st);
+
 }  // namespace moba

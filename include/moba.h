@@ -119,6 +119,47 @@ int moba_forward_timed(const void* q, const void* k, const void* v, int batch, i
                        void* out, float* lse, int32_t* idx, void* workspace,
                        size_t workspace_bytes, void* stream, void* const* stage_events);
 
+/* ---------------------------------------------------------------------------
+ * Backward pass, for training with MoBA attention (MoBA README, bullet "Trainable
+ * Block Sparse Attention"; paper summary page on atlas.scime.ai, which reports
+ * continual pre-training and SFT with MoBA layers).  The block selection of the
+ * forward (idx) is held fixed: it is a top-k over inner products with parameter-less
+ * mean-pooled keys (README bullet "Parameter-less Gating Mechanism"), piecewise
+ * constant, so no gradient flows through it.  For each query row, with N its
+ * attended keys (its selected history blocks whole, its current block up to itself)
+ * and p_u = exp(scale q.k_u - lse), D = dO.out:
+ *   dq      = scale * sum_u p_u (dO.v_u - D) k_u
+ *   dk_u   += scale * p_u (dO.v_u - D) q          (summed over the rows attending u
+ *   dv_u   += p_u dO                                and the G query heads of a kv-head)
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes moba_backward uses: the size that processes all kv-heads in one
+ * pass is returned, the one-kv-head-per-pass size stored in *min_bytes (if not
+ * NULL); sizes in between loop over groups of kv-heads, as for moba_forward.  Returns
+ * 0 if the shape is not supported by the backward (see moba_backward). */
+size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
+                                     int head_dim, int block, int topk,
+                                     size_t* min_bytes);
+
+/* Gradients of moba_forward with respect to q, k and v.
+ *   q, k, v, out, lse, idx   the inputs and the outputs of moba_forward for this
+ *                            problem (device pointers, layouts as above); idx must be
+ *                            a valid selection in moba_forward's format
+ *   dout                     [b, T, hq, d] bf16, the gradient of out
+ *   dq                       [b, T, hq, d] bf16, written
+ *   dk, dv                   [b, T, hkv, d] bf16, written (every element)
+ * Accumulation is float32; dq sums fp32 per-history-block parts in slot order and dk,
+ * dv are each summed by one workgroup in a fixed row order: deterministic.  Shape
+ * limits are moba_forward's plus G = hq / hkv in {1, 2, 4, 8} (MOBA_ERR_UNSUPPORTED
+ * otherwise).  `workspace` must hold at least the minimum of
+ * moba_backward_workspace_bytes and be 256-byte aligned (MOBA_ERR_WORKSPACE,
+ * MOBA_ERR_INVALID_ARG).  Enqueued on `stream` without synchronising. */
+int moba_backward(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const int32_t* idx, const void* dout, int batch,
+                  int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+                  float scale, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* A static, human-readable message for a status code. */
 const char* moba_strerror(int status);
 

@@ -13,7 +13,7 @@ KV heads, head_dim 128), which the MoBA paper continues to train to 1M tokens (p
 Key results).  No weights are used; only the shape.
 
 Random streams: ``numpy.random.default_rng([seed, tensor_id, head])`` with
-tensor_id Q=0, K=1, V=2, key offsets=3, planted blocks=4, query noise=5.  Each head
+tensor_id Q=0, K=1, V=2, key offsets=3, planted blocks=4, query noise=5, output gradient=6.  Each head
 is drawn on its own, so any head can be regenerated alone.
 """
 from __future__ import annotations
@@ -27,10 +27,10 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "make_inputs", "f32_to_bf16_bits",
-    "bf16_to_f64", "bf16_to_f32", "to_torch_bf16", "small_workload",
+    "bf16_to_f64", "bf16_to_f32", "to_torch_bf16", "small_workload", "make_output_grad",
 ]
 
-Q_ID, K_ID, V_ID, OFFSET_ID, PLANT_ID, NOISE_ID = 0, 1, 2, 3, 4, 5
+Q_ID, K_ID, V_ID, OFFSET_ID, PLANT_ID, NOISE_ID, DOUT_ID = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -247,3 +247,9 @@ def _planted_queries(w: Workload, kb: np.ndarray):
             q[bi, :, h, :] = (dirn + eps).astype(np.float32)
             planted[bi, h] = P.astype(np.int32)
     return f32_to_bf16_bits(q), planted
+
+
+def make_output_grad(w: Workload) -> np.ndarray:
+    """The upstream gradient dL/dout of a backward test or benchmark: [b,T,Hq,d] bf16
+    bits of i.i.d. N(0,1), one stream per query head (tensor_id 6)."""
+    return _bf16_heads(w, DOUT_ID, w.hq)
