@@ -23,6 +23,8 @@
 // lane l holds column l%32 and rows (i/4)*8 + (l/32)*4 + i%4, and a transposed operand
 // is read from a row-major LDS tile with ds_read_b64_tr_b16 in the order the result
 // registers hold the summation index.
+#include <type_traits>
+
 #include "moba_internal.h"
 
 namespace moba {
@@ -30,8 +32,8 @@ namespace {
 
 constexpr int kBwdWaves = 8;                // dQ kernel
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kKvWaves = 4;                 // dK/dV kernel: one wave per SIMD, 512 registers
-constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvTiles = 4;                 // dK/dV kernel: 32-key tiles per workgroup,
+constexpr int kKvThreads = 2 * 64 * kKvTiles;   // two waves each
 constexpr int kBwdKN = 64;                  // keys per subtile in the dQ kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -319,21 +321,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------------- dK/dV kernel
-// One workgroup = 32 * kKvWaves keys of block j of kv-head g (wave w: keys
-// kc0 + 32w + n).  Rows: the history list of (b, g, j) from the inverted index, then
-// the rows of block j from token kc0 on (causal: key u is attended by token t >= u), G
-// heads each.
+// One workgroup = 32 * kKvTiles keys of block j of kv-head g.  Rows: the history list
+// of (b, g, j) from the inverted index, then the rows of block j from token kc0 on
+// (causal: key u is attended by token t >= u), G heads each, in groups of 32.
+// Each 32-key tile has two waves on one SIMD: wave "P" computes S = Q K^T, P, and
+// dV^T += dO^T P; wave "dS" computes dP = dO V^T, takes P through LDS, and
+// dK^T += Q^T dS with dS = P (dP - D).  Each wave keeps one 32 x D accumulator and one
+// B operand, so two waves fit per SIMD and one's VALU work overlaps the other's MFMAs.
 template <int D>
 struct KvLds {
   using S = BwdStrides<D>;
   static constexpr int QR = 32 * S::RS;
   static constexpr int QT = 32 * S::TS;
   static constexpr int BUF = 2 * (QR + QT) + 3 * 32 * 4;   // Q, dO; lse2, delta, t
-  static constexpr int TOTAL = 2 * BUF;
+  static constexpr int PX = kKvTiles * 64 * 32;             // P tiles, 32 bytes per lane
+  static constexpr int TOTAL = 2 * BUF + PX;
 };
 
 template <int D>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int hkv,
@@ -346,9 +352,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
   const int G = hq / hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  const int j = blockIdx.y, gi = blockIdx.z % ng, b = blockIdx.z / ng, g = g0 + gi;
-  const int kc0 = j * block + blockIdx.x * 32 * kKvWaves;
-  const int u = kc0 + wave * 32 + n;                  // this lane's key
+  const int tile = wave % kKvTiles;
+  const bool role_ds = wave >= kKvTiles;      // false: S, P, dV   true: dP, dS, dK
+  // work item: key chunk fastest, then block, then (b, kv-head)
+  const int W = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int wx = W % gridDim.x, wyz = W / gridDim.x;
+  const int j = wyz % gridDim.y, gi = (wyz / gridDim.y) % ng, b = wyz / (gridDim.y * ng);
+  const int g = g0 + gi;
+  const int kc0 = j * block + wx * 32 * kKvTiles;
+  const int u = kc0 + tile * 32 + n;                  // this lane's key
   const int kend = (j + 1) * block;
   const bool kvalid = u < kend;
   const int list = (b * ng + gi) * nb + j;
@@ -356,165 +368,216 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(
   const int nhist = list_offsets ? list_offsets[list + 1] - hbeg : 0;
   // tokens of block j before kc0 attend none of these keys
   const int nrows = nhist + (kend - kc0) * G;
-  // K and V rows of this lane's key: B operands (lane = key column)
-  bf16x8_t bk[KS], bv[KS];
-  load_row_operand<D>(bk, k + (((size_t)b * T + (kvalid ? u : 0)) * hkv + g) * D, kvalid);
-  load_row_operand<D>(bv, v + (((size_t)b * T + (kvalid ? u : 0)) * hkv + g) * D, kvalid);
-  f32x16_t ak[D / 32], av[D / 32];
+  // the K (wave P) or V (wave dS) row of this lane's key: the B operand, lane = key
+  bf16x8_t bkv[KS];
+  load_row_operand<D>(bkv, (role_ds ? v : k) + (((size_t)b * T + (kvalid ? u : 0)) * hkv + g) * D,
+                      kvalid);
+  f32x16_t acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ak[dt][i] = av[dt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  // staging of a 32-row group: thread x moves 16-byte chunk x % (32*CPR) of Q (x <
-  // 32*CPR) or dO; threads 0..31 also the rows' lse2, delta and t
+  // Staging of a 32-row group: thread x moves 16-byte chunk x % (32*CPR) of Q (x <
+  // 32*CPR) or of dO; threads 0..31 also the rows' lse2, delta and causal limit t.  Rows
+  // are packed as rr = t*G + h%G (history rows: the inverted index's entries).  While
+  // group i is computed, the row data of group i+1 and the row ids of group i+2 are in
+  // flight, so the index read and the gather that depends on it overlap.  Rows past the
+  // end read a valid row (token kc0) and get p = 0 from lse2 = +inf, so the fetch has
+  // no branches.
   constexpr int CHUNKS = 2 * 32 * CPR;
-  constexpr int NC = (CHUNKS + kKvThreads - 1) / kKvThreads;
-  u32x4_t rg[NC];
-  float meta_f = 0.f, meta_d = 0.f;
-  int meta_t = 0;
-  auto row_of = [&](int r, int& t, int& h) {   // group-relative row -> token, head
-    if (r < nhist) {
-      const uint32_t rr = entries[hbeg + r] >> 5;
-      t = (int)rr / G;
-      h = g * G + (int)rr % G;
-    } else {
-      const int rc = r - nhist;
-      t = kc0 + rc / G;
-      h = g * G + rc % G;
-    }
+  constexpr int NC = CHUNKS / kKvThreads;
+  static_assert(CHUNKS % kKvThreads == 0, "every thread moves whole chunks");
+  const int gshift = __builtin_ctz((unsigned)G);   // G is a power of two
+  const uint32_t safe_rr = (uint32_t)kc0 << gshift;
+  // entries of this list through a buffer descriptor: reads past nhist return 0
+  const __amdgpu_buffer_rsrc_t ent_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(entries ? entries + hbeg : nullptr), (short)0, nhist * 4,
+      0x00020000);
+  const int row_base = (b * T) * hq + g * G;        // row index of (b, t=0, head g*G)
+  const int meta_base = (b * hq + g * G) * T;       // lse/delta index of (b, g*G, t=0)
+  int crow[NC], ccol[NC];
+  bool cdo[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int x = threadIdx.x + c * kKvThreads;
+    cdo[c] = x >= 32 * CPR;
+    crow[c] = (x % (32 * CPR)) / CPR;
+    ccol[c] = (x % CPR) * 8;
+  }
+  struct Ids {
+    uint32_t rr[NC];
+    uint32_t mr;       // the meta row of threads 0..31
+    bool mhist, mvalid;
   };
-  auto load_group = [&](int r0) {
+  struct Rows {
+    u32x4_t c[NC];
+    float f, d;
+    int t;
+  };
+  auto rowid = [&](int r) -> uint32_t {
+    const uint32_t e = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ent_rsrc, r * 4, 0, 0);
+    const int rc = r - nhist;
+    const uint32_t cur = ((uint32_t)(kc0 + (rc >> gshift)) << gshift) | (uint32_t)(rc & (G - 1));
+    return r >= nrows ? safe_rr : (r < nhist ? e >> 5 : cur);
+  };
+  auto fetch_ids = [&](int r0, Ids& id) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) id.rr[c] = rowid(r0 + crow[c]);
+    const int r = r0 + (threadIdx.x & 31);
+    id.mr = rowid(r);
+    id.mhist = r < nhist;
+    id.mvalid = r < nrows;
+  };
+  auto fetch_rows = [&](const Ids& id, Rows& rd) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int x = min((int)threadIdx.x + c * kKvThreads, CHUNKS - 1);
-      const int which = x / (32 * CPR), y = x % (32 * CPR), r = r0 + y / CPR;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (r < nrows) {
-        int t, h;
-        row_of(r, t, h);
-        const uint16_t* src = (which ? dout : q) + (((size_t)b * T + t) * hq + h) * D;
-        val = *reinterpret_cast<const u32x4_t*>(src + (y % CPR) * 8);
-      }
-      rg[c] = val;
+      const uint32_t rr = id.rr[c];
+      const int row = row_base + (int)(rr >> gshift) * hq + (int)(rr & (G - 1));
+      const uint16_t* src = (cdo[c] ? dout : q) + (size_t)row * D + ccol[c];
+      rd.c[c] = *reinterpret_cast<const u32x4_t*>(src);
     }
-    if (threadIdx.x < 32) {
-      const int r = r0 + threadIdx.x;
-      if (r < nrows) {
-        int t, h;
-        row_of(r, t, h);
-        const size_t at = ((size_t)b * hq + h) * T + t;
-        meta_f = lse[at] * kLog2e;
-        meta_d = delta[at];
-        meta_t = r < nhist ? 0x7fffffff : t;
-      } else {
-        meta_f = INFINITY;   // p = 0
-        meta_d = 0.f;
-        meta_t = 0x7fffffff;
-      }
-    }
+    const int t = (int)(id.mr >> gshift);
+    const int at = meta_base + (int)(id.mr & (G - 1)) * T + t;
+    const float lv = lse[at], dv0 = delta[at];
+    rd.f = id.mvalid ? lv * kLog2e : INFINITY;   // p = 0 for rows past the end
+    rd.d = id.mvalid ? dv0 : 0.f;
+    rd.t = id.mhist ? 0x7fffffff : t;
   };
-  auto store_group = [&](int buf) {
+  auto store_rows = [&](const Rows& rd, int buf) {
     char* base = lds + buf * L::BUF;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int x = threadIdx.x + c * kKvThreads;
-      if (CHUNKS % kKvThreads == 0 || x < CHUNKS) {
-        const int which = x / (32 * CPR), y = x % (32 * CPR);
-        const int row = y / CPR, col = (y % CPR) * 16;
-        char* t0 = base + which * (L::QR + L::QT);
-        *reinterpret_cast<u32x4_t*>(t0 + row * S::RS + col) = rg[c];
-        *reinterpret_cast<u32x4_t*>(t0 + L::QR + row * S::TS + col) = rg[c];
-      }
+      char* t0 = base + (cdo[c] ? L::QR + L::QT : 0) + crow[c] * S::RS + ccol[c] * 2;
+      *reinterpret_cast<u32x4_t*>(t0) = rd.c[c];
+      *reinterpret_cast<u32x4_t*>(t0 + L::QR + crow[c] * (S::TS - S::RS)) = rd.c[c];
     }
     if (threadIdx.x < 32) {
       float* mf = reinterpret_cast<float*>(base + 2 * (L::QR + L::QT));
-      mf[threadIdx.x] = meta_f;
-      mf[32 + threadIdx.x] = meta_d;
-      reinterpret_cast<int*>(mf + 64)[threadIdx.x] = meta_t;
+      mf[threadIdx.x] = rd.f;
+      mf[32 + threadIdx.x] = rd.d;
+      reinterpret_cast<int*>(mf + 64)[threadIdx.x] = rd.t;
     }
   };
-  const int ngroups = (nrows + 31) / 32;
-  load_group(0);
-  store_group(0);
-  __syncthreads();
-  for (int gidx = 0; gidx < ngroups; ++gidx) {
-    if (gidx + 1 < ngroups) load_group((gidx + 1) * 32);
-    const char* base = lds + (gidx & 1) * L::BUF;
-    const char* qr = base;
-    const char* qt = base + L::QR;
-    const char* dr = base + L::QR + L::QT;
-    const char* dtr = dr + L::QR;
+  // rows nhist + (0 .. 32*kKvTiles*G - 1) are the tokens kc0 .. kc0 + 32*kKvTiles - 1,
+  // the only ones that see keys after themselves; other groups need no causal mask
+  const int mask_lo = nhist, mask_hi = nhist + 32 * kKvTiles * G;
+  char* px = lds + 2 * L::BUF + (tile * 64 + lane) * 32;   // this lane's P slot
+  // One 32-row group.  Register e of a 32x32 result holds row (e/4)*8 + hf*4 + e%4.
+  auto compute = [&](int buf, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const char* base = lds + buf * L::BUF;
     const float* mf = reinterpret_cast<const float*>(base + 2 * (L::QR + L::QT));
-    // S = Q K^T and dP = dO V^T: rows (registers) x keys (lanes)
-    f32x16_t s, dp;
+    // S = Q K^T (wave P) or dP = dO V^T (wave dS): rows x keys
+    const char* ar = base + (role_ds ? L::QR + L::QT : 0) + n * S::RS + hf * 16;
+    f32x16_t sc = {};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
-    const char* qp = qr + n * S::RS + hf * 16;
-    const char* dpp = dr + n * S::RS + hf * 16;
+    for (int ks = 0; ks < KS; ++ks)
+      sc = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(ar + ks * 32)), bkv[ks],
+                        sc);
+    bf16x8_t op[2];
+    if (!role_ds) {
+      float p[16];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + ks * 32)), bk[ks], s);
-      dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(dpp + ks * 32)), bv[ks],
-                        dp);
-    }
-    // P and dS; register e holds row (e/4)*8 + hf*4 + e%4
-    float p[16], x[16];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(mf + q4 * 8 + hf * 4);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int r0 = q4 * 8 + hf * 4;
-      const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(mf + r0);
-      const f32x4_t ld = *reinterpret_cast<const f32x4_t*>(mf + 32 + r0);
-      const int4 lt = *reinterpret_cast<const int4*>(mf + 64 + r0);
-      const int tt[4] = {lt.x, lt.y, lt.z, lt.w};
+        for (int r = 0; r < 4; ++r)
+          p[q4 * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[q4 * 4 + r], sl, -lf[r]));
+      }
+      if (MASKED) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = q4 * 4 + r;
-        const bool keep = kvalid && u <= tt[r];
-        p[e] = keep ? __builtin_amdgcn_exp2f(fmaf(s[e], sl, -lf[r])) : 0.f;
-        x[e] = p[e] * (dp[e] - ld[r]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int4 lt = *reinterpret_cast<const int4*>(mf + 64 + q4 * 8 + hf * 4);
+          const int tt[4] = {lt.x, lt.y, lt.z, lt.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (u > tt[r]) p[q4 * 4 + r] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+        op[hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+        *reinterpret_cast<u32x4_t*>(px + 16 * hh) = u32x4_t{w[0], w[1], w[2], w[3]};
       }
     }
-    bf16x8_t pp[2], dsp[2];
+    __syncthreads();   // P of every tile is in LDS
+    if (role_ds) {
+      // dS = P (dP - D), P as rounded to bf16 by wave P
+      const u32x4_t pw0 = *reinterpret_cast<const u32x4_t*>(px);
+      const u32x4_t pw1 = *reinterpret_cast<const u32x4_t*>(px + 16);
+      const uint32_t pw[8] = {pw0[0], pw0[1], pw0[2], pw0[3], pw1[0], pw1[1], pw1[2], pw1[3]};
+      float x[16];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint32_t w1[4], w2[4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t ld = *reinterpret_cast<const f32x4_t*>(mf + 32 + q4 * 8 + hf * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w1[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
-        w2[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
+        for (int r = 0; r < 4; ++r) {
+          const int e = q4 * 4 + r;
+          const float pe = (e & 1) ? bf16hi(pw[e >> 1]) : bf16lo(pw[e >> 1]);
+          x[e] = pe * (sc[e] - ld[r]);
+        }
       }
-      pp[hh] = as_bf16x8(u32x4_t{w1[0], w1[1], w1[2], w1[3]});
-      dsp[hh] = as_bf16x8(u32x4_t{w2[0], w2[1], w2[2], w2[3]});
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
+        op[hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+      }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (summed over the group's 32 rows)
+    // dV^T += dO^T P (wave P) or dK^T += Q^T dS (wave dS), over the group's 32 rows
+    const char* tt = base + (role_ds ? 0 : L::QR + L::QT) + L::QR;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        av[dt] = mfma32x32x16(read_t_operand<D>(dtr, ks, dt), pp[ks], av[dt]);
-        ak[dt] = mfma32x32x16(read_t_operand<D>(qt, ks, dt), dsp[ks], ak[dt]);
-      }
-    if (gidx + 1 < ngroups) store_group((gidx + 1) & 1);
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = mfma32x32x16(read_t_operand<D>(tt, ks, dt), op[ks], acc[dt]);
+  };
+  const int ngroups = (nrows + 31) / 32;
+  Ids id;
+  Rows rd;
+  fetch_ids(0, id);
+  fetch_rows(id, rd);            // group 0
+  fetch_ids(32, id);             // group 1
+  store_rows(rd, 0);
+  __syncthreads();
+  using Mask = std::true_type;
+  using NoMask = std::false_type;
+  // groups [gm0, gm1) hold the rows that need the causal mask
+  const int gm0 = mask_lo / 32, gm1 = (mask_hi + 31) / 32;
+  for (int gidx = 0; gidx < ngroups; gidx += 2) {
+    fetch_rows(id, rd);          // group gidx + 1
+    fetch_ids((gidx + 2) * 32, id);
+    if (gidx >= gm0 && gidx < gm1) compute(0, Mask{});
+    else compute(0, NoMask{});
+    store_rows(rd, 1);
+    __syncthreads();
+    if (gidx + 1 >= ngroups) break;
+    fetch_rows(id, rd);          // group gidx + 2
+    fetch_ids((gidx + 3) * 32, id);
+    if (gidx + 1 >= gm0 && gidx + 1 < gm1) compute(1, Mask{});
+    else compute(1, NoMask{});
+    store_rows(rd, 0);
     __syncthreads();
   }
 
   if (!kvalid) return;
-  uint16_t* krow = dk + (((size_t)b * T + u) * hkv + g) * D + hf * 4;
-  uint16_t* vrow = dv + (((size_t)b * T + u) * hkv + g) * D + hf * 4;
+  const float os = role_ds ? scale : 1.f;
+  uint16_t* orow = (role_ds ? dk : dv) + (((size_t)b * T + u) * hkv + g) * D + hf * 4;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      u32x2_t a, c;
-      a[0] = f32_to_bf16_rne(ak[dt][ii * 4] * scale) |
-             (f32_to_bf16_rne(ak[dt][ii * 4 + 1] * scale) << 16);
-      a[1] = f32_to_bf16_rne(ak[dt][ii * 4 + 2] * scale) |
-             (f32_to_bf16_rne(ak[dt][ii * 4 + 3] * scale) << 16);
-      c[0] = f32_to_bf16_rne(av[dt][ii * 4]) | (f32_to_bf16_rne(av[dt][ii * 4 + 1]) << 16);
-      c[1] = f32_to_bf16_rne(av[dt][ii * 4 + 2]) | (f32_to_bf16_rne(av[dt][ii * 4 + 3]) << 16);
-      *reinterpret_cast<u32x2_t*>(krow + dt * 32 + ii * 8) = a;
-      *reinterpret_cast<u32x2_t*>(vrow + dt * 32 + ii * 8) = c;
+      u32x2_t w;
+      w[0] = f32_to_bf16_rne(acc[dt][ii * 4] * os) |
+             (f32_to_bf16_rne(acc[dt][ii * 4 + 1] * os) << 16);
+      w[1] = f32_to_bf16_rne(acc[dt][ii * 4 + 2] * os) |
+             (f32_to_bf16_rne(acc[dt][ii * 4 + 3] * os) << 16);
+      *reinterpret_cast<u32x2_t*>(orow + dt * 32 + ii * 8) = w;
     }
 }
 
@@ -572,7 +635,7 @@ hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
                            const int32_t* list_offsets, const uint32_t* entries, uint16_t* dk,
                            uint16_t* dv, hipStream_t st) {
   const float sl = scale * kLog2e;
-  const int kpw = 32 * kKvWaves;
+  const int kpw = 32 * kKvTiles;
   dim3 grid((s.block + kpw - 1) / kpw, s.nb(), s.b * ng);
 #define MOBA_KV(DD)                                                                        \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD>), grid, dim3(kKvThreads), 0, st, q, k, v, dout,    \
