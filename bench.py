@@ -133,6 +133,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip timing dense causal attention on the same inputs")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward pass (dQ, dK, dV) on the same inputs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one elementwise copy (torch.neg) of this many MiB "
                          "of bf16, a kernel of known traffic for scaling HBM counters")
@@ -287,6 +289,47 @@ def main(argv=None):
         }
         print(f"[bench] dense causal {dms:.2f} ms", file=sys.stderr, flush=True)
         del out_d, lse_d
+    if not a.no_backward:
+        # the training backward of the same layer (selection held fixed): context for
+        # the forward metric.  FLOP conventions: "effective" counts the five products of
+        # an attention backward (10 d per attended pair, 2.5x the forward's 4 d);
+        # "executed" counts what the kernels run (14 d: S and dP are computed in both
+        # the dQ and the dK/dV kernel).
+        from workloads import make_output_grad
+        dout = to_torch_bf16(make_output_grad(w), dev)
+        full_b, min_b = moba.backward_workspace_bytes(w.batch, w.seqlen, w.hq, w.hkv,
+                                                      w.head_dim, w.block, w.topk)
+        bws = torch.empty(full_b, dtype=torch.uint8, device=dev)
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+
+        def bstep():
+            moba.backward(q, k, v, out, lse, idx, dout, w.block, w.topk, w.sm_scale,
+                          workspace=bws, dq=dq, dk=dk, dv=dv)
+
+        bstep()
+        torch.cuda.synchronize()
+        n_bwd = 3
+        e0.record(stream)
+        for _ in range(n_bwd):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / n_bwd
+        pairs = heads * (hist + cur)
+        result["backward"] = {
+            "ms": bms,
+            "effective_tflops": 10 * w.head_dim * pairs / (bms * 1e-3) / 1e12,
+            "effective_frac_of_bf16_peak": (10 * w.head_dim * pairs / (bms * 1e-3) / 1e12
+                                            / PEAK_BF16_TFLOPS),
+            "executed_tflops": 14 * w.head_dim * pairs / (bms * 1e-3) / 1e12,
+            "forward_plus_backward_ms": ms + bms,
+            "workspace_bytes": full_b,
+            "note": "moba_backward (dq, dk, dv) on the same inputs, dout i.i.d. N(0,1)",
+        }
+        print(f"[bench] backward {bms:.2f} ms", file=sys.stderr, flush=True)
+        del bws, dq, dk, dv, dout
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_seconds:.0f} s)", file=sys.stderr,
               flush=True)
