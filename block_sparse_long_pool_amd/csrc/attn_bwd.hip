@@ -462,7 +462,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   // rows nhist + (0 .. 32*kKvTiles*G - 1) are the tokens kc0 .. kc0 + 32*kKvTiles - 1,
   // the only ones that see keys after themselves; other groups need no causal mask
   const int mask_lo = nhist, mask_hi = nhist + 32 * kKvTiles * G;
-  char* px = lds + 2 * L::BUF + (tile * 64 + lane) * 32;   // this lane's P slot
+  // this lane's P slot: two 16-byte planes 1 KB apart, so that the 64 lanes of a
+  // 16-byte access touch consecutive bytes
+  char* px = lds + 2 * L::BUF + tile * 2048 + lane * 16;
   // One 32-row group.  Register e of a 32x32 result holds row (e/4)*8 + hf*4 + e%4.
   auto compute = [&](int buf, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -501,14 +503,14 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
         op[hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
-        *reinterpret_cast<u32x4_t*>(px + 16 * hh) = u32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4_t*>(px + 1024 * hh) = u32x4_t{w[0], w[1], w[2], w[3]};
       }
     }
     __syncthreads();   // P of every tile is in LDS
     if (role_ds) {
       // dS = P (dP - D), P as rounded to bf16 by wave P
       const u32x4_t pw0 = *reinterpret_cast<const u32x4_t*>(px);
-      const u32x4_t pw1 = *reinterpret_cast<const u32x4_t*>(px + 16);
+      const u32x4_t pw1 = *reinterpret_cast<const u32x4_t*>(px + 1024);
       const uint32_t pw[8] = {pw0[0], pw0[1], pw0[2], pw0[3], pw1[0], pw1[1], pw1[2], pw1[3]};
       float x[16];
 #pragma unroll
