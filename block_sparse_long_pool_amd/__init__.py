@@ -21,7 +21,7 @@ __all__ = [
     "LIB_PATH", "MobaError", "check_args", "workspace_bytes", "forward",
     "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
-    "backward", "backward_workspace_bytes",
+    "backward", "backward_workspace_bytes", "forward_varlen", "varlen_workspace_bytes",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -49,6 +49,10 @@ _SIGS = {
                                 _vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "moba_dense_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "moba_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "moba_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i,
+                                          ctypes.POINTER(_sz)]),
+    "moba_forward_varlen": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
+                                 _vp, _vp, _vp, _sz, _vp]),
     "moba_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                            _vp, _vp, _vp, _vp, _sz, _vp]),
     "moba_strerror": (ctypes.c_char_p, [_i]),
@@ -239,6 +243,72 @@ def dense_forward(q, k, v, scale: float | None = None, out=None, lse=None):
                                     _stream_ptr())
     _raise(st, "moba_dense_forward")
     return out, lse
+
+
+def varlen_workspace_bytes(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk):
+    """(all-kv-heads size, one-kv-head size) of the packed-sequence workspace; (0, 0)
+    when unsupported."""
+    mn = _sz(0)
+    full = lib.moba_varlen_workspace_bytes(nseq, total, max_seqlen, hq, hkv, head_dim, block,
+                                           topk, ctypes.byref(mn))
+    return int(full), int(mn.value)
+
+
+def forward_varlen(q, k, v, cu_seqlens, block: int, topk: int, scale: float | None = None,
+                   workspace=None, max_workspace_bytes: int | None = None, out=None,
+                   lse=None, idx=None):
+    """MoBA prefill over packed sequences of different lengths, each with its own block
+    grid.  q [total, Hq, d], k and v [total, Hkv, d] bf16 on the GPU; cu_seqlens: the
+    cumulative lengths [nseq + 1] (int, any device), checked here on the host.
+    Returns (out [total, Hq, d] bf16, lse [Hq, total] fp32, idx [Hq, total, topk] int32,
+    block ids counted within each sequence)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape[0] != total or k.shape[2] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    cu_host = torch.as_tensor(cu_seqlens).to("cpu", torch.int64)
+    if cu_host.dim() != 1 or cu_host.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+    lens = cu_host[1:] - cu_host[:-1]
+    if int(cu_host[0]) != 0 or int(cu_host[-1]) != total or bool((lens < 0).any()):
+        raise ValueError("cu_seqlens must start at 0, not decrease and end at q.shape[0]")
+    nseq = cu_host.numel() - 1
+    max_seqlen = max(1, int(lens.max()))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        full, mn = varlen_workspace_bytes(nseq, total, max_seqlen, hq, hkv, d, block, topk)
+        if full == 0:
+            _raise(MOBA_ERR_UNSUPPORTED, "moba_varlen_workspace_bytes")
+        if max_workspace_bytes is None:
+            free, _ = torch.cuda.mem_get_info(q.device)
+            max_workspace_bytes = int(0.6 * free)
+        workspace = _alloc_workspace(full if full <= max_workspace_bytes
+                                     else max(mn, max_workspace_bytes), q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    cu_dev = cu_host.to(device=q.device, dtype=torch.int32)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq, total), dtype=torch.float32, device=q.device) if lse is None else lse
+    if idx is None:
+        idx = torch.empty((hq, total, topk), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    _need(idx, "idx", torch.int32, 3)
+    if out.shape != q.shape or lse.shape != (hq, total) or idx.shape != (hq, total, topk):
+        raise ValueError("output shapes do not match the inputs")
+    with torch.cuda.device(q.device):
+        st = lib.moba_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     cu_dev.data_ptr(), nseq, total, max_seqlen, hq, hkv, d,
+                                     block, topk, float(scale), out.data_ptr(),
+                                     lse.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel(), _stream_ptr())
+    _raise(st, "moba_forward_varlen")
+    return out, lse, idx
 
 
 def backward_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk):

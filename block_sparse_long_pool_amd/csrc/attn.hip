@@ -606,7 +606,7 @@ __device__ __forceinline__ void load_q(WaveState<D, QT>& st, int qt, const uint1
 template <int D, int QT>
 __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
+    const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
@@ -616,6 +616,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
   const int4 tl = tiles[tile_id];
   const int list = tl.x;
   const int j = list % nb, gi = (list / nb) % ng, b = list / (nb * ng);
+  const int tok0 = sq.tok0(b);
   const int G = hq / hkv, g = g0 + gi;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
 
@@ -632,13 +633,13 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
     tq[qt] = rr / G;
     hlq[qt] = rr % G;
     tpos[qt] = 0x7fffffff;    // history keys all precede the query
-    const uint16_t* qrow = q + ((size_t)((size_t)b * T + tq[qt]) * hq + g * G + hlq[qt]) * D;
+    const uint16_t* qrow = q + ((size_t)((size_t)tok0 + tq[qt]) * hq + g * G + hlq[qt]) * D;
     load_q(st, qt, qrow, vq[qt]);
   }
   state_init(st);
   const size_t rs = (size_t)hkv * D;
-  const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
+  const uint16_t* kbase = k + ((size_t)tok0 * hkv + g) * D;
+  const uint16_t* vbase = v + ((size_t)tok0 * hkv + g) * D;
   const int key_begin = j * block;
   attend_range<D, QT>(st, lds, kbase, vbase, rs, key_begin, key_begin + block, sl,
                       0x7fffffff, tpos);
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const size_t prow =
-        ((size_t)(b * ngq + gi * G + hlq[qt]) * T + tq[qt]) * (topk - 1) + slq[qt];
+        (sq.prow(b, gi * G + hlq[qt], ngq) + tq[qt]) * (topk - 1) + slq[qt];
     store_partial(st, qt, vq[qt], part_o + prow * D, part_lse + prow);
   }
 }
@@ -664,7 +665,7 @@ __host__ __device__ __forceinline__ int current_subtiles(int G) {
 template <int D, int QT>
 __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int T, int hq, int hkv, int block, int topk,
+    const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
@@ -675,14 +676,17 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
   const int TT = 32 * QT * TS;
   const int x = gridDim.x - 1 - blockIdx.x;
   const int t0 = c * block + x * TT;
-  const int t_end = min(t0 + TT, (c + 1) * block);
+  const int Tb = sq.len(b), tok0 = sq.tok0(b);
+  // a partial last block, or a block past the end of a shorter packed sequence
+  const int t_end = min(min(t0 + TT, (c + 1) * block), Tb);
+  if (t0 >= t_end) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
   const int hw = TS > 1 ? wave % G : wave;      // head of this wave within a round
   const int tsub = TS > 1 ? wave / G : 0;
   const int hstep = TS > 1 ? G : kAttnWaves;     // heads covered per round
   const size_t rs = (size_t)hkv * D;
-  const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
+  const uint16_t* kbase = k + ((size_t)tok0 * hkv + g) * D;
+  const uint16_t* vbase = v + ((size_t)tok0 * hkv + g) * D;
   const int ngq = ng * G;
   for (int round = 0; round * hstep < G; ++round) {
     const int hl = round * hstep + hw;
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
     for (int qt = 0; qt < QT; ++qt) {
       tpos[qt] = t0 + (tsub * QT + qt) * 32 + n;
       vq[qt] = active && tpos[qt] < t_end;
-      const uint16_t* qrow = q + ((size_t)((size_t)b * T + (vq[qt] ? tpos[qt] : 0)) * hq +
+      const uint16_t* qrow = q + ((size_t)((size_t)tok0 + (vq[qt] ? tpos[qt] : 0)) * hq +
                                   g * G + (active ? hl : 0)) * D;
       load_q(st, qt, qrow, vq[qt]);
     }
@@ -707,10 +711,10 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const int t = vq[qt] ? tpos[qt] : 0;
-        const size_t prow = ((size_t)(b * ngq + gi * G + hl) * T + t) * (topk - 1);
+        const size_t prow = (sq.prow(b, gi * G + hl, ngq) + t) * (topk - 1);
         merge_store(st, qt, vq[qt], nh, part_o + prow * D, part_lse + prow,
-                    out + ((size_t)((size_t)b * T + t) * hq + g * G + hl) * D,
-                    lse + ((size_t)b * hq + g * G + hl) * T + t);
+                    out + ((size_t)((size_t)tok0 + t) * hq + g * G + hl) * D,
+                    lse + sq.lrow(b, g * G + hl, hq) + t);
       }
     }
   }
@@ -729,12 +733,12 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
   const float sl = scale * 1.4426950408889634f;
   if (s.d == 128)
     hipLaunchKernelGGL((attn_history_kernel<128, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
-                       st, q, k, v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, s.nb(),
-                       tiles, tile_count, entries, part_o, part_lse);
+                       st, q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng,
+                       s.nb(), tiles, tile_count, entries, part_o, part_lse);
   else
     hipLaunchKernelGGL((attn_history_kernel<64, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
-                       st, q, k, v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, s.nb(),
-                       tiles, tile_count, entries, part_o, part_lse);
+                       st, q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng,
+                       s.nb(), tiles, tile_count, entries, part_o, part_lse);
   return hipGetLastError();
 }
 
@@ -747,12 +751,12 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
   dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng);
   if (s.d == 128)
     hipLaunchKernelGGL((attn_current_kernel<128, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
-                       v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse,
-                       out, lse);
+                       v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o,
+                       part_lse, out, lse);
   else
     hipLaunchKernelGGL((attn_current_kernel<64, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
-                       v, s.T, s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o, part_lse,
-                       out, lse);
+                       v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o,
+                       part_lse, out, lse);
   return hipGetLastError();
 }
 

@@ -100,16 +100,16 @@ __device__ __forceinline__ void bitonic_sort_asc(int (&a)[N]) {
 
 }  // namespace
 
-// Query operands of one chunk (64 tokens t0 .. t0+63 of head h, batch b): tile qt,
-// k-step s holds dims 16*s + 8*hf .. +7 of token t0 + 32*qt + n.  Loads go through a
-// buffer descriptor of the chunk's rows (zero size when not needed), so rows past T
-// read as zeros.
+// Query operands of one chunk (64 tokens t0 .. t0+63 of head h of a sequence of T
+// tokens starting at packed token tok0): tile qt, k-step s holds dims 16*s + 8*hf ..
+// +7 of token t0 + 32*qt + n.  Loads go through a buffer descriptor of the chunk's rows
+// (zero size when not needed), so rows past T read as zeros.
 template <int D>
 __device__ __forceinline__ void gate_load_q(bf16x8_t (&bq)[2][D / 16],
                                             const uint16_t* __restrict__ q, int T, int hq,
-                                            int b, int h, int t0, bool needed) {
+                                            int tok0, int h, int t0, bool needed) {
   const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  const uint16_t* base = q + ((size_t)((size_t)b * T + t0) * hq + h) * D;
+  const uint16_t* base = q + ((size_t)((size_t)tok0 + t0) * hq + h) * D;
   const int rows = min(64, T - t0);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(base), (short)0,
@@ -126,17 +126,34 @@ __device__ __forceinline__ void gate_load_q(bf16x8_t (&bq)[2][D / 16],
 
 struct GateChunk {
   int b, h, t0;
+  int T, tok0;   // the sequence's length and first packed token
+  size_t lrow;   // idx row of (b, h, t = 0), in rows of topk
   bool compete;  // some row has more causal history blocks than slots
 };
 
-__device__ __forceinline__ GateChunk gate_chunk_of(int cid, int T, int hq, int block, int KH) {
-  const int nct = (T + 63) / 64;
+// chunk (b, h, t0) of a sequence; T is the longest sequence (the chunk grid)
+__device__ __forceinline__ GateChunk gate_chunk_make(const SeqMap& sq, int b, int h, int t0,
+                                                     int hq, int block, int KH) {
   GateChunk k;
-  k.t0 = (cid % nct) * 64;
-  k.h = (cid / nct) % hq;
-  k.b = cid / (nct * hq);
-  k.compete = min(k.t0 + 63, T - 1) / block > KH;
+  k.b = b;
+  k.h = h;
+  k.t0 = t0;
+  k.T = sq.len(b);
+  k.tok0 = sq.tok0(b);
+  k.lrow = sq.lrow(b, h, hq);
+  k.compete = min(k.t0 + 63, k.T - 1) / block > KH;
   return k;
+}
+
+// rows of a chunk whose every causal block is selected: 0..c, then -1
+__device__ __forceinline__ void gate_all_blocks(const GateChunk& k, int block, int topk,
+                                                int32_t* __restrict__ idx) {
+  const int t = k.t0 + (threadIdx.x & 63);
+  if (t < k.T) {
+    const int c = t / block;
+    int32_t* row = idx + (k.lrow + t) * topk;
+    for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
+  }
 }
 
 // LDS image of one kv-head's centroids: the bf16 hi rows then the lo rows, each row
@@ -155,17 +172,17 @@ template <int D, int KHMAX, bool CLDS>
 __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], const GateChunk& k,
                                            const uint16_t* __restrict__ chi,
                                            const uint16_t* __restrict__ clo,
-                                           const char* __restrict__ lds, int T, int hq,
+                                           const char* __restrict__ lds, int hq,
                                            int hkv, int block, int nb, int topk, int nbits,
                                            int32_t* __restrict__ idx) {
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
   const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
   const int G = hq / hkv, g = k.h / G;
   const int t = k.t0 + lane;  // the row this lane ranks and writes
-  const bool valid = t < T;
+  const bool valid = t < k.T;
   const int c = valid ? t / block : 0;
   const int KH = topk - 1;
-  int32_t* row = idx + ((size_t)(k.b * hq + k.h) * T + (valid ? t : 0)) * topk;
+  int32_t* row = idx + (k.lrow + (valid ? t : 0)) * topk;
 
   const uint32_t mask = (1u << nbits) - 1u;
   uint32_t L[KHMAX];
@@ -292,25 +309,22 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
 template <int D, int KHMAX>
 __global__ __launch_bounds__(kThreads, 3) void gate_topk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
-    const uint16_t* __restrict__ clo, int batch, int T, int hq, int hkv, int block, int nb,
-    int topk, int nbits, int32_t* __restrict__ idx) {
-  const int nchunks = batch * hq * ((T + 63) / 64);
+    const uint16_t* __restrict__ clo, int batch, SeqMap sq, int hq, int hkv, int block,
+    int nb, int topk, int nbits, int32_t* __restrict__ idx) {
+  const int nct = (sq.T + 63) / 64;
+  const int nchunks = batch * hq * nct;
   const int cid = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (cid >= nchunks) return;
-  const GateChunk k = gate_chunk_of(cid, T, hq, block, topk - 1);
+  const GateChunk k = gate_chunk_make(sq, cid / (nct * hq), (cid / nct) % hq,
+                                      (cid % nct) * 64, hq, block, topk - 1);
+  if (k.t0 >= k.T) return;   // past the end of a shorter packed sequence
   if (!k.compete) {
-    // every causal block is selected: 0..c, then -1
-    const int t = k.t0 + (threadIdx.x & 63);
-    if (t < T) {
-      const int c = t / block;
-      int32_t* row = idx + ((size_t)(k.b * hq + k.h) * T + t) * topk;
-      for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
-    }
+    gate_all_blocks(k, block, topk, idx);
     return;
   }
   bf16x8_t bq[2][D / 16];
-  gate_load_q<D>(bq, q, T, hq, k.b, k.h, k.t0, true);
-  gate_chunk<D, KHMAX, false>(bq, k, chi, clo, nullptr, T, hq, hkv, block, nb, topk, nbits,
+  gate_load_q<D>(bq, q, k.T, hq, k.tok0, k.h, k.t0, true);
+  gate_chunk<D, KHMAX, false>(bq, k, chi, clo, nullptr, hq, hkv, block, nb, topk, nbits,
                               idx);
 }
 
@@ -320,11 +334,11 @@ __global__ __launch_bounds__(kThreads, 3) void gate_topk_kernel(
 template <int D, int KHMAX>
 __global__ __launch_bounds__(kThreads, 3) void gate_topk_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
-    const uint16_t* __restrict__ clo, int batch, int T, int hq, int hkv, int block, int nb,
-    int topk, int nbits, int32_t* __restrict__ idx) {
+    const uint16_t* __restrict__ clo, int batch, SeqMap sq, int hq, int hkv, int block,
+    int nb, int topk, int nbits, int32_t* __restrict__ idx) {
   using CL = CentLds<D>;
   __shared__ __attribute__((aligned(16))) char lds[CL::BYTES];
-  const int G = hq / hkv, nct = (T + 63) / 64;
+  const int G = hq / hkv, nct = (sq.T + 63) / 64;
   const int b = blockIdx.y / hkv, g = blockIdx.y % hkv;
   const int ci = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // chunk in group
   const size_t cbase = (size_t)(b * hkv + g) * nb;
@@ -337,23 +351,16 @@ __global__ __launch_bounds__(kThreads, 3) void gate_topk_lds_kernel(
   }
   __syncthreads();
   if (ci >= G * nct) return;
-  GateChunk k;
-  k.b = b;
-  k.h = g * G + ci / nct;
-  k.t0 = (ci % nct) * 64;
-  k.compete = min(k.t0 + 63, T - 1) / block > topk - 1;
+  const GateChunk k = gate_chunk_make(sq, b, g * G + ci / nct, (ci % nct) * 64, hq, block,
+                                      topk - 1);
+  if (k.t0 >= k.T) return;   // past the end of a shorter packed sequence
   if (!k.compete) {
-    const int t = k.t0 + (threadIdx.x & 63);
-    if (t < T) {
-      const int c = t / block;
-      int32_t* row = idx + ((size_t)(k.b * hq + k.h) * T + t) * topk;
-      for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
-    }
+    gate_all_blocks(k, block, topk, idx);
     return;
   }
   bf16x8_t bq[2][D / 16];
-  gate_load_q<D>(bq, q, T, hq, k.b, k.h, k.t0, true);
-  gate_chunk<D, KHMAX, true>(bq, k, chi, clo, lds, T, hq, hkv, block, nb, topk, nbits, idx);
+  gate_load_q<D>(bq, q, k.T, hq, k.tok0, k.h, k.t0, true);
+  gate_chunk<D, KHMAX, true>(bq, k, chi, clo, lds, hq, hkv, block, nb, topk, nbits, idx);
 }
 
 hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
@@ -373,11 +380,12 @@ hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
   do {                                                                                   \
     if (clds)                                                                            \
       hipLaunchKernelGGL((gate_topk_lds_kernel<DD, KK>), grid_lds, dim3(kThreads), 0, st, \
-                         q, chi, clo, s.b, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits,  \
-                         idx);                                                           \
+                         q, chi, clo, s.b, s.seqs(), s.hq, s.hkv, s.block, nb, s.topk,    \
+                         nbits, idx);                                                    \
     else                                                                                 \
       hipLaunchKernelGGL((gate_topk_kernel<DD, KK>), grid, dim3(kThreads), 0, st, q, chi, \
-                         clo, s.b, s.T, s.hq, s.hkv, s.block, nb, s.topk, nbits, idx);    \
+                         clo, s.b, s.seqs(), s.hq, s.hkv, s.block, nb, s.topk, nbits,     \
+                         idx);                                                           \
   } while (0)
   if (s.d == 128) {
     if (KH <= 16) MOBA_GATE(128, 16);

@@ -24,7 +24,7 @@ int index_chunks(const Shape& s) {
 }
 
 __global__ __launch_bounds__(kThreads) void index_count_kernel(
-    const int32_t* __restrict__ idx, int T, int hq, int G, int block, int topk, int nb,
+    const int32_t* __restrict__ idx, SeqMap sq, int hq, int G, int block, int topk, int nb,
     int g0, int ng, int nchunks, int32_t* __restrict__ chunk_counts) {
   extern __shared__ int32_t cnt[];
   const int chunk = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
@@ -33,10 +33,10 @@ __global__ __launch_bounds__(kThreads) void index_count_kernel(
   __syncthreads();
   const long r = (long)chunk * kChunk + tid;
   const int t = (int)(r / G), hl = (int)(r % G);
-  if (t < T) {
+  if (t < sq.len(b)) {
     const int c = t / block;
     const int h = (g0 + gi) * G + hl;
-    const int32_t* row = idx + ((size_t)(b * hq + h) * T + t) * topk;
+    const int32_t* row = idx + (sq.lrow(b, h, hq) + t) * topk;
     for (int s = 0; s < topk - 1; ++s) {
       const int j = row[s];
       if (j >= 0 && j < c) atomicAdd(&cnt[j], 1);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64) void index_tiles_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
-    const int32_t* __restrict__ idx, int T, int hq, int G, int block, int topk, int nb,
+    const int32_t* __restrict__ idx, SeqMap sq, int hq, int G, int block, int topk, int nb,
     int nbits, int g0, int ng, int nchunks, const int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ list_offsets, uint32_t* __restrict__ entries,
     long long cap) {
@@ -153,9 +153,9 @@ __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
   __syncthreads();
   const long r = (long)chunk * kChunk + tid;
   const int t = (int)(r / G), hl = (int)(r % G);
-  const bool valid = t < T;
+  const bool valid = t < sq.len(b);
   const int c = valid ? t / block : 0;
-  const int32_t* row = idx + ((size_t)(b * hq + (g0 + gi) * G + hl) * T + (valid ? t : 0)) * topk;
+  const int32_t* row = idx + (sq.lrow(b, (g0 + gi) * G + hl, hq) + (valid ? t : 0)) * topk;
   const uint64_t below = (1ull << lane) - 1ull;
   for (int s = 0; s < topk - 1; ++s) {
     int j = valid ? row[s] : -1;
@@ -199,7 +199,7 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
   const int nlists = s.b * ng * nb;
   dim3 grid(nchunks, ng, s.b);
   hipLaunchKernelGGL(index_count_kernel, grid, dim3(kThreads), nb * sizeof(int32_t), st,
-                     idx, s.T, s.hq, s.G(), s.block, s.topk, nb, g0, ng, nchunks,
+                     idx, s.seqs(), s.hq, s.G(), s.block, s.topk, nb, g0, ng, nchunks,
                      chunk_counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -215,7 +215,7 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(index_scatter_kernel, grid, dim3(kThreads), 6 * nb * sizeof(int32_t),
-                     st, idx, s.T, s.hq, s.G(), s.block, s.topk, nb, nbits, g0, ng,
+                     st, idx, s.seqs(), s.hq, s.G(), s.block, s.topk, nb, nbits, g0, ng,
                      nchunks, chunk_counts, list_offsets, entries, cap);
   return hipGetLastError();
 }

@@ -25,20 +25,36 @@ int check(int batch, int seqlen, int hq, int hkv, int head_dim, int block, int t
   if (scale <= 0.f) return MOBA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return MOBA_ERR_UNSUPPORTED;
   if (block < 16 || block % 16 != 0) return MOBA_ERR_UNSUPPORTED;
-  if (seqlen % block != 0) return MOBA_ERR_UNSUPPORTED;
   if (topk > 33) return MOBA_ERR_UNSUPPORTED;
-  if (seqlen / block > kMaxBlocks) return MOBA_ERR_UNSUPPORTED;
+  if ((seqlen + block - 1) / block > kMaxBlocks) return MOBA_ERR_UNSUPPORTED;
   const long long G = hq / hkv;
   if ((long long)seqlen * G >= (1ll << 27)) return MOBA_ERR_UNSUPPORTED;
   if ((long long)batch * seqlen * hq >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
   return MOBA_OK;
 }
 
-// rows of one query head that carry history slot entries, times slots
+// rows of one query head of one sequence that carry history slot entries, times slots
+// (a partial last block has fewer rows)
 long long entries_per_head(const Shape& s) {
   long long per = 0;
-  for (int c = 0; c < s.nb(); ++c) per += (long long)s.block * (c < s.KH() ? c : s.KH());
+  for (int c = 0; c < s.nb(); ++c) {
+    const int rows = s.T - c * s.block < s.block ? s.T - c * s.block : s.block;
+    per += (long long)rows * (c < s.KH() ? c : s.KH());
+  }
   return per;
+}
+
+// entries of a group of ng kv-heads: exact for a uniform batch; for packed sequences a
+// bound (every token with every slot), since the lengths live on the device
+long long group_entries(const Shape& s, int ng) {
+  if (s.cu) return (long long)ng * s.G() * s.total * s.KH();
+  return (long long)s.b * ng * s.G() * entries_per_head(s);
+}
+
+// rows of the history partials of a group of ng kv-heads
+size_t group_part_rows(const Shape& s, int ng) {
+  const size_t tokens = s.cu ? (size_t)s.total : (size_t)s.b * s.T;
+  return tokens * ng * s.G() * s.KH();
 }
 
 struct Layout {
@@ -69,7 +85,7 @@ Layout make_layout(const Shape& s, int ng) {
   L.clo = take(ncent * sizeof(uint16_t));
   const size_t nlists = (size_t)s.b * ng * nb;
   const size_t nchunks = moba::index_chunks(s);
-  L.n_entries = (long long)s.b * ng * s.G() * entries_per_head(s);
+  L.n_entries = group_entries(s, ng);
   const int tm = moba::history_tile_rows();
   L.max_tiles = (L.n_entries + tm - 1) / tm + (long long)nlists;
   L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
@@ -78,7 +94,7 @@ Layout make_layout(const Shape& s, int ng) {
   L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
-  const size_t prow = (size_t)s.b * ng * s.G() * s.T * s.KH();   // history slots only
+  const size_t prow = group_part_rows(s, ng);   // history slots only
   L.part_o = take(prow * s.d * sizeof(uint16_t));   // bf16 partial outputs
   L.part_lse = take(prow * sizeof(float));
   L.total = off;
@@ -111,7 +127,7 @@ BwdLayout make_bwd_layout(const Shape& s, int ng) {
   L.delta = take((size_t)s.b * s.hq * s.T * sizeof(float));
   const size_t nlists = (size_t)s.b * ng * nb;
   const size_t nchunks = moba::index_chunks(s);
-  L.n_entries = (long long)s.b * ng * s.G() * entries_per_head(s);
+  L.n_entries = group_entries(s, ng);
   const int tm = moba::bwd_tile_rows();
   L.max_tiles = (L.n_entries + tm - 1) / tm + (long long)nlists;
   L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
@@ -221,16 +237,14 @@ struct StageClock {
   }
 };
 
-int forward_impl(const void* q, const void* k, const void* v, int batch, int seqlen,
-                 int hq, int hkv, int head_dim, int block, int topk, float scale,
-                 void* out, float* lse, int32_t* idx, void* workspace,
-                 size_t workspace_bytes, void* stream, float* stage_ms,
-                 void* const* stage_events) {
-  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
-  if (st != MOBA_OK) return st;
+// the whole forward for a validated shape (a uniform batch or packed sequences)
+int run_forward(const Shape& s, const void* q, const void* k, const void* v, float scale,
+                void* out, float* lse, int32_t* idx, void* workspace,
+                size_t workspace_bytes, void* stream, float* stage_ms,
+                void* const* stage_events) {
   if (!q || !k || !v || !out || !lse || !idx || !workspace) return MOBA_ERR_INVALID_ARG;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
-  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  const int hkv = s.hkv;
   // the largest group of kv-heads whose buffers fit
   int ng = hkv;
   Layout L = make_layout(s, ng);
@@ -283,6 +297,33 @@ int forward_impl(const void* q, const void* k, const void* v, int batch, int seq
   return clock.finish(stage_ms);
 }
 
+int forward_impl(const void* q, const void* k, const void* v, int batch, int seqlen,
+                 int hq, int hkv, int head_dim, int block, int topk, float scale,
+                 void* out, float* lse, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, void* stream, float* stage_ms,
+                 void* const* stage_events) {
+  const int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  return run_forward(s, q, k, v, scale, out, lse, idx, workspace, workspace_bytes, stream,
+                     stage_ms, stage_events);
+}
+
+// packed sequences: the shape checks of a batch of nseq sequences of max_seqlen tokens,
+// plus the packed token count
+int varlen_shape(int nseq, int total, int max_seqlen, int hq, int hkv, int head_dim,
+                 int block, int topk, float scale, const int32_t* cu, Shape* out) {
+  const int st = check(nseq, max_seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  if (total <= 0 || max_seqlen > total) return MOBA_ERR_INVALID_ARG;
+  if ((long long)total * hq >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  Shape s{nseq, max_seqlen, hq, hkv, head_dim, block, topk};
+  s.cu = cu;
+  s.total = total;
+  *out = s;
+  return MOBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,6 +373,39 @@ int moba_forward_timed(const void* q, const void* k, const void* v, int batch, i
     if (!stage_events[i]) return MOBA_ERR_INVALID_ARG;
   return forward_impl(q, k, v, batch, seqlen, hq, hkv, head_dim, block, topk, scale, out,
                       lse, idx, workspace, workspace_bytes, stream, nullptr, stage_events);
+}
+
+// ------------------------------------------------------------------- packed sequences
+size_t moba_varlen_workspace_bytes(int nseq, int total, int max_seqlen, int hq, int hkv,
+                                   int head_dim, int block, int topk, size_t* min_bytes) {
+  if (min_bytes) *min_bytes = 0;
+  Shape s{};
+  static const int32_t kDummy = 0;   // only the null-ness of cu matters for sizing
+  if (varlen_shape(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk, 1.f, &kDummy,
+                   &s) != MOBA_OK)
+    return 0;
+  const Layout one = make_layout(s, 1);
+  if (!layout_ok(one)) return 0;
+  if (min_bytes) *min_bytes = one.total;
+  for (int ng = hkv; ng >= 1; --ng) {
+    const Layout L = make_layout(s, ng);
+    if (layout_ok(L)) return L.total;
+  }
+  return one.total;
+}
+
+int moba_forward_varlen(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                        int hq, int hkv, int head_dim, int block, int topk, float scale,
+                        void* out, float* lse, int32_t* idx, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return MOBA_ERR_INVALID_ARG;
+  Shape s{};
+  const int st = varlen_shape(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk, scale,
+                              cu_seqlens, &s);
+  if (st != MOBA_OK) return st;
+  return run_forward(s, q, k, v, scale, out, lse, idx, workspace, workspace_bytes, stream,
+                     nullptr, nullptr);
 }
 
 // ------------------------------------------------------------------- stages
@@ -421,7 +495,7 @@ size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
   if (min_bytes) *min_bytes = 0;
   if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
   const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
-  if (!moba::bwd_supported(s)) return 0;
+  if (!moba::bwd_supported(s) || seqlen % block != 0) return 0;
   const BwdLayout one = make_bwd_layout(s, 1);
   if (!bwd_layout_ok(one)) return 0;
   if (min_bytes) *min_bytes = one.total;
@@ -443,7 +517,7 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
     return MOBA_ERR_INVALID_ARG;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
   const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
-  if (!moba::bwd_supported(s)) return MOBA_ERR_UNSUPPORTED;
+  if (!moba::bwd_supported(s) || seqlen % block != 0) return MOBA_ERR_UNSUPPORTED;
   int ng = hkv;
   BwdLayout L = make_bwd_layout(s, ng);
   while (ng > 1 && (L.total > workspace_bytes || !bwd_layout_ok(L)))

@@ -65,11 +65,35 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
 namespace moba {
 
+// Token layout.  cu == nullptr: b sequences of T tokens each, tensors [b, T, heads, d],
+// lse [b, hq, T], idx [b, hq, T, topk].  Otherwise b packed sequences: sequence i is
+// tokens cu[i] .. cu[i+1]-1 of [total, heads, d] tensors, T is at least every length,
+// lse is [hq, total] and idx [hq, total, topk].  Each sequence has its own block grid
+// starting at its first token; its last block may be partial.
+struct SeqMap {
+  const int32_t* cu;
+  int T, total;
+  __device__ __forceinline__ int tok0(int b) const { return cu ? cu[b] : b * T; }
+  __device__ __forceinline__ int len(int b) const { return cu ? cu[b + 1] - cu[b] : T; }
+  // element index of (b, h, t = 0) in lse; the token stride is 1
+  __device__ __forceinline__ size_t lrow(int b, int h, int hq) const {
+    return cu ? (size_t)h * total + cu[b] : ((size_t)b * hq + h) * T;
+  }
+  // row of (b, head hh of the ngq heads of a kv-head group, t = 0) in the history
+  // partials, [b, ngq, T] or packed [ngq, total]; the token stride is 1
+  __device__ __forceinline__ size_t prow(int b, int hh, int ngq) const {
+    return cu ? (size_t)hh * total + cu[b] : ((size_t)b * ngq + hh) * T;
+  }
+};
+
 struct Shape {
   int b, T, hq, hkv, d, block, topk;
-  int nb() const { return T / block; }
+  const int32_t* cu = nullptr;   // packed sequences (device), see SeqMap
+  int total = 0;
+  int nb() const { return (T + block - 1) / block; }
   int G() const { return hq / hkv; }
   int KH() const { return topk - 1; }
+  SeqMap seqs() const { return SeqMap{cu, T, total}; }
 };
 
 // (a1) centroid mean-pool

@@ -1,4 +1,5 @@
-// Centroid mean-pool: C[b][g][j][:] = mean of the keys of block j of kv-head g
+// Centroid mean-pool: C[b][g][j][:] = mean of the keys of block j of kv-head g of
+// sequence b
 // ("MoBA: Mixture of Block Attention for Long-Context LLMs", paper summary page,
 // section "Approach": a block is represented by its mean-pooled key).
 //
@@ -12,9 +13,10 @@
 namespace moba {
 
 __global__ __launch_bounds__(kThreads) void pool_partial_kernel(
-    const uint16_t* __restrict__ k, int T, int cols, int block, int rows_per_split,
+    const uint16_t* __restrict__ k, SeqMap sq, int cols, int block, int rows_per_split,
     float* __restrict__ partial) {
   const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int T = sq.len(b), tok0 = sq.tok0(b);
   const int splits = gridDim.x, nb = gridDim.y;
   const int W = cols / 8;                    // 16-byte column chunks per row
   const int R = W >= kThreads ? 1 : kThreads / W;
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void pool_partial_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (rsub < R) {
-      const uint16_t* p = k + ((size_t)b * T + row0 + rsub) * cols + cc * 8;
+      const uint16_t* p = k + ((size_t)tok0 + row0 + rsub) * cols + cc * 8;
       const size_t stride = (size_t)R * cols;
       for (int row = row0 + rsub; row < row1; row += R, p += stride) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
@@ -61,9 +63,10 @@ __global__ __launch_bounds__(kThreads) void pool_partial_kernel(
   }
 }
 
-// sum the split partials in order, divide by the block's token count
+// sum the split partials in order, divide by the block's token count (a block past
+// the end of a shorter packed sequence gets 0; no query ever scores it)
 __global__ __launch_bounds__(kThreads) void pool_finalize_kernel(
-    const float* __restrict__ partial, int b_, int T, int hkv, int d, int block, int nb,
+    const float* __restrict__ partial, int b_, SeqMap sq, int hkv, int d, int block, int nb,
     int splits, float* __restrict__ cent) {
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const size_t total = (size_t)b_ * hkv * nb * d;
@@ -76,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void pool_finalize_kernel(
   const float* p = partial + ((size_t)(b * nb + j) * splits) * cols + g * d + dim;
   float sum = 0.f;
   for (int s = 0; s < splits; ++s) sum += p[(size_t)s * cols];
-  const int n = min(block, T - j * block);
-  cent[i] = sum / (float)n;  // layout [b][hkv][nb][d] == i
+  const int n = min(block, sq.len(b) - j * block);
+  cent[i] = n > 0 ? sum / (float)n : 0.f;  // layout [b][hkv][nb][d] == i
 }
 
 __global__ __launch_bounds__(kThreads) void centroid_split_kernel(
@@ -106,13 +109,13 @@ hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float*
   const int rows_per_split = (s.block + splits - 1) / splits;
   const int cols = s.hkv * s.d;
   dim3 grid(splits, nb, s.b);
-  hipLaunchKernelGGL(pool_partial_kernel, grid, dim3(kThreads), 0, st, k, s.T, cols,
+  hipLaunchKernelGGL(pool_partial_kernel, grid, dim3(kThreads), 0, st, k, s.seqs(), cols,
                      s.block, rows_per_split, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t total = (size_t)s.b * s.hkv * nb * s.d;
   hipLaunchKernelGGL(pool_finalize_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, partial, s.b, s.T, s.hkv, s.d, s.block, nb,
+                     dim3(kThreads), 0, st, partial, s.b, s.seqs(), s.hkv, s.d, s.block, nb,
                      splits, cent);
   return hipGetLastError();
 }

@@ -33,9 +33,12 @@
  *   centroids    [b, hkv, nb, d] float32
  *
  * Supported shapes: head_dim 64 or 128; hq % hkv == 0; block >= 16 and a multiple of
- * 16; seqlen a multiple of block; 1 <= topk <= 33 (topk counts the current block);
- * scale finite and > 0; seqlen * G < 2^27.  Anything else returns
- * MOBA_ERR_UNSUPPORTED or MOBA_ERR_INVALID_ARG before any device work.
+ * 16; 1 <= topk <= 33 (topk counts the current block); scale finite and > 0;
+ * seqlen * G < 2^27; at most 2048 blocks.  seqlen need not be a multiple of block: the
+ * last block is then partial.  It is only ever a current block (no later token routes
+ * to it), so routing is unchanged; its centroid is the mean of the keys present.
+ * Anything else returns MOBA_ERR_UNSUPPORTED or MOBA_ERR_INVALID_ARG before any device
+ * work.
  *
  * Errors: every check runs on the host before the first launch, so a call that
  * returns an error has written nothing.  MOBA_ERR_HIP means a launch failed; the
@@ -150,8 +153,8 @@ size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
  *   dk, dv                   [b, T, hkv, d] bf16, written (every element)
  * Accumulation is float32; dq sums fp32 per-history-block parts in slot order and dk,
  * dv are each summed by one workgroup in a fixed row order: deterministic.  Shape
- * limits are moba_forward's plus G = hq / hkv in {1, 2, 4, 8} (MOBA_ERR_UNSUPPORTED
- * otherwise).  `workspace` must hold at least the minimum of
+ * limits are moba_forward's plus G = hq / hkv in {1, 2, 4, 8} and seqlen a multiple of
+ * block (MOBA_ERR_UNSUPPORTED otherwise).  `workspace` must hold at least the minimum of
  * moba_backward_workspace_bytes and be 256-byte aligned (MOBA_ERR_WORKSPACE,
  * MOBA_ERR_INVALID_ARG).  Enqueued on `stream` without synchronising. */
 int moba_backward(const void* q, const void* k, const void* v, const void* out,
@@ -159,6 +162,34 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
                   int seqlen, int hq, int hkv, int head_dim, int block, int topk,
                   float scale, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Packed variable-length prefill: several sequences of different lengths in one call,
+ * each with its own block grid (block j of sequence i is its tokens jB .. jB+B-1,
+ * the last one possibly partial), routed and attended only within the sequence, as if
+ * each were a batch-1 moba_forward (paper summary page, "Approach", applied per
+ * sequence).
+ *   cu_seqlens  DEVICE int32 [nseq + 1]: cu_seqlens[0] = 0, non-decreasing,
+ *               cu_seqlens[nseq] = total, every length <= max_seqlen.  The library
+ *               cannot check device values: other contents are undefined behaviour.
+ *   q, out      [total, hq, d] bf16;  k, v  [total, hkv, d] bf16
+ *   lse         [hq, total] float32;  idx  [hq, total, topk] int32 (moba_forward's rows,
+ *               block ids counted within each sequence)
+ * Shape limits are moba_forward's with batch = nseq and seqlen = max_seqlen, plus
+ * total * hq < 2^31.  Returns as moba_forward.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace for moba_forward_varlen (all kv-heads at once; *min_bytes: one per pass).
+ * The index part is sized for every token using every history slot, since the lengths
+ * are only known on the device.  0 if unsupported. */
+size_t moba_varlen_workspace_bytes(int nseq, int total, int max_seqlen, int hq, int hkv,
+                                   int head_dim, int block, int topk, size_t* min_bytes);
+
+int moba_forward_varlen(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                        int hq, int hkv, int head_dim, int block, int topk, float scale,
+                        void* out, float* lse, int32_t* idx, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* A static, human-readable message for a status code. */
 const char* moba_strerror(int status);

@@ -270,3 +270,28 @@ def moba_backward(Q, K, V, dO, B: int, topk: int, scale: float, idx=None):
                 dK[bi, keys, g] += dk
                 dV[bi, keys, g] += dv
     return dQ, dK, dV
+
+
+# --------------------------------------------------------------------- packed sequences
+# Several sequences of different lengths packed along the token axis (cu = cumulative
+# lengths).  Each sequence is its own MoBA problem ("Approach" of the paper summary,
+# applied per sequence): its blocks start at its first token, its last block may be
+# partial, and it routes and attends only within itself.
+
+def moba_forward_varlen(Q, K, V, cu, B: int, topk: int, scale: float):
+    """Q [total, Hq, d], K/V [total, Hkv, d] float64, cu [nseq + 1] ->
+    (out [total, Hq, d], lse [Hq, total], idx [Hq, total, topk]), block ids counted
+    within each sequence."""
+    total, hq, d = Q.shape
+    out = np.empty_like(Q)
+    lse = np.empty((hq, total))
+    idx = np.full((hq, total, topk), -1, np.int32)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        o, l, i, _ = moba_forward(Q[None, a:e], K[None, a:e], V[None, a:e], B, topk, scale)
+        out[a:e] = o[0]
+        lse[:, a:e] = l[0]
+        idx[:, a:e] = i[0]
+    return out, lse, idx

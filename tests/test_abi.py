@@ -47,7 +47,11 @@ def test_check_args_codes(moba):
     assert moba.check_args(1, 128, 1, 1, 64, 16, 1, float("inf")) == E_ARG
     assert moba.check_args(1, 128, 1, 1, 96, 16, 1, 1.0) == E_UNS          # head_dim
     assert moba.check_args(1, 128, 1, 1, 64, 24, 1, 1.0) == E_UNS          # block % 16
-    assert moba.check_args(1, 130, 1, 1, 64, 16, 1, 1.0) == E_UNS          # T % block
+    assert moba.check_args(1, 130, 1, 1, 64, 16, 1, 1.0) == ok             # partial last block
+    assert moba.check_args(1, 16 * 2049, 1, 1, 64, 16, 1, 1.0) == E_UNS    # > 2048 blocks
+    # the backward needs whole blocks
+    assert moba.backward_workspace_bytes(1, 130, 1, 1, 64, 16, 2) == (0, 0)
+    assert moba.backward_workspace_bytes(1, 128, 1, 1, 64, 16, 2)[0] > 0
     assert moba.check_args(1, 128, 1, 1, 64, 16, 34, 1.0) == E_UNS         # topk > 33
     assert moba.check_args(1, 128, 1, 1, 64, 16, 33, 1.0) == 0
     assert moba.check_args(1, 128, 1, 1, 64, 16, 2, -1.0) == E_UNS         # scale <= 0
@@ -60,7 +64,8 @@ def test_workspace_sizes(moba):
     # history partials dominate: [Hq, T, topk - 1, d] bf16 for all heads
     assert full > 32 * 131072 * 11 * 128 * 2
     assert mn < full / 4
-    assert moba.workspace_bytes(1, 130, 1, 1, 64, 16, 2) == (0, 0)
+    assert moba.workspace_bytes(1, 130, 1, 1, 64, 16, 2)[0] > 0    # partial last block
+    assert moba.workspace_bytes(1, 130, 1, 1, 96, 16, 2) == (0, 0)    # head_dim 96
 
 
 def test_index_entry_count_closed_form(moba):
@@ -83,9 +88,18 @@ def test_forward_rejects_bad_args_before_any_launch(moba):
                           None, None, 0, None)
     assert st == -1
     # unsupported shape is reported before pointers are looked at
-    st = lib.moba_forward(None, None, None, 1, 130, 1, 1, 64, 16, 2, 0.125, None, None,
+    st = lib.moba_forward(None, None, None, 1, 128, 1, 1, 96, 16, 2, 0.125, None, None,
                           None, None, 0, None)
     assert st == -2
+    # packed sequences: the same shape rules, then the pointers (cu_seqlens first)
+    vargs = (None, None, None, None, 2, 300, 200, 1, 1, 64, 16, 2, 0.125, None, None, None,
+             None, 0, None)
+    assert lib.moba_forward_varlen(*vargs) == -1
+    assert lib.moba_forward_varlen(None, None, None, None, 2, 300, 200, 1, 1, 96, 16, 2,
+                                   0.125, None, None, None, None, 0, None) == -1
+    assert lib.moba_varlen_workspace_bytes(2, 300, 200, 1, 1, 96, 16, 2, None) == 0
+    assert lib.moba_varlen_workspace_bytes(2, 300, 400, 1, 1, 64, 16, 2, None) == 0
+    assert lib.moba_varlen_workspace_bytes(2, 300, 200, 1, 1, 64, 16, 2, None) > 0
     # dense causal attention: seqlen a multiple of 16, pointers checked on the host
     assert lib.moba_dense_forward(None, None, None, 1, 130, 1, 1, 64, 0.125, None, None,
                                   None) == -2
