@@ -36,11 +36,20 @@ ATTN_SOURCE = os.path.join(ROOT, "block_sparse_long_pool_amd", "csrc", "attn.hip
 # ------------------------------------------------------------------ work counts
 def pair_counts(T: int, B: int, k: int):
     """Per query head: (history pairs, current-block pairs) attended, from the
-    definition (T a multiple of B): B^2 * sum_c min(c, k-1) and nb * B (B+1) / 2."""
-    nb = T // B
-    hist = B * B * sum(min(c, k - 1) for c in range(nb))
-    cur = nb * B * (B + 1) // 2
+    definition: every row of block c attends min(c, k-1) whole blocks and the causal
+    prefix of its own block (the last block may be partial)."""
+    hist = cur = 0
+    for c in range((T + B - 1) // B):
+        n = min(B, T - c * B)
+        hist += n * min(c, k - 1) * B
+        cur += n * (n + 1) // 2
     return hist, cur
+
+
+# packed-sequence mix timed beside the main workload: six requests of ragged lengths
+# (131072 tokens in all), read out of the main workload's resident tensors
+VARLEN_LENGTHS = (40000, 30000, 25000, 20000, 10000, 6072)
+VARLEN_BLOCK, VARLEN_TOPK = 1024, 8
 
 
 def gate_bytes(w, needed_only: bool) -> int:
@@ -133,6 +142,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip timing dense causal attention on the same inputs")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip timing packed variable-length sequences")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward pass (dQ, dK, dV) on the same inputs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -289,6 +300,46 @@ def main(argv=None):
         }
         print(f"[bench] dense causal {dms:.2f} ms", file=sys.stderr, flush=True)
         del out_d, lse_d
+    if not a.no_varlen and w.batch == 1 and w.seqlen == sum(VARLEN_LENGTHS):
+        # packed variable-length prefill: the same tokens cut into six requests, each
+        # with its own block grid (B = 1024, top-8, ragged last blocks)
+        cu = [0]
+        for n in VARLEN_LENGTHS:
+            cu.append(cu[-1] + n)
+        total = cu[-1]
+        qv, kv, vv = (x.view(total, x.shape[2], x.shape[3]) for x in (q, k, v))
+        full_v, _ = moba.varlen_workspace_bytes(len(VARLEN_LENGTHS), total,
+                                                max(VARLEN_LENGTHS), w.hq, w.hkv, w.head_dim,
+                                                VARLEN_BLOCK, VARLEN_TOPK)
+        vws = torch.empty(full_v, dtype=torch.uint8, device=dev)
+        vo = torch.empty_like(qv)
+        vl = torch.empty((w.hq, total), dtype=torch.float32, device=dev)
+        vi = torch.empty((w.hq, total, VARLEN_TOPK), dtype=torch.int32, device=dev)
+
+        def vstep():
+            moba.forward_varlen(qv, kv, vv, cu, VARLEN_BLOCK, VARLEN_TOPK, w.sm_scale,
+                                workspace=vws, out=vo, lse=vl, idx=vi)
+
+        vstep()
+        torch.cuda.synchronize()
+        n_var = 5
+        e0.record(stream)
+        for _ in range(n_var):
+            vstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / n_var
+        vpairs = sum(sum(pair_counts(n, VARLEN_BLOCK, VARLEN_TOPK)) for n in VARLEN_LENGTHS)
+        vflop = 4 * w.head_dim * w.hq * vpairs
+        result["varlen"] = {
+            "ms": vms, "tflops": vflop / (vms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": vflop / (vms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "lengths": list(VARLEN_LENGTHS), "block": VARLEN_BLOCK, "topk": VARLEN_TOPK,
+            "flop": vflop,
+            "note": "moba_forward_varlen: the main inputs' tokens as six packed requests",
+        }
+        print(f"[bench] varlen {vms:.2f} ms", file=sys.stderr, flush=True)
+        del vws, vo, vl, vi
     if not a.no_backward:
         # the training backward of the same layer (selection held fixed): context for
         # the forward metric.  FLOP conventions: "effective" counts the five products of
