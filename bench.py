@@ -142,6 +142,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip timing dense causal attention on the same inputs")
+    ap.add_argument("--no-conv", action="store_true",
+                    help="skip timing the short key convolution")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip timing packed variable-length sequences")
     ap.add_argument("--no-backward", action="store_true",
@@ -300,6 +302,42 @@ def main(argv=None):
         }
         print(f"[bench] dense causal {dms:.2f} ms", file=sys.stderr, flush=True)
         del out_d, lse_d
+    if not a.no_conv:
+        # short key convolution within blocks (width 4, synthetic weights): HBM-bound,
+        # every key read once and written once
+        width = 4
+        gw = torch.Generator(device=dev)
+        gw.manual_seed(7)
+        wconv = torch.randn(w.hkv, w.head_dim, width, device=dev, generator=gw) / 2.0
+        kc = torch.empty_like(k)
+        moba.key_short_conv(k, wconv, w.block, out=kc)
+        torch.cuda.synchronize()
+        n_conv = 20
+        e0.record(stream)
+        for _ in range(n_conv):
+            moba.key_short_conv(k, wconv, w.block, out=kc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / n_conv
+        # a plain device copy of the same bytes, for scale
+        kc.copy_(k)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_conv):
+            kc.copy_(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = e0.elapsed_time(e1) / n_conv
+        cbytes = 2 * k.numel() * 2
+        result["key_short_conv"] = {
+            "ms": cms, "gbs": cbytes / (cms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": cbytes / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "width": width, "algorithmic_bytes": cbytes,
+            "copy_gbs": cbytes / (copy_ms * 1e-3) / 1e9,
+            "note": "moba_key_short_conv over the keys (read + write of k)",
+        }
+        print(f"[bench] key conv {cms:.3f} ms", file=sys.stderr, flush=True)
+        del kc, wconv
     if not a.no_varlen and w.batch == 1 and w.seqlen == sum(VARLEN_LENGTHS):
         # packed variable-length prefill: the same tokens cut into six requests, each
         # with its own block grid (B = 1024, top-8, ragged last blocks)

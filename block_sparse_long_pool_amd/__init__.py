@@ -22,6 +22,7 @@ __all__ = [
     "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
     "backward", "backward_workspace_bytes", "forward_varlen", "varlen_workspace_bytes",
+    "key_short_conv",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -49,6 +50,7 @@ _SIGS = {
                                 _vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "moba_dense_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "moba_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "moba_key_short_conv": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "moba_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i,
                                           ctypes.POINTER(_sz)]),
     "moba_forward_varlen": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
@@ -309,6 +311,41 @@ def forward_varlen(q, k, v, cu_seqlens, block: int, topk: int, scale: float | No
                                      workspace.numel(), _stream_ptr())
     _raise(st, "moba_forward_varlen")
     return out, lse, idx
+
+
+def key_short_conv(k, weight, block: int, cu_seqlens=None, out=None):
+    """Short depthwise causal convolution of the keys within blocks.  k [b, T, Hkv, d]
+    (or packed [total, Hkv, d] with cu_seqlens) bf16 on the GPU, weight [Hkv, d, width]
+    float32 on the GPU (width <= 8).  Returns the convolved keys, bf16, like k."""
+    torch = _torch()
+    packed = cu_seqlens is not None
+    _need(k, "k", torch.bfloat16, 3 if packed else 4)
+    _need(weight, "weight", torch.float32, 3)
+    hkv, d = k.shape[-2], k.shape[-1]
+    if weight.shape[0] != hkv or weight.shape[1] != d:
+        raise ValueError(f"weight must be [{hkv}, {d}, width] (got {tuple(weight.shape)})")
+    if packed:
+        cu_host = torch.as_tensor(cu_seqlens).to("cpu", torch.int64)
+        lens = cu_host[1:] - cu_host[:-1]
+        if (cu_host.dim() != 1 or cu_host.numel() < 2 or int(cu_host[0]) != 0
+                or int(cu_host[-1]) != k.shape[0] or bool((lens < 0).any())):
+            raise ValueError("cu_seqlens must start at 0, not decrease and end at k.shape[0]")
+        batch, seqlen, total = cu_host.numel() - 1, max(1, int(lens.max())), k.shape[0]
+        cu_dev = cu_host.to(device=k.device, dtype=torch.int32)
+        cu_ptr = cu_dev.data_ptr()
+    else:
+        batch, seqlen, total = k.shape[0], k.shape[1], 0
+        cu_ptr = None
+    out = torch.empty_like(k) if out is None else out
+    _need(out, "out", torch.bfloat16, k.dim())
+    if out.shape != k.shape:
+        raise ValueError("out must have the shape of k")
+    with torch.cuda.device(k.device):
+        st = lib.moba_key_short_conv(k.data_ptr(), weight.data_ptr(), cu_ptr, batch, seqlen,
+                                     total, hkv, d, block, weight.shape[2], out.data_ptr(),
+                                     _stream_ptr())
+    _raise(st, "moba_key_short_conv")
+    return out
 
 
 def backward_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk):

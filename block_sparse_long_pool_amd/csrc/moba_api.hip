@@ -408,6 +408,28 @@ int moba_forward_varlen(const void* q, const void* k, const void* v,
                      nullptr, nullptr);
 }
 
+// ------------------------------------------------------------------- key convolution
+int moba_key_short_conv(const void* k, const float* weight, const int32_t* cu_seqlens,
+                        int batch, int seqlen, int total, int hkv, int head_dim, int block,
+                        int width, void* out, void* stream) {
+  Shape s{};
+  int st;
+  if (cu_seqlens) {
+    st = varlen_shape(batch, total, seqlen, hkv, hkv, head_dim, block, 1, 1.f, cu_seqlens,
+                      &s);
+  } else {
+    st = check(batch, seqlen, hkv, hkv, head_dim, block, 1, 1.f);
+    s = Shape{batch, seqlen, hkv, hkv, head_dim, block, 1};
+  }
+  if (st != MOBA_OK) return st;
+  if (width < 1) return MOBA_ERR_INVALID_ARG;
+  if (width > moba::conv_max_width()) return MOBA_ERR_UNSUPPORTED;
+  if (!k || !weight || !out) return MOBA_ERR_INVALID_ARG;
+  return hip_status(moba::launch_key_conv(s, static_cast<const uint16_t*>(k), weight, width,
+                                          static_cast<uint16_t*>(out),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------------- stages
 size_t moba_stage_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim,
                                   int block, int topk) {

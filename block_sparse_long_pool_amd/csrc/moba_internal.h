@@ -126,6 +126,11 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
                                float* lse, hipStream_t st);
 int history_tile_rows();
 
+// short depthwise causal convolution of the keys within blocks (width <= 8)
+int conv_max_width();
+hipError_t launch_key_conv(const Shape& s, const uint16_t* k, const float* weight, int width,
+                           uint16_t* out, hipStream_t st);
+
 // backward with the selection held fixed: D = rowsum(dO * out), dQ over the history
 // tiles (fp32 partials per row and slot) and the current blocks (sum -> dq), and dK/dV
 // per 32*4 keys of a block over the rows that attend them

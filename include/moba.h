@@ -191,6 +191,27 @@ int moba_forward_varlen(const void* q, const void* k, const void* v,
                         void* out, float* lse, int32_t* idx, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Short convolution of the keys within blocks (FlashMoBA story on hyper.ai, paragraph
+ * on short convolutions: a short convolution inside each block clusters the block's
+ * relevant information and strengthens the routing signal).  Depthwise and causal
+ * along tokens, per kv-head channel, and no tap crosses a block boundary:
+ *   out[t, g, c] = sum over i < width with t - i in t's block of
+ *                  weight[g, c, i] * k[t - i, g, c]
+ * accumulated in float32, rounded to bf16 (nearest even).  The result is meant to be
+ * passed as the keys of moba_forward / moba_forward_varlen.
+ *   k, out      [batch, seqlen, hkv, d] bf16, or with cu_seqlens (DEVICE int32
+ *               [batch + 1], as for moba_forward_varlen; seqlen = the longest
+ *               sequence) packed [total, hkv, d].  out must not overlap k.
+ *   weight      DEVICE float32 [hkv, d, width]
+ *   width       1 .. 8 (MOBA_ERR_UNSUPPORTED above, MOBA_ERR_INVALID_ARG below)
+ * Shape limits as moba_forward's (with hq = hkv); total is ignored without cu_seqlens.
+ * Enqueued on `stream` without synchronising; needs no workspace.
+ * ------------------------------------------------------------------------- */
+int moba_key_short_conv(const void* k, const float* weight, const int32_t* cu_seqlens,
+                        int batch, int seqlen, int total, int hkv, int head_dim, int block,
+                        int width, void* out, void* stream);
+
 /* A static, human-readable message for a status code. */
 const char* moba_strerror(int status);
 

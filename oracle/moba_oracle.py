@@ -295,3 +295,31 @@ def moba_forward_varlen(Q, K, V, cu, B: int, topk: int, scale: float):
         lse[:, a:e] = l[0]
         idx[:, a:e] = i[0]
     return out, lse, idx
+
+
+# ------------------------------------------------------------------- key short convolution
+# A short convolution of the keys inside each block before pooling (FlashMoBA story,
+# paragraph on short convolutions).  Reading: depthwise and causal along tokens, per
+# kv-head channel, with no tap reaching into the previous block.
+
+def key_short_conv(K, W, B: int, cu=None):
+    """K [b, T, Hkv, d] (or packed [total, Hkv, d] with cu), W [Hkv, d, w] float64 ->
+    out like K: out[t, g, c] = sum over taps i with t - i in t's block of
+    W[g, c, i] * K[t - i, g, c] (t counted within its sequence)."""
+    if cu is not None:
+        out = np.empty_like(K)
+        for s in range(len(cu) - 1):
+            a, e = int(cu[s]), int(cu[s + 1])
+            if e > a:
+                out[a:e] = key_short_conv(K[None, a:e], W, B)[0]
+        return out
+    b, T, hkv, d = K.shape
+    w = W.shape[2]
+    out = np.zeros_like(K)
+    for t in range(T):
+        start = (t // B) * B
+        for i in range(w):
+            if t - i < start:
+                break
+            out[:, t] += W[None, :, :, i] * K[:, t - i]
+    return out
