@@ -320,6 +320,42 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     }
 }
 
+// ------------------------------------------------------------------------ densify
+// Copies, for every entry e of the inverted index (one workgroup per index tile of up
+// to 256 entries of one list (b, g, j)), the entry's Q row and dO row to rows[e] =
+// [q | dout] (2 D bf16) and its lse and delta to meta[e] = [lse, delta]: the history
+// rows of each block in list order, contiguous, for the dK/dV kernel.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_densify_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int G,
+    int g0, int ng, int nb, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
+    uint16_t* __restrict__ rows, float* __restrict__ meta) {
+  constexpr int CPR = D / 8;
+  if ((int)blockIdx.x >= *tile_count) return;
+  const int4 tl = tiles[blockIdx.x];
+  const int list = tl.x, e0 = tl.y, ne = tl.z - tl.y;
+  const int gi = (list / nb) % ng, b = list / (nb * ng);
+  const int hb = (g0 + gi) * G;
+  for (int x = threadIdx.x; x < ne * 2 * CPR; x += 256) {
+    const int e = e0 + x / (2 * CPR), which = (x / CPR) & 1, col = (x % CPR) * 8;
+    const uint32_t rr = entries[e] >> 5;
+    const int t = (int)rr / G, h = hb + (int)rr % G;
+    const uint16_t* src = (which ? dout : q) + (((size_t)b * T + t) * hq + h) * D + col;
+    *reinterpret_cast<u32x4_t*>(rows + ((size_t)e * 2 + which) * D + col) =
+        *reinterpret_cast<const u32x4_t*>(src);
+  }
+  if ((int)threadIdx.x < ne) {
+    const int e = e0 + threadIdx.x;
+    const uint32_t rr = entries[e] >> 5;
+    const int t = (int)rr / G, h = hb + (int)rr % G;
+    const size_t at = ((size_t)b * hq + h) * T + t;
+    meta[(size_t)e * 2] = lse[at];
+    meta[(size_t)e * 2 + 1] = delta[at];
+  }
+}
+
 // ----------------------------------------------------------------------- dK/dV kernel
 // One workgroup = 32 * kKvTiles keys of block j of kv-head g.  Rows: the history list
 // of (b, g, j) from the inverted index, then the rows of block j from token kc0 on
@@ -328,6 +364,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 // dV^T += dO^T P; wave "dS" computes dP = dO V^T, takes P through LDS, and
 // dK^T += Q^T dS with dS = P (dP - D).  Each wave keeps one 32 x D accumulator and one
 // B operand, so two waves fit per SIMD and one's VALU work overlaps the other's MFMAs.
+// The history rows are read from bwd_densify_kernel's copy: every workgroup of the
+// block streams the same contiguous rows instead of gathering them from all over Q.
 template <int D>
 struct KvLds {
   using S = BwdStrides<D>;
@@ -344,8 +382,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int hkv,
     int block, float sl, float scale, int g0, int ng, int nb,
-    const int32_t* __restrict__ list_offsets, const uint32_t* __restrict__ entries,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    const int32_t* __restrict__ list_offsets, const uint16_t* __restrict__ dense_rows,
+    const float* __restrict__ dense_meta, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv) {
   using S = BwdStrides<D>;
   using L = KvLds<D>;
   constexpr int KS = D / 16, CPR = D / 8;
@@ -379,21 +418,15 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   // Staging of a 32-row group: thread x moves 16-byte chunk x % (32*CPR) of Q (x <
-  // 32*CPR) or of dO; threads 0..31 also the rows' lse2, delta and causal limit t.  Rows
-  // are packed as rr = t*G + h%G (history rows: the inverted index's entries).  While
-  // group i is computed, the row data of group i+1 and the row ids of group i+2 are in
-  // flight, so the index read and the gather that depends on it overlap.  Rows past the
-  // end read a valid row (token kc0) and get p = 0 from lse2 = +inf, so the fetch has
-  // no branches.
+  // 32*CPR) or of dO; threads 0..31 also the rows' lse2, delta and causal limit t.
+  // History rows come from the densified copy of the list (entry order, contiguous);
+  // the block's own rows are token kc0 + rc / G, head rc % G.  Rows past the end read a
+  // valid row and get p = 0 from lse2 = +inf, so the fetch has no branches.  Group i+1
+  // is in flight while group i is computed.
   constexpr int CHUNKS = 2 * 32 * CPR;
   constexpr int NC = CHUNKS / kKvThreads;
   static_assert(CHUNKS % kKvThreads == 0, "every thread moves whole chunks");
   const int gshift = __builtin_ctz((unsigned)G);   // G is a power of two
-  const uint32_t safe_rr = (uint32_t)kc0 << gshift;
-  // entries of this list through a buffer descriptor: reads past nhist return 0
-  const __amdgpu_buffer_rsrc_t ent_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(entries ? entries + hbeg : nullptr), (short)0, nhist * 4,
-      0x00020000);
   const int row_base = (b * T) * hq + g * G;        // row index of (b, t=0, head g*G)
   const int meta_base = (b * hq + g * G) * T;       // lse/delta index of (b, g*G, t=0)
   int crow[NC], ccol[NC];
@@ -405,44 +438,39 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     crow[c] = (x % (32 * CPR)) / CPR;
     ccol[c] = (x % CPR) * 8;
   }
-  struct Ids {
-    uint32_t rr[NC];
-    uint32_t mr;       // the meta row of threads 0..31
-    bool mhist, mvalid;
-  };
   struct Rows {
     u32x4_t c[NC];
     float f, d;
     int t;
   };
-  auto rowid = [&](int r) -> uint32_t {
-    const uint32_t e = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ent_rsrc, r * 4, 0, 0);
-    const int rc = r - nhist;
-    const uint32_t cur = ((uint32_t)(kc0 + (rc >> gshift)) << gshift) | (uint32_t)(rc & (G - 1));
-    return r >= nrows ? safe_rr : (r < nhist ? e >> 5 : cur);
+  // the q (dO) row of current row r >= nhist (clamped to the last row past the end)
+  auto cur_row = [&](int r) -> int {
+    const int rc = min(r, nrows - 1) - nhist;
+    return row_base + (kc0 + (rc >> gshift)) * hq + (rc & (G - 1));
   };
-  auto fetch_ids = [&](int r0, Ids& id) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) id.rr[c] = rowid(r0 + crow[c]);
-    const int r = r0 + (threadIdx.x & 31);
-    id.mr = rowid(r);
-    id.mhist = r < nhist;
-    id.mvalid = r < nrows;
-  };
-  auto fetch_rows = [&](const Ids& id, Rows& rd) {
+  auto fetch_rows = [&](int r0, Rows& rd) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint32_t rr = id.rr[c];
-      const int row = row_base + (int)(rr >> gshift) * hq + (int)(rr & (G - 1));
-      const uint16_t* src = (cdo[c] ? dout : q) + (size_t)row * D + ccol[c];
-      rd.c[c] = *reinterpret_cast<const u32x4_t*>(src);
+      const int r = r0 + crow[c];
+      const uint16_t* hsrc = dense_rows + ((size_t)(hbeg + r) * 2 + cdo[c]) * D;
+      const uint16_t* csrc = (cdo[c] ? dout : q) + (size_t)cur_row(r) * D;
+      rd.c[c] = *reinterpret_cast<const u32x4_t*>((r < nhist ? hsrc : csrc) + ccol[c]);
     }
-    const int t = (int)(id.mr >> gshift);
-    const int at = meta_base + (int)(id.mr & (G - 1)) * T + t;
-    const float lv = lse[at], dv0 = delta[at];
-    rd.f = id.mvalid ? lv * kLog2e : INFINITY;   // p = 0 for rows past the end
-    rd.d = id.mvalid ? dv0 : 0.f;
-    rd.t = id.mhist ? 0x7fffffff : t;
+    const int r = r0 + (threadIdx.x & 31);
+    float lv, dv0;
+    if (r < nhist) {
+      const float* m = dense_meta + (size_t)(hbeg + r) * 2;
+      lv = m[0];
+      dv0 = m[1];
+    } else {
+      const int rc = min(r, nrows - 1) - nhist;
+      const int at = meta_base + (rc & (G - 1)) * T + kc0 + (rc >> gshift);
+      lv = lse[at];
+      dv0 = delta[at];
+    }
+    rd.f = r < nrows ? lv * kLog2e : INFINITY;   // p = 0 for rows past the end
+    rd.d = r < nrows ? dv0 : 0.f;
+    rd.t = r < nhist ? 0x7fffffff : kc0 + ((min(r, nrows - 1) - nhist) >> gshift);
   };
   auto store_rows = [&](const Rows& rd, int buf) {
     char* base = lds + buf * L::BUF;
@@ -540,11 +568,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
         acc[dt] = mfma32x32x16(read_t_operand<D>(tt, ks, dt), op[ks], acc[dt]);
   };
   const int ngroups = (nrows + 31) / 32;
-  Ids id;
   Rows rd;
-  fetch_ids(0, id);
-  fetch_rows(id, rd);            // group 0
-  fetch_ids(32, id);             // group 1
+  fetch_rows(0, rd);             // group 0
   store_rows(rd, 0);
   __syncthreads();
   using Mask = std::true_type;
@@ -552,15 +577,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   // groups [gm0, gm1) hold the rows that need the causal mask
   const int gm0 = mask_lo / 32, gm1 = (mask_hi + 31) / 32;
   for (int gidx = 0; gidx < ngroups; gidx += 2) {
-    fetch_rows(id, rd);          // group gidx + 1
-    fetch_ids((gidx + 2) * 32, id);
+    fetch_rows((gidx + 1) * 32, rd);     // group gidx + 1
     if (gidx >= gm0 && gidx < gm1) compute(0, Mask{});
     else compute(0, NoMask{});
     store_rows(rd, 1);
     __syncthreads();
     if (gidx + 1 >= ngroups) break;
-    fetch_rows(id, rd);          // group gidx + 2
-    fetch_ids((gidx + 3) * 32, id);
+    fetch_rows((gidx + 2) * 32, rd);     // group gidx + 2
     if (gidx + 1 >= gm0 && gidx + 1 < gm1) compute(1, Mask{});
     else compute(1, NoMask{});
     store_rows(rd, 0);
@@ -631,18 +654,35 @@ hipError_t launch_bwd_dq_current(const Shape& s, const uint16_t* q, const uint16
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_densify(const Shape& s, const uint16_t* q, const uint16_t* dout,
+                              const float* lse, const float* delta, int g0, int ng,
+                              const int4* tiles, const int32_t* tile_count, int max_tiles,
+                              const uint32_t* entries, uint16_t* rows, float* meta,
+                              hipStream_t st) {
+  if (max_tiles <= 0) return hipSuccess;
+#define MOBA_DENSE(DD)                                                                     \
+  hipLaunchKernelGGL((bwd_densify_kernel<DD>), dim3(max_tiles), dim3(256), 0, st, q, dout,  \
+                     lse, delta, s.T, s.hq, s.G(), g0, ng, s.nb(), tiles, tile_count,        \
+                     entries, rows, meta)
+  if (s.d == 128) MOBA_DENSE(128);
+  else MOBA_DENSE(64);
+#undef MOBA_DENSE
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* dout, const float* lse,
                            const float* delta, float scale, int g0, int ng,
-                           const int32_t* list_offsets, const uint32_t* entries, uint16_t* dk,
-                           uint16_t* dv, hipStream_t st) {
+                           const int32_t* list_offsets, const uint16_t* dense_rows,
+                           const float* dense_meta, uint16_t* dk, uint16_t* dv,
+                           hipStream_t st) {
   const float sl = scale * kLog2e;
   const int kpw = 32 * kKvTiles;
   dim3 grid((s.block + kpw - 1) / kpw, s.nb(), s.b * ng);
 #define MOBA_KV(DD)                                                                        \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD>), grid, dim3(kKvThreads), 0, st, q, k, v, dout,    \
                      lse, delta, s.T, s.hq, s.hkv, s.block, sl, scale, g0, ng, s.nb(),        \
-                     list_offsets, entries, dk, dv)
+                     list_offsets, dense_rows, dense_meta, dk, dv)
   if (s.d == 128) MOBA_KV(128);
   else MOBA_KV(64);
 #undef MOBA_KV

@@ -110,7 +110,7 @@ bool layout_ok(const Layout& L) {
 // fp32 dQ parts of every (row, history slot).
 struct BwdLayout {
   size_t delta, chunk_counts, list_count, list_offsets, tile_offsets, tiles, entries,
-      dq_part;
+      dense_rows, dense_meta, dq_part;
   size_t total;
   long long n_entries, max_tiles;
 };
@@ -136,6 +136,8 @@ BwdLayout make_bwd_layout(const Shape& s, int ng) {
   L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
+  L.dense_rows = take((size_t)L.n_entries * 2 * s.d * sizeof(uint16_t));
+  L.dense_meta = take((size_t)L.n_entries * 2 * sizeof(float));
   L.dq_part = take((size_t)s.b * ng * s.G() * s.T * s.KH() * s.d * sizeof(float));
   L.total = off;
   return L;
@@ -560,7 +562,8 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
     const int ngc = ng < hkv - g0 ? ng : hkv - g0;
     const int nlc = s.b * ngc * s.nb();
     const int32_t* list_offsets = nullptr;
-    const uint32_t* entries = nullptr;
+    uint16_t* dense_rows = reinterpret_cast<uint16_t*>(ws + L.dense_rows);
+    float* dense_meta = reinterpret_cast<float*>(ws + L.dense_meta);
     if (s.KH() > 0) {
       int32_t* lo = reinterpret_cast<int32_t*>(ws + L.list_offsets);
       int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
@@ -574,14 +577,17 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
       MOBA_TRY(moba::launch_bwd_dq_history(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
                                            tiles, tile_offsets + nlc, (int)Lc.max_tiles,
                                            ent, dq_part, hs));
+      MOBA_TRY(moba::launch_bwd_densify(s, qb, gb, lse, delta, g0, ngc, tiles,
+                                        tile_offsets + nlc, (int)Lc.max_tiles, ent,
+                                        dense_rows, dense_meta, hs));
       list_offsets = lo;
-      entries = ent;
     }
     MOBA_TRY(moba::launch_bwd_dq_current(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
                                          dq_part, static_cast<uint16_t*>(dq), hs));
     MOBA_TRY(moba::launch_bwd_dkdv(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
-                                   list_offsets, entries, static_cast<uint16_t*>(dk),
-                                   static_cast<uint16_t*>(dv), hs));
+                                   list_offsets, dense_rows, dense_meta,
+                                   static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                                   hs));
   }
   return MOBA_OK;
 }

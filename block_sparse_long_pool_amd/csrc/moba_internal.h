@@ -147,10 +147,17 @@ hipError_t launch_bwd_dq_current(const Shape& s, const uint16_t* q, const uint16
                                  const uint16_t* v, const uint16_t* dout, const float* lse,
                                  const float* delta, float scale, int g0, int ng,
                                  const float* dq_part, uint16_t* dq, hipStream_t st);
+// the Q and dO rows and lse/delta of every index entry, in entry order (contiguous)
+hipError_t launch_bwd_densify(const Shape& s, const uint16_t* q, const uint16_t* dout,
+                              const float* lse, const float* delta, int g0, int ng,
+                              const int4* tiles, const int32_t* tile_count, int max_tiles,
+                              const uint32_t* entries, uint16_t* rows, float* meta,
+                              hipStream_t st);
 hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* dout, const float* lse,
                            const float* delta, float scale, int g0, int ng,
-                           const int32_t* list_offsets, const uint32_t* entries, uint16_t* dk,
-                           uint16_t* dv, hipStream_t st);
+                           const int32_t* list_offsets, const uint16_t* dense_rows,
+                           const float* dense_meta, uint16_t* dk, uint16_t* dv,
+                           hipStream_t st);
 
 }  // namespace moba
