@@ -323,3 +323,19 @@ def key_short_conv(K, W, B: int, cu=None):
                 break
             out[:, t] += W[None, :, :, i] * K[:, t - i]
     return out
+
+
+def moba_backward_varlen(Q, K, V, dO, cu, B: int, topk: int, scale: float):
+    """dQ, dK, dV (float64, packed like Q, K, V) of packed sequences, each one the batch-1
+    backward of its own sequence with the oracle's own selection."""
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        gq, gk, gv = moba_backward(Q[None, a:e], K[None, a:e], V[None, a:e], dO[None, a:e],
+                                   B, topk, scale)
+        dQ[a:e], dK[a:e], dV[a:e] = gq[0], gk[0], gv[0]
+    return dQ, dK, dV

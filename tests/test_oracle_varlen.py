@@ -72,3 +72,36 @@ def test_varlen_all_blocks_is_causal_attention_per_sequence():
     m = z.max(axis=2)
     np.testing.assert_allclose(l1, m + np.log(np.exp(z - m[..., None]).sum(axis=2)),
                                rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("lengths,B,k", [((37, 100, 64, 5), 16, 3), ((48, 1, 96), 16, 4)])
+def test_varlen_backward_matches_packed_autograd(lengths, B, k):
+    """Gradients of packed sequences against torch autograd through one dense masked
+    softmax over the packed token axis: allowed[h, i, u] = u is in a block of i's own
+    sequence that i selected (ids from the packed brute force) and u <= i (fp64)."""
+    hq, hkv, d = 4, 2, 8
+    Q, K, V, cu = packed_qkv(sum(lengths) + 7, lengths, hq, hkv, d)
+    dO = np.random.default_rng(3).standard_normal(Q.shape)
+    sc = 0.35
+    _, _, idx = oracle.moba_bruteforce_packed(Q, K, V, cu, B, k, sc)
+    total = int(cu[-1])
+    seq = np.searchsorted(cu, np.arange(total), side="right") - 1
+    pos = np.arange(total) - cu[seq]
+    allowed = np.zeros((hq, total, total), bool)
+    for h in range(hq):
+        for i in range(total):
+            S = set(int(j) for j in idx[h, i] if j >= 0)
+            allowed[h, i] = ((seq == seq[i]) & np.isin(pos // B, list(S))
+                             & (pos <= pos[i]))
+    G = hq // hkv
+    q = torch.tensor(Q.transpose(1, 0, 2), requires_grad=True)
+    kk = torch.tensor(K.transpose(1, 0, 2), requires_grad=True)
+    vv = torch.tensor(V.transpose(1, 0, 2), requires_grad=True)
+    s = sc * q @ kk.repeat_interleave(G, 0).transpose(1, 2)
+    s = s.masked_fill(~torch.tensor(allowed), float("-inf"))
+    out = torch.softmax(s, -1) @ vv.repeat_interleave(G, 0)
+    (out * torch.tensor(dO.transpose(1, 0, 2))).sum().backward()
+    ref = [x.grad.numpy().transpose(1, 0, 2) for x in (q, kk, vv)]
+    got = oracle.moba_backward_varlen(Q, K, V, dO, cu, B, k, sc)
+    for g_, r_ in zip(got, ref):
+        np.testing.assert_allclose(g_, r_, rtol=1e-9, atol=1e-11)
