@@ -22,7 +22,7 @@ __all__ = [
     "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
     "backward", "backward_workspace_bytes", "forward_varlen", "varlen_workspace_bytes",
-    "key_short_conv",
+    "key_short_conv", "backward_varlen", "backward_varlen_workspace_bytes",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -51,6 +51,10 @@ _SIGS = {
     "moba_dense_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "moba_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "moba_key_short_conv": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "moba_backward_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i,
+                                                   ctypes.POINTER(_sz)]),
+    "moba_backward_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                  _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moba_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i,
                                           ctypes.POINTER(_sz)]),
     "moba_forward_varlen": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
@@ -346,6 +350,69 @@ def key_short_conv(k, weight, block: int, cu_seqlens=None, out=None):
                                      _stream_ptr())
     _raise(st, "moba_key_short_conv")
     return out
+
+
+def _cu_host(cu_seqlens, total):
+    torch = _torch()
+    cu_host = torch.as_tensor(cu_seqlens).to("cpu", torch.int64)
+    if cu_host.dim() != 1 or cu_host.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+    lens = cu_host[1:] - cu_host[:-1]
+    if int(cu_host[0]) != 0 or int(cu_host[-1]) != total or bool((lens < 0).any()):
+        raise ValueError("cu_seqlens must start at 0, not decrease and end at the token count")
+    return cu_host, cu_host.numel() - 1, max(1, int(lens.max()))
+
+
+def backward_varlen_workspace_bytes(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk):
+    """(all-kv-heads size, one-kv-head size) of the packed-sequence backward workspace."""
+    mn = _sz(0)
+    full = lib.moba_backward_varlen_workspace_bytes(nseq, total, max_seqlen, hq, hkv, head_dim,
+                                                    block, topk, ctypes.byref(mn))
+    return int(full), int(mn.value)
+
+
+def backward_varlen(q, k, v, out, lse, idx, dout, cu_seqlens, block: int, topk: int,
+                    scale: float | None = None, workspace=None,
+                    max_workspace_bytes: int | None = None):
+    """Gradients of ``forward_varlen`` with its selection ``idx`` held fixed.  Packed
+    layouts as ``forward_varlen``; returns (dq, dk, dv) bf16 like q, k, v."""
+    torch = _torch()
+    for t, nme in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, nme, torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    _need(idx, "idx", torch.int32, 3)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if (k.shape[0] != total or k.shape[2] != d or v.shape != k.shape or out.shape != q.shape
+            or dout.shape != q.shape or lse.shape != (hq, total)
+            or idx.shape != (hq, total, topk)):
+        raise ValueError("shape mismatch between q, k, v, out, lse, idx, dout")
+    cu_host, nseq, max_seqlen = _cu_host(cu_seqlens, total)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        full, mn = backward_varlen_workspace_bytes(nseq, total, max_seqlen, hq, hkv, d, block,
+                                                   topk)
+        if full == 0:
+            _raise(MOBA_ERR_UNSUPPORTED, "moba_backward_varlen_workspace_bytes")
+        if max_workspace_bytes is None:
+            free, _ = torch.cuda.mem_get_info(q.device)
+            max_workspace_bytes = int(0.6 * free)
+        workspace = _alloc_workspace(full if full <= max_workspace_bytes
+                                     else max(mn, max_workspace_bytes), q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    cu_dev = cu_host.to(device=q.device, dtype=torch.int32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        st = lib.moba_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), idx.data_ptr(), dout.data_ptr(),
+                                      cu_dev.data_ptr(), nseq, total, max_seqlen, hq, hkv, d,
+                                      block, topk, float(scale), dq.data_ptr(), dk.data_ptr(),
+                                      dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      _stream_ptr())
+    _raise(st, "moba_backward_varlen")
+    return dq, dk, dv
 
 
 def backward_workspace_bytes(batch, seqlen, hq, hkv, head_dim, block, topk):

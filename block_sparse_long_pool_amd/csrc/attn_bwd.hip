@@ -89,11 +89,12 @@ __device__ __forceinline__ void load_row_operand(bf16x8_t (&x)[D / 16], const ui
 }  // namespace
 
 // ------------------------------------------------------------------- D = rowsum(dO*O)
+// rows are (token, head) of the [tokens, hq, d] tensors; delta is laid out like lse
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ out,
                                                         const uint16_t* __restrict__ dout,
-                                                        int T, int hq, int d, long rows,
+                                                        SeqMap sq, int hq, int d, long rows,
                                                         float* __restrict__ delta) {
-  const long r = (long)blockIdx.x * 256 + threadIdx.x;   // row index b*T*hq + t*hq + h
+  const long r = (long)blockIdx.x * 256 + threadIdx.x;   // row index token*hq + h
   if (r >= rows) return;
   const uint16_t* o = out + r * d;
   const uint16_t* g = dout + r * d;
@@ -105,8 +106,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
     for (int e = 0; e < 4; ++e)
       acc += bf16lo(a[e]) * bf16lo(b[e]) + bf16hi(a[e]) * bf16hi(b[e]);
   }
-  const long h = r % hq, t = (r / hq) % T, b = r / ((long)hq * T);
-  delta[(b * hq + h) * T + t] = acc;
+  const long h = r % hq, token = r / hq;
+  if (sq.cu) delta[h * sq.total + token] = acc;
+  else delta[((token / sq.T) * hq + h) * sq.T + token % sq.T] = acc;
 }
 
 // ------------------------------------------------------------------------- dQ kernel
@@ -128,8 +130,8 @@ template <int D, bool CUR>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int hkv,
-    int block, int topk, float sl, float scale, int g0, int ng, int nb,
+    const float* __restrict__ lse, const float* __restrict__ delta, SeqMap sq, int hq,
+    int hkv, int block, int topk, float sl, float scale, int g0, int ng, int nb,
     const int4* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint32_t* __restrict__ entries, float* __restrict__ dq_part,
     uint16_t* __restrict__ dq) {
@@ -169,22 +171,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const int t0 = c * block + x * TT;
     hl = wave % G;
     t = t0 + (wave / G) * 32 + n;
-    valid = t < min(t0 + TT, (c + 1) * block);
     kbeg = c * block;
-    kend = min(t0 + TT, (c + 1) * block);
+    // a partial last block, or a block past the end of a shorter packed sequence
+    kend = min(min(t0 + TT, (c + 1) * block), sq.len(b));
+    if (t0 >= kend) return;
+    valid = t < kend;
     if (!valid) t = c * block;
   }
   const int g = g0 + gi, h = g * G + hl;
+  const int tok0 = sq.tok0(b);
   const size_t rs = (size_t)hkv * D;
-  const uint16_t* kbase = k + ((size_t)b * T * hkv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * T * hkv + g) * D;
+  const uint16_t* kbase = k + ((size_t)tok0 * hkv + g) * D;
+  const uint16_t* vbase = v + ((size_t)tok0 * hkv + g) * D;
   // the row's operands and statistics
   bf16x8_t bq[KS], bo[KS];
-  const size_t qrow = ((size_t)b * T + t) * hq + h;
+  const size_t qrow = ((size_t)tok0 + t) * hq + h;
   load_row_operand<D>(bq, q + qrow * D, valid);
   load_row_operand<D>(bo, dout + qrow * D, valid);
-  const float lse2 = valid ? lse[((size_t)b * hq + h) * T + t] * kLog2e : 0.f;
-  const float dlt = valid ? delta[((size_t)b * hq + h) * T + t] : 0.f;
+  const size_t lrow = sq.lrow(b, h, hq) + t;
+  const float lse2 = valid ? lse[lrow] * kLog2e : 0.f;
+  const float dlt = valid ? delta[lrow] : 0.f;
   f32x16_t acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 
   if (!valid) return;
   const int ngq = ng * G;
-  const size_t prow = ((size_t)(b * ngq + gi * G + hl) * T + t) * KH;
+  const size_t prow = (sq.prow(b, gi * G + hl, ngq) + t) * KH;
   if (!CUR) {
     float* po = dq_part + (prow + slot) * D + hf * 4;
 #pragma unroll
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void bwd_densify_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int G,
+    const float* __restrict__ lse, const float* __restrict__ delta, SeqMap sq, int hq, int G,
     int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     uint16_t* __restrict__ rows, float* __restrict__ meta) {
@@ -337,12 +343,12 @@ __global__ __launch_bounds__(256) void bwd_densify_kernel(
   const int4 tl = tiles[blockIdx.x];
   const int list = tl.x, e0 = tl.y, ne = tl.z - tl.y;
   const int gi = (list / nb) % ng, b = list / (nb * ng);
-  const int hb = (g0 + gi) * G;
+  const int hb = (g0 + gi) * G, tok0 = sq.tok0(b);
   for (int x = threadIdx.x; x < ne * 2 * CPR; x += 256) {
     const int e = e0 + x / (2 * CPR), which = (x / CPR) & 1, col = (x % CPR) * 8;
     const uint32_t rr = entries[e] >> 5;
     const int t = (int)rr / G, h = hb + (int)rr % G;
-    const uint16_t* src = (which ? dout : q) + (((size_t)b * T + t) * hq + h) * D + col;
+    const uint16_t* src = (which ? dout : q) + (((size_t)tok0 + t) * hq + h) * D + col;
     *reinterpret_cast<u32x4_t*>(rows + ((size_t)e * 2 + which) * D + col) =
         *reinterpret_cast<const u32x4_t*>(src);
   }
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256) void bwd_densify_kernel(
     const int e = e0 + threadIdx.x;
     const uint32_t rr = entries[e] >> 5;
     const int t = (int)rr / G, h = hb + (int)rr % G;
-    const size_t at = ((size_t)b * hq + h) * T + t;
+    const size_t at = sq.lrow(b, h, hq) + t;
     meta[(size_t)e * 2] = lse[at];
     meta[(size_t)e * 2 + 1] = delta[at];
   }
@@ -380,8 +386,8 @@ template <int D>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, int T, int hq, int hkv,
-    int block, float sl, float scale, int g0, int ng, int nb,
+    const float* __restrict__ lse, const float* __restrict__ delta, SeqMap sq, int hq,
+    int hkv, int block, float sl, float scale, int g0, int ng, int nb,
     const int32_t* __restrict__ list_offsets, const uint16_t* __restrict__ dense_rows,
     const float* __restrict__ dense_meta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv) {
@@ -400,7 +406,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   const int g = g0 + gi;
   const int kc0 = j * block + wx * 32 * kKvTiles;
   const int u = kc0 + tile * 32 + n;                  // this lane's key
-  const int kend = (j + 1) * block;
+  // a partial last block, or a block past the end of a shorter packed sequence
+  const int kend = min((j + 1) * block, sq.len(b));
+  if (kc0 >= kend) return;
+  const int tok0 = sq.tok0(b);
   const bool kvalid = u < kend;
   const int list = (b * ng + gi) * nb + j;
   const int hbeg = list_offsets ? list_offsets[list] : 0;
@@ -409,7 +418,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   const int nrows = nhist + (kend - kc0) * G;
   // the K (wave P) or V (wave dS) row of this lane's key: the B operand, lane = key
   bf16x8_t bkv[KS];
-  load_row_operand<D>(bkv, (role_ds ? v : k) + (((size_t)b * T + (kvalid ? u : 0)) * hkv + g) * D,
+  load_row_operand<D>(bkv,
+                      (role_ds ? v : k) + (((size_t)tok0 + (kvalid ? u : kc0)) * hkv + g) * D,
                       kvalid);
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -427,8 +437,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   constexpr int NC = CHUNKS / kKvThreads;
   static_assert(CHUNKS % kKvThreads == 0, "every thread moves whole chunks");
   const int gshift = __builtin_ctz((unsigned)G);   // G is a power of two
-  const int row_base = (b * T) * hq + g * G;        // row index of (b, t=0, head g*G)
-  const int meta_base = (b * hq + g * G) * T;       // lse/delta index of (b, g*G, t=0)
+  const size_t row_base = (size_t)tok0 * hq + g * G;   // row of (b, t = 0, head g*G)
+  const size_t meta_base = sq.lrow(b, g * G, hq);     // lse/delta of (b, g*G, t = 0)
+  const int lhs = sq.lhead();                          // lse stride between heads
   int crow[NC], ccol[NC];
   bool cdo[NC];
 #pragma unroll
@@ -444,16 +455,16 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     int t;
   };
   // the q (dO) row of current row r >= nhist (clamped to the last row past the end)
-  auto cur_row = [&](int r) -> int {
+  auto cur_row = [&](int r) -> size_t {
     const int rc = min(r, nrows - 1) - nhist;
-    return row_base + (kc0 + (rc >> gshift)) * hq + (rc & (G - 1));
+    return row_base + (size_t)(kc0 + (rc >> gshift)) * hq + (rc & (G - 1));
   };
   auto fetch_rows = [&](int r0, Rows& rd) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int r = r0 + crow[c];
       const uint16_t* hsrc = dense_rows + ((size_t)(hbeg + r) * 2 + cdo[c]) * D;
-      const uint16_t* csrc = (cdo[c] ? dout : q) + (size_t)cur_row(r) * D;
+      const uint16_t* csrc = (cdo[c] ? dout : q) + cur_row(r) * D;
       rd.c[c] = *reinterpret_cast<const u32x4_t*>((r < nhist ? hsrc : csrc) + ccol[c]);
     }
     const int r = r0 + (threadIdx.x & 31);
@@ -464,7 +475,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
       dv0 = m[1];
     } else {
       const int rc = min(r, nrows - 1) - nhist;
-      const int at = meta_base + (rc & (G - 1)) * T + kc0 + (rc >> gshift);
+      const size_t at = meta_base + (size_t)(rc & (G - 1)) * lhs + kc0 + (rc >> gshift);
       lv = lse[at];
       dv0 = delta[at];
     }
@@ -592,7 +603,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
 
   if (!kvalid) return;
   const float os = role_ds ? scale : 1.f;
-  uint16_t* orow = (role_ds ? dk : dv) + (((size_t)b * T + u) * hkv + g) * D + hf * 4;
+  uint16_t* orow = (role_ds ? dk : dv) + (((size_t)tok0 + u) * hkv + g) * D + hf * 4;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -614,9 +625,9 @@ bool bwd_supported(const Shape& s) { return kBwdWaves % s.G() == 0; }
 
 hipError_t launch_bwd_delta(const Shape& s, const uint16_t* out, const uint16_t* dout,
                             float* delta, hipStream_t st) {
-  const long rows = (long)s.b * s.T * s.hq;
+  const long rows = (s.cu ? (long)s.total : (long)s.b * s.T) * s.hq;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
-                     out, dout, s.T, s.hq, s.d, rows, delta);
+                     out, dout, s.seqs(), s.hq, s.d, rows, delta);
   return hipGetLastError();
 }
 
@@ -629,8 +640,8 @@ hipError_t launch_bwd_dq_history(const Shape& s, const uint16_t* q, const uint16
   const float sl = scale * kLog2e;
 #define MOBA_DQH(DD)                                                                       \
   hipLaunchKernelGGL((bwd_dq_kernel<DD, false>), dim3(max_tiles), dim3(kBwdThreads), 0, st, \
-                     q, k, v, dout, lse, delta, s.T, s.hq, s.hkv, s.block, s.topk, sl, scale, \
-                     g0, ng, s.nb(), tiles, tile_count, entries, dq_part, nullptr)
+                     q, k, v, dout, lse, delta, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl,   \
+                     scale, g0, ng, s.nb(), tiles, tile_count, entries, dq_part, nullptr)
   if (s.d == 128) MOBA_DQH(128);
   else MOBA_DQH(64);
 #undef MOBA_DQH
@@ -646,8 +657,8 @@ hipError_t launch_bwd_dq_current(const Shape& s, const uint16_t* q, const uint16
   dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng);
 #define MOBA_DQC(DD)                                                                       \
   hipLaunchKernelGGL((bwd_dq_kernel<DD, true>), grid, dim3(kBwdThreads), 0, st, q, k, v,     \
-                     dout, lse, delta, s.T, s.hq, s.hkv, s.block, s.topk, sl, scale, g0, ng,  \
-                     s.nb(), nullptr, nullptr, nullptr, const_cast<float*>(dq_part), dq)
+                     dout, lse, delta, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, scale, g0, \
+                     ng, s.nb(), nullptr, nullptr, nullptr, const_cast<float*>(dq_part), dq)
   if (s.d == 128) MOBA_DQC(128);
   else MOBA_DQC(64);
 #undef MOBA_DQC
@@ -662,7 +673,7 @@ hipError_t launch_bwd_densify(const Shape& s, const uint16_t* q, const uint16_t*
   if (max_tiles <= 0) return hipSuccess;
 #define MOBA_DENSE(DD)                                                                     \
   hipLaunchKernelGGL((bwd_densify_kernel<DD>), dim3(max_tiles), dim3(256), 0, st, q, dout,  \
-                     lse, delta, s.T, s.hq, s.G(), g0, ng, s.nb(), tiles, tile_count,        \
+                     lse, delta, s.seqs(), s.hq, s.G(), g0, ng, s.nb(), tiles, tile_count,   \
                      entries, rows, meta)
   if (s.d == 128) MOBA_DENSE(128);
   else MOBA_DENSE(64);
@@ -681,7 +692,7 @@ hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
   dim3 grid((s.block + kpw - 1) / kpw, s.nb(), s.b * ng);
 #define MOBA_KV(DD)                                                                        \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD>), grid, dim3(kKvThreads), 0, st, q, k, v, dout,    \
-                     lse, delta, s.T, s.hq, s.hkv, s.block, sl, scale, g0, ng, s.nb(),        \
+                     lse, delta, s.seqs(), s.hq, s.hkv, s.block, sl, scale, g0, ng, s.nb(),   \
                      list_offsets, dense_rows, dense_meta, dk, dv)
   if (s.d == 128) MOBA_KV(128);
   else MOBA_KV(64);

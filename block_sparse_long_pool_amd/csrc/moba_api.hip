@@ -124,7 +124,8 @@ BwdLayout make_bwd_layout(const Shape& s, int ng) {
     off = align_up(off + bytes);
     return at;
   };
-  L.delta = take((size_t)s.b * s.hq * s.T * sizeof(float));
+  const size_t tokens = s.cu ? (size_t)s.total : (size_t)s.b * s.T;
+  L.delta = take(tokens * s.hq * sizeof(float));
   const size_t nlists = (size_t)s.b * ng * nb;
   const size_t nchunks = moba::index_chunks(s);
   L.n_entries = group_entries(s, ng);
@@ -138,7 +139,7 @@ BwdLayout make_bwd_layout(const Shape& s, int ng) {
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
   L.dense_rows = take((size_t)L.n_entries * 2 * s.d * sizeof(uint16_t));
   L.dense_meta = take((size_t)L.n_entries * 2 * sizeof(float));
-  L.dq_part = take((size_t)s.b * ng * s.G() * s.T * s.KH() * s.d * sizeof(float));
+  L.dq_part = take(group_part_rows(s, ng) * s.d * sizeof(float));
   L.total = off;
   return L;
 }
@@ -323,6 +324,79 @@ int varlen_shape(int nseq, int total, int max_seqlen, int hq, int hkv, int head_
   s.cu = cu;
   s.total = total;
   *out = s;
+  return MOBA_OK;
+}
+
+// backward workspace of a validated shape: all kv-heads at once, *min_bytes one per pass
+size_t bwd_workspace(const Shape& s, size_t* min_bytes) {
+  if (!moba::bwd_supported(s)) return 0;
+  const BwdLayout one = make_bwd_layout(s, 1);
+  if (!bwd_layout_ok(one)) return 0;
+  if (min_bytes) *min_bytes = one.total;
+  for (int ng = s.hkv; ng >= 1; --ng) {
+    const BwdLayout L = make_bwd_layout(s, ng);
+    if (bwd_layout_ok(L)) return L.total;
+  }
+  return one.total;
+}
+
+// the whole backward for a validated shape (a uniform batch or packed sequences)
+int run_backward(const Shape& s, const void* q, const void* k, const void* v,
+                 const void* out, const float* lse, const int32_t* idx, const void* dout,
+                 float scale, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out || !lse || !idx || !dout || !dq || !dk || !dv || !workspace)
+    return MOBA_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
+  if (!moba::bwd_supported(s)) return MOBA_ERR_UNSUPPORTED;
+  const int hkv = s.hkv;
+  int ng = hkv;
+  BwdLayout L = make_bwd_layout(s, ng);
+  while (ng > 1 && (L.total > workspace_bytes || !bwd_layout_ok(L)))
+    L = make_bwd_layout(s, --ng);
+  if (L.total > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  if (!bwd_layout_ok(L)) return MOBA_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  const uint16_t* vb = static_cast<const uint16_t*>(v);
+  const uint16_t* gb = static_cast<const uint16_t*>(dout);
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* dq_part = reinterpret_cast<float*>(ws + L.dq_part);
+  MOBA_TRY(moba::launch_bwd_delta(s, static_cast<const uint16_t*>(out), gb, delta, hs));
+  for (int g0 = 0; g0 < hkv; g0 += ng) {
+    const int ngc = ng < hkv - g0 ? ng : hkv - g0;
+    const int nlc = s.b * ngc * s.nb();
+    const int32_t* list_offsets = nullptr;
+    uint16_t* dense_rows = reinterpret_cast<uint16_t*>(ws + L.dense_rows);
+    float* dense_meta = reinterpret_cast<float*>(ws + L.dense_meta);
+    if (s.KH() > 0) {
+      int32_t* lo = reinterpret_cast<int32_t*>(ws + L.list_offsets);
+      int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
+      int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
+      uint32_t* ent = reinterpret_cast<uint32_t*>(ws + L.entries);
+      MOBA_TRY(moba::launch_index(s, idx, g0, ngc, moba::bwd_tile_rows(),
+                                  reinterpret_cast<int32_t*>(ws + L.chunk_counts),
+                                  reinterpret_cast<int32_t*>(ws + L.list_count), lo,
+                                  tile_offsets, tiles, ent, L.n_entries, hs));
+      const BwdLayout Lc = make_bwd_layout(s, ngc);
+      MOBA_TRY(moba::launch_bwd_dq_history(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
+                                           tiles, tile_offsets + nlc, (int)Lc.max_tiles,
+                                           ent, dq_part, hs));
+      MOBA_TRY(moba::launch_bwd_densify(s, qb, gb, lse, delta, g0, ngc, tiles,
+                                        tile_offsets + nlc, (int)Lc.max_tiles, ent,
+                                        dense_rows, dense_meta, hs));
+      list_offsets = lo;
+    }
+    MOBA_TRY(moba::launch_bwd_dq_current(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
+                                         dq_part, static_cast<uint16_t*>(dq), hs));
+    MOBA_TRY(moba::launch_bwd_dkdv(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
+                                   list_offsets, dense_rows, dense_meta,
+                                   static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                                   hs));
+  }
   return MOBA_OK;
 }
 
@@ -518,16 +592,7 @@ size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
                                      size_t* min_bytes) {
   if (min_bytes) *min_bytes = 0;
   if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
-  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
-  if (!moba::bwd_supported(s) || seqlen % block != 0) return 0;
-  const BwdLayout one = make_bwd_layout(s, 1);
-  if (!bwd_layout_ok(one)) return 0;
-  if (min_bytes) *min_bytes = one.total;
-  for (int ng = hkv; ng >= 1; --ng) {
-    const BwdLayout L = make_bwd_layout(s, ng);
-    if (bwd_layout_ok(L)) return L.total;
-  }
-  return one.total;
+  return bwd_workspace(Shape{batch, seqlen, hq, hkv, head_dim, block, topk}, min_bytes);
 }
 
 int moba_backward(const void* q, const void* k, const void* v, const void* out,
@@ -535,61 +600,37 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
                   int seqlen, int hq, int hkv, int head_dim, int block, int topk,
                   float scale, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  const int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
   if (st != MOBA_OK) return st;
-  if (!q || !k || !v || !out || !lse || !idx || !dout || !dq || !dk || !dv || !workspace)
-    return MOBA_ERR_INVALID_ARG;
-  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
-  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
-  if (!moba::bwd_supported(s) || seqlen % block != 0) return MOBA_ERR_UNSUPPORTED;
-  int ng = hkv;
-  BwdLayout L = make_bwd_layout(s, ng);
-  while (ng > 1 && (L.total > workspace_bytes || !bwd_layout_ok(L)))
-    L = make_bwd_layout(s, --ng);
-  if (L.total > workspace_bytes) return MOBA_ERR_WORKSPACE;
-  if (!bwd_layout_ok(L)) return MOBA_ERR_UNSUPPORTED;
+  return run_backward(Shape{batch, seqlen, hq, hkv, head_dim, block, topk}, q, k, v, out,
+                      lse, idx, dout, scale, dq, dk, dv, workspace, workspace_bytes, stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const uint16_t* qb = static_cast<const uint16_t*>(q);
-  const uint16_t* kb = static_cast<const uint16_t*>(k);
-  const uint16_t* vb = static_cast<const uint16_t*>(v);
-  const uint16_t* gb = static_cast<const uint16_t*>(dout);
-  float* delta = reinterpret_cast<float*>(ws + L.delta);
-  float* dq_part = reinterpret_cast<float*>(ws + L.dq_part);
-  MOBA_TRY(moba::launch_bwd_delta(s, static_cast<const uint16_t*>(out), gb, delta, hs));
-  for (int g0 = 0; g0 < hkv; g0 += ng) {
-    const int ngc = ng < hkv - g0 ? ng : hkv - g0;
-    const int nlc = s.b * ngc * s.nb();
-    const int32_t* list_offsets = nullptr;
-    uint16_t* dense_rows = reinterpret_cast<uint16_t*>(ws + L.dense_rows);
-    float* dense_meta = reinterpret_cast<float*>(ws + L.dense_meta);
-    if (s.KH() > 0) {
-      int32_t* lo = reinterpret_cast<int32_t*>(ws + L.list_offsets);
-      int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
-      int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
-      uint32_t* ent = reinterpret_cast<uint32_t*>(ws + L.entries);
-      MOBA_TRY(moba::launch_index(s, idx, g0, ngc, moba::bwd_tile_rows(),
-                                  reinterpret_cast<int32_t*>(ws + L.chunk_counts),
-                                  reinterpret_cast<int32_t*>(ws + L.list_count), lo,
-                                  tile_offsets, tiles, ent, L.n_entries, hs));
-      const BwdLayout Lc = make_bwd_layout(s, ngc);
-      MOBA_TRY(moba::launch_bwd_dq_history(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
-                                           tiles, tile_offsets + nlc, (int)Lc.max_tiles,
-                                           ent, dq_part, hs));
-      MOBA_TRY(moba::launch_bwd_densify(s, qb, gb, lse, delta, g0, ngc, tiles,
-                                        tile_offsets + nlc, (int)Lc.max_tiles, ent,
-                                        dense_rows, dense_meta, hs));
-      list_offsets = lo;
-    }
-    MOBA_TRY(moba::launch_bwd_dq_current(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
-                                         dq_part, static_cast<uint16_t*>(dq), hs));
-    MOBA_TRY(moba::launch_bwd_dkdv(s, qb, kb, vb, gb, lse, delta, scale, g0, ngc,
-                                   list_offsets, dense_rows, dense_meta,
-                                   static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
-                                   hs));
-  }
-  return MOBA_OK;
+size_t moba_backward_varlen_workspace_bytes(int nseq, int total, int max_seqlen, int hq,
+                                            int hkv, int head_dim, int block, int topk,
+                                            size_t* min_bytes) {
+  if (min_bytes) *min_bytes = 0;
+  Shape s{};
+  static const int32_t kDummy = 0;   // only the null-ness of cu matters for sizing
+  if (varlen_shape(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk, 1.f, &kDummy,
+                   &s) != MOBA_OK)
+    return 0;
+  return bwd_workspace(s, min_bytes);
+}
+
+int moba_backward_varlen(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const int32_t* idx, const void* dout,
+                         const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                         int hq, int hkv, int head_dim, int block, int topk, float scale,
+                         void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return MOBA_ERR_INVALID_ARG;
+  Shape s{};
+  const int st = varlen_shape(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk, scale,
+                              cu_seqlens, &s);
+  if (st != MOBA_OK) return st;
+  return run_backward(s, q, k, v, out, lse, idx, dout, scale, dq, dk, dv, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

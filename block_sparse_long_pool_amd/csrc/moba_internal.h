@@ -79,6 +79,8 @@ struct SeqMap {
   __device__ __forceinline__ size_t lrow(int b, int h, int hq) const {
     return cu ? (size_t)h * total + cu[b] : ((size_t)b * hq + h) * T;
   }
+  // stride between the lse rows of two heads of one sequence
+  __device__ __forceinline__ int lhead() const { return cu ? total : T; }
   // row of (b, head hh of the ngq heads of a kv-head group, t = 0) in the history
   // partials, [b, ngq, T] or packed [ngq, total]; the token stride is 1
   __device__ __forceinline__ size_t prow(int b, int hh, int ngq) const {

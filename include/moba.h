@@ -153,8 +153,8 @@ size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
  *   dk, dv                   [b, T, hkv, d] bf16, written (every element)
  * Accumulation is float32; dq sums fp32 per-history-block parts in slot order and dk,
  * dv are each summed by one workgroup in a fixed row order: deterministic.  Shape
- * limits are moba_forward's plus G = hq / hkv in {1, 2, 4, 8} and seqlen a multiple of
- * block (MOBA_ERR_UNSUPPORTED otherwise).  `workspace` must hold at least the minimum of
+ * limits are moba_forward's (a partial last block included) plus G = hq / hkv in
+ * {1, 2, 4, 8} (MOBA_ERR_UNSUPPORTED otherwise).  `workspace` must hold at least the minimum of
  * moba_backward_workspace_bytes and be 256-byte aligned (MOBA_ERR_WORKSPACE,
  * MOBA_ERR_INVALID_ARG).  Enqueued on `stream` without synchronising. */
 int moba_backward(const void* q, const void* k, const void* v, const void* out,
@@ -162,6 +162,21 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
                   int seqlen, int hq, int hkv, int head_dim, int block, int topk,
                   float scale, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* Backward of moba_forward_varlen (packed sequences, each with its own block grid):
+ * the same gradients as moba_backward run on each sequence alone.  q, k, v, out, dout,
+ * dq, dk, dv in the packed [total, heads, d] layout; lse [hq, total]; idx
+ * [hq, total, topk]; cu_seqlens as for moba_forward_varlen (DEVICE, unchecked
+ * contents).  Limits as moba_forward_varlen's plus moba_backward's G rule. */
+size_t moba_backward_varlen_workspace_bytes(int nseq, int total, int max_seqlen, int hq,
+                                            int hkv, int head_dim, int block, int topk,
+                                            size_t* min_bytes);
+int moba_backward_varlen(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const int32_t* idx, const void* dout,
+                         const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                         int hq, int hkv, int head_dim, int block, int topk, float scale,
+                         void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Packed variable-length prefill: several sequences of different lengths in one call,

@@ -49,9 +49,11 @@ def test_check_args_codes(moba):
     assert moba.check_args(1, 128, 1, 1, 64, 24, 1, 1.0) == E_UNS          # block % 16
     assert moba.check_args(1, 130, 1, 1, 64, 16, 1, 1.0) == ok             # partial last block
     assert moba.check_args(1, 16 * 2049, 1, 1, 64, 16, 1, 1.0) == E_UNS    # > 2048 blocks
-    # the backward needs whole blocks
-    assert moba.backward_workspace_bytes(1, 130, 1, 1, 64, 16, 2) == (0, 0)
+    # the backward takes a partial last block as well
+    assert moba.backward_workspace_bytes(1, 130, 1, 1, 64, 16, 2)[0] > 0
     assert moba.backward_workspace_bytes(1, 128, 1, 1, 64, 16, 2)[0] > 0
+    assert moba.backward_varlen_workspace_bytes(2, 300, 200, 4, 2, 64, 16, 3)[0] > 0
+    assert moba.backward_varlen_workspace_bytes(2, 300, 400, 4, 2, 64, 16, 3) == (0, 0)
     assert moba.check_args(1, 128, 1, 1, 64, 16, 34, 1.0) == E_UNS         # topk > 33
     assert moba.check_args(1, 128, 1, 1, 64, 16, 33, 1.0) == 0
     assert moba.check_args(1, 128, 1, 1, 64, 16, 2, -1.0) == E_UNS         # scale <= 0
