@@ -491,14 +491,20 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
   const float ltot = pair_sum(st.l[qt]);
   if (!valid) return;
   const float inv = 1.f / ltot;
+  // lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row; they are stored as
+  // the contiguous half hf of the row (position hf*D/2 + dt*16 + ii*4 + r), so each
+  // lane writes, and the merge reads, whole 16-byte chunks
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int i2 = 0; i2 < 2; ++i2) {
       const f32x16_t& o = st.o[qt][dt];
-      const u32x2_t w = {pack_bf16x2(o[ii * 4] * inv, o[ii * 4 + 1] * inv),
-                         pack_bf16x2(o[ii * 4 + 2] * inv, o[ii * 4 + 3] * inv)};
-      *reinterpret_cast<u32x2_t*>(po + dt * 32 + ii * 8 + hf * 4) = w;
+      const int a = 8 * i2;
+      const u32x4_t w = {pack_bf16x2(o[a] * inv, o[a + 1] * inv),
+                         pack_bf16x2(o[a + 2] * inv, o[a + 3] * inv),
+                         pack_bf16x2(o[a + 4] * inv, o[a + 5] * inv),
+                         pack_bf16x2(o[a + 6] * inv, o[a + 7] * inv)};
+      *reinterpret_cast<u32x4_t*>(po + hf * (D / 2) + dt * 16 + i2 * 8) = w;
     }
   if (hf == 0) *pl = (st.m[qt] + __log2f(ltot)) * 0.69314718055994530942f;
 }
@@ -550,17 +556,14 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[dt][ii][r] = st.o[qt][dt][ii * 4 + r] * wc;
   for (int s0 = 0; s0 < nh; s0 += CH) {
-    u32x2_t x[CH][D / 32][4];
+    u32x4_t x[CH][D / 16];     // the lane's half of each part row (see store_partial)
     float w[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int sc = min(s0 + u, nh - 1);
-      const uint16_t* ps = po + (size_t)sc * D + hf * 4;
+      const uint16_t* ps = po + (size_t)sc * D + hf * (D / 2);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          x[u][dt][ii] = *reinterpret_cast<const u32x2_t*>(ps + dt * 32 + ii * 8);
+      for (int c = 0; c < D / 16; ++c) x[u][c] = *reinterpret_cast<const u32x4_t*>(ps + c * 8);
       w[u] = s0 + u < nh ? expf(pl[sc] - L) : 0.f;
     }
 #pragma unroll
@@ -569,7 +572,8 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const u32x2_t y = x[u][dt][ii];
+          const u32x4_t& xc = x[u][dt * 2 + ii / 2];
+          const u32x2_t y = {xc[(ii & 1) * 2], xc[(ii & 1) * 2 + 1]};
           const float xf[4] = {__uint_as_float(y[0] << 16), __uint_as_float(y[0] & 0xffff0000u),
                                __uint_as_float(y[1] << 16), __uint_as_float(y[1] & 0xffff0000u)};
 #pragma unroll
