@@ -415,20 +415,28 @@ struct Walker {
     __syncthreads();
   }
 
-  __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT]) {
+  // The first loads, which depend on nothing the caller computes, issued before the
+  // caller's query loads so that their latencies overlap: K(0), and for group 0 the
+  // subtile of its half-step 1 (V(0)), for group 1 that of half-step 0 (K(1)), which
+  // it stages in the prologue because it waits that half-step out.
+  __device__ __forceinline__ void begin() {
     to.init(rs);
     nsub = (key_end - key_begin + KN - 1) / KN;
-    // prologue: K(0) into LDS.  Group 1 waits out half-step 0, so it stages its slices
-    // of that half-step's subtile (K(1)) now.  Then the registers for the first two
-    // phases: the subtiles of half-steps grp and grp + 1.
     tile_load<D>(bank[0], to, kbase + (size_t)kb(0) * rs, rs, nvalid(0));
+    stage_load(bank[1], grp ? 0 : 1);
+  }
+
+  __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT]) {
+    // prologue: K(0) into LDS (and K(1) for group 1), then the registers of the first
+    // two phases: the subtiles of half-steps grp and grp + 1
     tile_store<D, L::KS>(bank[0], kbuf(0));
     if (grp) {
+      for (int c = 0; c < NC; ++c) stage_store(bank[1], c, 0);
+      stage_load(bank[0], 1);
+      stage_load(bank[1], 2);
+    } else {
       stage_load(bank[0], 0);
-      for (int c = 0; c < NC; ++c) stage_store(bank[0], c, 0);
     }
-    stage_load(bank[0], grp);
-    stage_load(bank[1], grp + 1);
     __syncthreads();
     if (grp) __syncthreads();            // group 1 trails by one half-step
     Scores sa, sb;
@@ -453,13 +461,15 @@ struct Walker {
 
 // The wave's rows over keys [key_begin, key_end) of one kv-head; subtiles whose last
 // key exceeds diag_from (the smallest query position of the workgroup) or key_end are
-// masked.
-template <int D, int QT>
+// masked.  load_queries() fills st (query operands and the initial state); it runs
+// after the walker's first K/V loads are issued.
+template <int D, int QT, typename QueryLoad>
 __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
                                              const uint16_t* __restrict__ kbase,
                                              const uint16_t* __restrict__ vbase, size_t rs,
                                              int key_begin, int key_end, float sl,
-                                             int diag_from, const int (&tpos)[QT]) {
+                                             int diag_from, const int (&tpos)[QT],
+                                             QueryLoad&& load_queries) {
   Walker<D, QT> w;
   w.lds = lds;
   w.kbase = kbase;
@@ -479,6 +489,8 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
 #else
   w.grp = wave / (kAttnWaves / 2);
 #endif
+  w.begin();
+  load_queries();
   w.run(st, tpos);
 }
 
@@ -628,25 +640,27 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
   int tq[QT], hlq[QT], slq[QT], tpos[QT];
   bool vq[QT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int e = tl.y + (wave * QT + qt) * 32 + n;
-    vq[qt] = e < tl.z;
-    const uint32_t ent = vq[qt] ? entries[e] : 0u;
-    slq[qt] = (int)(ent & 31u);
-    const int rr = (int)(ent >> 5);
-    tq[qt] = rr / G;
-    hlq[qt] = rr % G;
-    tpos[qt] = 0x7fffffff;    // history keys all precede the query
-    const uint16_t* qrow = q + ((size_t)((size_t)tok0 + tq[qt]) * hq + g * G + hlq[qt]) * D;
-    load_q(st, qt, qrow, vq[qt]);
-  }
-  state_init(st);
+  for (int qt = 0; qt < QT; ++qt) tpos[qt] = 0x7fffffff;    // history keys all precede
   const size_t rs = (size_t)hkv * D;
   const uint16_t* kbase = k + ((size_t)tok0 * hkv + g) * D;
   const uint16_t* vbase = v + ((size_t)tok0 * hkv + g) * D;
   const int key_begin = j * block;
   attend_range<D, QT>(st, lds, kbase, vbase, rs, key_begin, key_begin + block, sl,
-                      0x7fffffff, tpos);
+                      0x7fffffff, tpos, [&] {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int e = tl.y + (wave * QT + qt) * 32 + n;
+      vq[qt] = e < tl.z;
+      const uint32_t ent = vq[qt] ? entries[e] : 0u;
+      slq[qt] = (int)(ent & 31u);
+      const int rr = (int)(ent >> 5);
+      tq[qt] = rr / G;
+      hlq[qt] = rr % G;
+      const uint16_t* qrow = q + ((size_t)((size_t)tok0 + tq[qt]) * hq + g * G + hlq[qt]) * D;
+      load_q(st, qt, qrow, vq[qt]);
+    }
+    state_init(st);
+  });
   const int ngq = ng * G;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -702,14 +716,18 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
     for (int qt = 0; qt < QT; ++qt) {
       tpos[qt] = t0 + (tsub * QT + qt) * 32 + n;
       vq[qt] = active && tpos[qt] < t_end;
-      const uint16_t* qrow = q + ((size_t)((size_t)tok0 + (vq[qt] ? tpos[qt] : 0)) * hq +
-                                  g * G + (active ? hl : 0)) * D;
-      load_q(st, qt, qrow, vq[qt]);
     }
-    state_init(st);
     // waves without a head this round run on zero queries: every wave takes part in
     // every phase and barrier of the walker
-    attend_range<D, QT>(st, lds, kbase, vbase, rs, c * block, t_end, sl, t0, tpos);
+    attend_range<D, QT>(st, lds, kbase, vbase, rs, c * block, t_end, sl, t0, tpos, [&] {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const uint16_t* qrow = q + ((size_t)((size_t)tok0 + (vq[qt] ? tpos[qt] : 0)) * hq +
+                                    g * G + (active ? hl : 0)) * D;
+        load_q(st, qt, qrow, vq[qt]);
+      }
+      state_init(st);
+    });
     if (active) {
       const int nh = min(c, topk - 1);   // history slots of every row of this block
 #pragma unroll
