@@ -14,7 +14,9 @@
 //                      tiles (the inverted index's gathered rows) write an fp32 partial
 //                      per (row, slot); current-block tiles add the row's partials to
 //                      their own and write dq.
-//   bwd_dkdv_kernel    per 256 keys of one block: every row that attends them (the
+//   bwd_densify_kernel the Q and dO rows (and lse, D) of every index entry, copied
+//                      into entry order so that the dK/dV kernel reads them contiguously
+//   bwd_dkdv_kernel    per 128 keys of one block: every row that attends them (the
 //                      block's history list, then the block's own rows causally) in
 //                      groups of 32: S = Q K^T, dP = dO V^T, P, dS, then
 //                      dV^T += dO^T P and dK^T += Q^T dS; dK and dV stay in registers
