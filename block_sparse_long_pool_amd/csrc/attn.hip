@@ -482,13 +482,7 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
   // waves w and w + kAttnWaves/2 share a SIMD (waves are dealt to SIMDs in turn), so
   // the halves of the workgroup are the two groups
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#if MOBA_ATTN_NO_PINGPONG
-  w.grp = 0 * wave;
-#elif MOBA_ATTN_GROUP_BY_PARITY
-  w.grp = wave & 1;
-#else
   w.grp = wave / (kAttnWaves / 2);
-#endif
   w.begin();
   load_queries();
   w.run(st, tpos);
