@@ -377,6 +377,36 @@ def main(argv=None):
             "note": "moba_forward_varlen: the main inputs' tokens as six packed requests",
         }
         print(f"[bench] varlen {vms:.2f} ms", file=sys.stderr, flush=True)
+        if not a.no_backward:
+            # the packed backward of the same requests (selection of the forward above)
+            from workloads import make_output_grad
+            vdout = to_torch_bf16(make_output_grad(w), dev).view(total, w.hq, w.head_dim)
+            full_vb, _ = moba.backward_varlen_workspace_bytes(
+                len(VARLEN_LENGTHS), total, max(VARLEN_LENGTHS), w.hq, w.hkv, w.head_dim,
+                VARLEN_BLOCK, VARLEN_TOPK)
+            vbws = torch.empty(full_vb, dtype=torch.uint8, device=dev)
+
+            def vbstep():
+                return moba.backward_varlen(qv, kv, vv, vo, vl, vi, vdout, cu, VARLEN_BLOCK,
+                                            VARLEN_TOPK, w.sm_scale, workspace=vbws)
+
+            vbstep()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n_var):
+                vbstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            vbms = e0.elapsed_time(e1) / n_var
+            vbflop = 10 * w.head_dim * w.hq * vpairs
+            result["varlen"].update({
+                "backward_ms": vbms,
+                "backward_effective_tflops": vbflop / (vbms * 1e-3) / 1e12,
+                "backward_note": "moba_backward_varlen of the same requests, dout i.i.d. "
+                                 "N(0,1); 10 d FLOP per attended pair",
+            })
+            print(f"[bench] varlen backward {vbms:.2f} ms", file=sys.stderr, flush=True)
+            del vbws, vdout
         del vws, vo, vl, vi
     if not a.no_backward:
         # the training backward of the same layer (selection held fixed): context for
