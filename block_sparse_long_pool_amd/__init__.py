@@ -267,7 +267,8 @@ def forward_varlen(q, k, v, cu_seqlens, block: int, topk: int, scale: float | No
     grid.  q [total, Hq, d], k and v [total, Hkv, d] bf16 on the GPU; cu_seqlens: the
     cumulative lengths [nseq + 1] (int, any device), checked here on the host.
     Returns (out [total, Hq, d] bf16, lse [Hq, total] fp32, idx [Hq, total, topk] int32,
-    block ids counted within each sequence)."""
+    block ids counted within each sequence).  The call copies cu_seqlens to the device,
+    so unlike ``forward`` it is not meant for graph capture."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 3)

@@ -20,7 +20,11 @@
  * returns without synchronising.  The caller owns every buffer; the library allocates
  * no device memory and keeps no state between calls, so calls on different streams
  * with separate buffers may run concurrently.  Calls that share a workspace must be
- * ordered on one stream.
+ * ordered on one stream.  No entry point calls a HIP memset, copy, allocation or
+ * synchronisation, and every workspace word a kernel reads is written earlier in the
+ * same call, so a call may be captured into a HIP graph (hipStreamBeginCapture on
+ * `stream`) and replayed; the _profile and _timed forms record events and the
+ * _profile form synchronises, so only the plain forms are meant for capture.
  *
  * Layouts (contiguous, row-major; b = batch, T = seqlen, d = head_dim,
  * nb = ceil(T / block), G = hq / hkv, query head h reads kv-head h / G):
