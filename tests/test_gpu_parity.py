@@ -213,6 +213,9 @@ SMALL = [
     ("topk1", small_workload("topk1", 1, 4, 2, 128, 2048, 256, 1, "iid", 12)),
     ("dense", small_workload("dense", 1, 4, 1, 64, 1024, 128, 8, "iid", 13)),
     ("k_over_nb", small_workload("k_over_nb", 1, 2, 2, 128, 768, 256, 9, "iid", 14)),
+    # G = 3 (does not divide the eight waves: heads in rounds) and G = 16 (two rounds)
+    ("g3", small_workload("g3", 1, 6, 2, 128, 2048, 128, 4, "offset", 16)),
+    ("g16_d64", small_workload("g16_d64", 1, 16, 1, 64, 1024, 64, 5, "offset", 17)),
 ]
 
 
