@@ -158,7 +158,7 @@ def main(argv=None):
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE "
               f"{world}): the MoBA layer shards by kv-head with no communication, so "
               "the figure at N GPUs is N times the one-GPU figure on 1/N of the heads; "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+              "this script measures one GPU.", file=sys.stderr)
         return 2
 
     import torch

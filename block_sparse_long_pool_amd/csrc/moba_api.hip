@@ -184,7 +184,7 @@ const char* moba_strerror(int status) {
   switch (status) {
     case MOBA_OK: return "success";
     case MOBA_ERR_INVALID_ARG: return "invalid argument";
-    case MOBA_ERR_UNSUPPORTED: return "shape or value not supported by this build";
+    case MOBA_ERR_UNSUPPORTED: return "shape or value not supported by this library";
     case MOBA_ERR_WORKSPACE: return "workspace too small";
     case MOBA_ERR_HIP: return "HIP launch or runtime error";
     default: return "unknown status";

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   MOBA_OK = 0,
   MOBA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, hq % hkv != 0 ... */
-  MOBA_ERR_UNSUPPORTED = -2, /* valid MoBA shape this build does not run */
+  MOBA_ERR_UNSUPPORTED = -2, /* valid MoBA shape this library does not run */
   MOBA_ERR_WORKSPACE = -3,   /* workspace smaller than the minimum */
   MOBA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } moba_status;
