@@ -25,6 +25,6 @@ from .moba_oracle import (  # noqa: F401
     num_blocks, centroids, gate_scores_rows, select_rows, select_blocks,
     attended_keys, attend_row, attend_rows, attend_parts_row, merge_parts,
     moba_forward, moba_rows, attended_pairs, attend_row_grad, moba_backward,
-    moba_forward_varlen, key_short_conv, moba_backward_varlen,
+    moba_forward_varlen, key_short_conv, moba_backward_varlen, decode_attention,
 )
 from .bruteforce import moba_bruteforce, moba_bruteforce_packed  # noqa: F401

@@ -339,3 +339,27 @@ def moba_backward_varlen(Q, K, V, dO, cu, B: int, topk: int, scale: float):
                                    B, topk, scale)
         dQ[a:e], dK[a:e], dV[a:e] = gq[0], gk[0], gv[0]
     return dQ, dK, dV
+
+
+# ------------------------------------------------------------- full-attention decode
+# After a MoBA prefill, generation switches to full attention (paper summary page,
+# "Limitations"; README bullet "Seamlessly Transition between Full and Sparse
+# Attention").  Reading: the n new query tokens are the last n positions of the key
+# sequence, and each attends every key up to its own position.
+
+def decode_attention(Q, K, V, scale: float):
+    """Q [b, n, Hq, d], K and V [b, Tk, Hkv, d] float64 (Tk >= n): query i sits at
+    position Tk - n + i and attends keys 0 .. Tk - n + i.  Returns out [b, n, Hq, d]
+    and lse [b, Hq, n]."""
+    b, n, hq, d = Q.shape
+    Tk, hkv = K.shape[1], K.shape[2]
+    G = hq // hkv
+    out = np.empty_like(Q)
+    lse = np.empty((b, hq, n))
+    for bi in range(b):
+        for h in range(hq):
+            Kg, Vg = K[bi, :, h // G], V[bi, :, h // G]
+            for i in range(n):
+                keys = np.arange(Tk - n + i + 1)
+                out[bi, i, h], lse[bi, h, i] = attend_row(Q[bi, i, h], Kg, Vg, keys, scale)
+    return out, lse
