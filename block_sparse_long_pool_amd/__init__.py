@@ -61,6 +61,8 @@ _SIGS = {
                                  _vp, _vp, _vp, _sz, _vp]),
     "moba_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                            _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moba_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moba_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "moba_strerror": (ctypes.c_char_p, [_i]),
     "moba_stage_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moba_pool_centroids": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -248,6 +250,53 @@ def dense_forward(q, k, v, scale: float | None = None, out=None, lse=None):
                                     d, float(scale), out.data_ptr(), lse.data_ptr(),
                                     _stream_ptr())
     _raise(st, "moba_dense_forward")
+    return out, lse
+
+
+def decode_workspace_bytes(batch, n_new, kv_len, hq, hkv, head_dim) -> int:
+    """Workspace bytes of ``decode`` (0 when the shape is not supported)."""
+    return int(lib.moba_decode_workspace_bytes(batch, n_new, kv_len, hq, hkv, head_dim))
+
+
+def decode(q, k, v, scale: float | None = None, workspace=None, out=None, lse=None):
+    """Full-attention decode after a prefill (the hand-off from a MoBA prefill to
+    generation).  q [b, n_new, Hq, d] holds the new tokens, which are the last n_new
+    positions of the cache k, v [b, kv_len, Hkv, d] (bf16); new token i attends keys
+    0 .. kv_len - n_new + i.  Returns (out bf16 [b, n_new, Hq, d], lse fp32
+    [b, Hq, n_new])."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    b, n, hq, d = q.shape
+    Tk, hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != b or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(b, n, Tk, hq, hkv, d)
+        if nbytes == 0:
+            _raise(MOBA_ERR_UNSUPPORTED if hq % hkv == 0 and 1 <= n <= Tk
+                   else MOBA_ERR_INVALID_ARG, "moba_decode_workspace_bytes")
+        workspace = _alloc_workspace(nbytes, q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (b, hq, n):
+        raise ValueError("output shapes do not match the inputs")
+    with torch.cuda.device(q.device):
+        st = lib.moba_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, n, Tk, hq, hkv, d,
+                             float(scale), out.data_ptr(), lse.data_ptr(),
+                             workspace.data_ptr(), workspace.numel(), _stream_ptr())
+    _raise(st, "moba_decode")
     return out, lse
 
 

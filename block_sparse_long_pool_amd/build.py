@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoba.so")
 SOURCES = ["pool.hip", "gate.hip", "index.hip", "attn.hip", "attn_bwd.hip", "conv.hip",
-           "moba_api.hip"]
+           "decode.hip", "moba_api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

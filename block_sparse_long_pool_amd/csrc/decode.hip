@@ -1,0 +1,250 @@
+// Full-attention decode after a prefill: n new query tokens, which are the last n
+// positions of the key sequence, attend every key up to their own position.  After a
+// MoBA prefill, generation switches to full attention ("MoBA: Mixture of Block
+// Attention for Long-Context LLMs", paper summary page, "Limitations"; README bullet
+// "Seamlessly Transition between Full and Sparse Attention").
+//
+// HBM-bound: every key and value of the cache is read once.  The G*n query rows of a
+// kv-head (G query heads per kv-head, n new tokens; G*n <= 32) form one 32-row MFMA
+// tile, so each key row read serves all of them.  The key range is split over many
+// single-wavefront workgroups (split-K), each writing an fp32 (o, lse) partial for its
+// rows; a second kernel merges the partials by log-sum-exp.
+//
+// Per 32-key subtile a wavefront reads the K rows straight into MFMA A operands
+// (lane = key), computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16, lane = query), runs
+// the online softmax in the log2 domain, stages the V rows in LDS and reads V^T with
+// the transpose read ds_read_b64_tr_b16 in the key order the score registers hold, so
+// that O^T += V^T P^T takes P^T straight from registers.  Latency is hidden by many
+// resident wavefronts rather than by prefetch registers.
+#include "moba_internal.h"
+
+namespace moba {
+namespace {
+
+constexpr int kDecRows = 32;          // query rows per kv-head (one MFMA tile)
+constexpr int kDecTargetWaves = 4096; // split the keys until about this many wavefronts
+
+typedef short dec_s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dec_s16x4_t dec_lds_s16x4_t;
+
+// within each group of 16 lanes, lane i receives element i%4 of the 8 bytes addressed
+// by lanes 4j + i/4, j = 0..3
+__device__ __forceinline__ u32x2_t dec_tr16(const char* p) {
+  const dec_s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+__device__ __forceinline__ float dec_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float dec_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One wavefront: rows r = i*G + hl (new token i, query head g*G + hl) of kv-head g of
+// sequence b against 32-key subtiles [s*spt, min((s+1)*spt, nsub)).
+template <int D>
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int n, int Tk, int hq, int hkv, float sl, int spt,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int KS = D / 16;           // MFMA k-steps over the head dim
+  constexpr int VS = 2 * D + 64;       // V row stride in LDS: transpose reads hit all banks
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int CPL = 32 * CPR / 64;   // V chunks per lane per subtile
+  __shared__ __attribute__((aligned(16))) char vt[32 * VS];
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z, nsplit = gridDim.x;
+  const int lane = threadIdx.x, n32 = lane & 31, hf = lane >> 5;
+  const int G = hq / hkv, R = G * n;
+  const bool rv = n32 < R;
+  const int i = rv ? n32 / G : 0, hl = rv ? n32 % G : 0;
+  const int pos = Tk - n + i;          // this row's position among the keys
+
+  // Q^T operand: query n32, dims 16ks + 8hf .. +7 (zero for padding rows)
+  bf16x8_t bq[KS];
+  const uint16_t* qrow = q + (((size_t)b * n + i) * hq + g * G + hl) * D;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (rv) x = *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks + 8 * hf);
+    bq[ks] = as_bf16x8(x);
+  }
+  const size_t rs = (size_t)hkv * D;   // elements between consecutive keys
+  const uint16_t* kbase = k + ((size_t)b * Tk * hkv + g) * D;
+  const uint16_t* vbase = v + ((size_t)b * Tk * hkv + g) * D;
+  const int nsub = (Tk + 31) / 32;
+  const int sub0 = s * spt, sub1 = min(sub0 + spt, nsub);
+
+  float m = -INFINITY, l = 0.f;
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  // V^T read address of this lane (key order matching the score registers)
+  const char* vp = vt + (4 * hf + ((lane & 15) >> 2)) * VS +
+                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+  for (int sub = sub0; sub < sub1; ++sub) {
+    const int kb = sub * 32;
+    const int nvalid = min(32, Tk - kb);
+    // rows past the end of the cache read as zeros (and are masked below)
+    const int bytes = (int)(nvalid * rs * sizeof(uint16_t));
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbase + (size_t)kb * rs), (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vbase + (size_t)kb * rs), (short)0, bytes, 0x00020000);
+    u32x4_t ka[KS], vc[CPL];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rk, (int)((n32 * rs + 16 * ks + 8 * hf) * 2), 0, 0));
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int x = lane + 64 * c;
+      vc[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rvv, (int)(((x / CPR) * rs + (x % CPR) * 8) * 2), 0, 0));
+    }
+    // the previous subtile's V^T reads are complete (their MFMAs have issued): rewrite
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int x = lane + 64 * c;
+      *reinterpret_cast<u32x4_t*>(vt + (x / CPR) * VS + (x % CPR) * 16) = vc[c];
+    }
+    // S^T = K Q^T: lane holds query n32, keys (e/4)*8 + hf*4 + e%4
+    f32x16_t sc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = mfma32x32x16(as_bf16x8(ka[ks]), bq[ks], sc);
+    if (kb + 31 > Tk - n) {            // some row does not see every key of the subtile
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kb + (e >> 2) * 8 + hf * 4 + (e & 3) > pos) sc[e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    const float mnew = fmaxf(m, dec_pair_max(mx) * sl);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);   // 0 while m = -inf
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], sl, -mref));
+      l += p[e];
+    }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+      pb[h] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+    }
+    // O^T += V^T P^T over the subtile's two 16-key k-steps
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u32x2_t lo = dec_tr16(vp + (16 * ks) * VS + dt * 64);
+        const u32x2_t hi = dec_tr16(vp + (16 * ks + 8) * VS + dt * 64);
+        o[dt] = mfma32x32x16(as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o[dt]);
+      }
+  }
+
+  // partial of this split: o normalised (fp32), lse in natural log; a row that saw no
+  // key of the split gets lse = -inf and o = 0
+  const float ltot = dec_pair_sum(l);
+  if (!rv) return;
+  const size_t pr = ((size_t)(b * hkv + g) * nsplit + s) * R + n32;
+  const bool seen = ltot > 0.f;
+  const float inv = seen ? 1.f / ltot : 0.f;
+  float* po = part_o + pr * D + hf * 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const f32x4_t w = {o[dt][ii * 4] * inv, o[dt][ii * 4 + 1] * inv,
+                         o[dt][ii * 4 + 2] * inv, o[dt][ii * 4 + 3] * inv};
+      *reinterpret_cast<f32x4_t*>(po + dt * 32 + ii * 8) = w;
+    }
+  if (hf == 0)
+    part_lse[pr] = seen ? (m + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+}
+
+// One workgroup per (row, kv-head, sequence), one thread per dim: the log-sum-exp merge
+// of the row's split partials, written as bf16 out (nearest even) and fp32 lse.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_lse,
+                                                         int n, int hq, int hkv, int nsplit,
+                                                         uint16_t* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z, dim = threadIdx.x;
+  const int G = hq / hkv, R = G * n;
+  const int i = r / G, h = g * G + r % G;
+  const size_t p0 = (size_t)(b * hkv + g) * nsplit * R + r;   // split s: p0 + s * R
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[p0 + (size_t)s * R]);
+  float den = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = part_lse[p0 + (size_t)s * R];
+    if (ls == -INFINITY) continue;     // the split saw no key of this row
+    const float w = expf(ls - mx);
+    den += w;
+    acc = fmaf(w, part_o[(p0 + (size_t)s * R) * D + dim], acc);
+  }
+  out[(((size_t)b * n + i) * hq + h) * D + dim] = (uint16_t)f32_to_bf16_rne(acc / den);
+  if (dim == 0) lse[((size_t)b * hq + h) * n + i] = mx + logf(den);
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int b, int n, int Tk, int hq, int hkv, int d) {
+  DecodePlan p{};
+  const int nsub = (Tk + 31) / 32;
+  const long groups = (long)b * hkv;
+  int nsplit = (int)((kDecTargetWaves + groups - 1) / groups);
+  if (nsplit > nsub) nsplit = nsub;
+  if (nsplit < 1) nsplit = 1;
+  p.spt = (nsub + nsplit - 1) / nsplit;
+  p.nsplit = (nsub + p.spt - 1) / p.spt;
+  const size_t rows = (size_t)groups * p.nsplit * (hq / hkv) * n;
+  p.part_o_bytes = rows * d * sizeof(float);
+  p.part_lse_bytes = rows * sizeof(float);
+  return p;
+}
+
+int decode_max_rows() { return kDecRows; }
+
+hipError_t launch_decode(int b, int n, int Tk, int hq, int hkv, int d, float scale,
+                         const DecodePlan& p, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, float* part_o, float* part_lse, uint16_t* out,
+                         float* lse, hipStream_t st) {
+  const float sl = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)p.nsplit, (unsigned)hkv, (unsigned)b);
+  const dim3 mgrid((unsigned)((hq / hkv) * n), (unsigned)hkv, (unsigned)b);
+  if (d == 128) {
+    hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(64), 0, st, q, k, v, n, Tk, hq,
+                       hkv, sl, p.spt, part_o, part_lse);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), mgrid, dim3(128), 0, st, part_o, part_lse,
+                       n, hq, hkv, p.nsplit, out, lse);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(64), 0, st, q, k, v, n, Tk, hq,
+                       hkv, sl, p.spt, part_o, part_lse);
+    hipLaunchKernelGGL((decode_merge_kernel<64>), mgrid, dim3(64), 0, st, part_o, part_lse,
+                       n, hq, hkv, p.nsplit, out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moba

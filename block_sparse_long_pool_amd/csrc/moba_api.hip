@@ -430,6 +430,56 @@ int moba_dense_forward(const void* q, const void* k, const void* v, int batch, i
   return MOBA_OK;
 }
 
+// ------------------------------------------------------------------- decode
+namespace {
+
+int decode_check(int batch, int n_new, int kv_len, int hq, int hkv, int head_dim,
+                 float scale) {
+  if (batch <= 0 || n_new <= 0 || kv_len <= 0 || hq <= 0 || hkv <= 0 || head_dim <= 0)
+    return MOBA_ERR_INVALID_ARG;
+  if (hq % hkv != 0 || n_new > kv_len) return MOBA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return MOBA_ERR_INVALID_ARG;
+  if (scale <= 0.f) return MOBA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)(hq / hkv) * n_new > moba::decode_max_rows()) return MOBA_ERR_UNSUPPORTED;
+  if (batch > 65535 || hkv > 65535) return MOBA_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets within a 32-key subtile, and int token counts
+  if ((long long)32 * hkv * head_dim * 2 >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)batch * kv_len >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  return MOBA_OK;
+}
+
+}  // namespace
+
+size_t moba_decode_workspace_bytes(int batch, int n_new, int kv_len, int hq, int hkv,
+                                   int head_dim) {
+  if (decode_check(batch, n_new, kv_len, hq, hkv, head_dim, 1.f) != MOBA_OK) return 0;
+  const moba::DecodePlan p = moba::decode_plan(batch, n_new, kv_len, hq, hkv, head_dim);
+  return align_up(p.part_o_bytes) + align_up(p.part_lse_bytes);
+}
+
+int moba_decode(const void* q, const void* k, const void* v, int batch, int n_new,
+                int kv_len, int hq, int hkv, int head_dim, float scale, void* out,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = decode_check(batch, n_new, kv_len, hq, hkv, head_dim, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out || !lse || !workspace) return MOBA_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
+  const moba::DecodePlan p = moba::decode_plan(batch, n_new, kv_len, hq, hkv, head_dim);
+  if (align_up(p.part_o_bytes) + align_up(p.part_lse_bytes) > workspace_bytes)
+    return MOBA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_lse = reinterpret_cast<float*>(ws + align_up(p.part_o_bytes));
+  if (moba::launch_decode(batch, n_new, kv_len, hq, hkv, head_dim, scale, p,
+                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), part_o, part_lse,
+                          static_cast<uint16_t*>(out), lse,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOBA_ERR_HIP;
+  return MOBA_OK;
+}
+
 int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
                          int seqlen, int hq, int hkv, int head_dim, int block, int topk,
                          float scale, void* out, float* lse, int32_t* idx,

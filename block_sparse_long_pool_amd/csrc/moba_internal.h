@@ -128,6 +128,19 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
                                float* lse, hipStream_t st);
 int history_tile_rows();
 
+// full-attention decode: n new queries at the last n positions of a Tk-key cache, the
+// keys split over many wavefronts (fp32 (o, lse) partials per split), then a merge
+struct DecodePlan {
+  int nsplit, spt;                     // splits, 32-key subtiles per split
+  size_t part_o_bytes, part_lse_bytes;
+};
+DecodePlan decode_plan(int b, int n, int Tk, int hq, int hkv, int d);
+int decode_max_rows();                 // bound on (hq / hkv) * n
+hipError_t launch_decode(int b, int n, int Tk, int hq, int hkv, int d, float scale,
+                         const DecodePlan& p, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, float* part_o, float* part_lse, uint16_t* out,
+                         float* lse, hipStream_t st);
+
 // short depthwise causal convolution of the keys within blocks (width <= 8)
 int conv_max_width();
 hipError_t launch_key_conv(const Shape& s, const uint16_t* k, const float* weight, int width,

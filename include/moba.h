@@ -167,6 +167,27 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
                   float scale, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Full-attention decode, the hand-off after a MoBA prefill: generation switches to
+ * full attention (paper summary page on atlas.scime.ai, "Limitations"; README bullet
+ * "Seamlessly Transition between Full and Sparse Attention").  The n_new query tokens
+ * are the last n_new positions of a cache of kv_len keys: new token i (0-based) sits at
+ * position kv_len - n_new + i and attends keys 0 .. kv_len - n_new + i.
+ *   q          [b, n_new, hq, d] bf16
+ *   k, v       [b, kv_len, hkv, d] bf16 (the cache, the new tokens' keys included)
+ *   out        [b, n_new, hq, d] bf16, written
+ *   lse        [b, hq, n_new] float32, natural log, written
+ * The keys are split over many wavefronts that write fp32 partials to the workspace,
+ * merged by log-sum-exp in a second kernel.  Limits: head_dim 64 or 128,
+ * (hq / hkv) * n_new <= 32, 1 <= n_new <= kv_len (MOBA_ERR_UNSUPPORTED or
+ * MOBA_ERR_INVALID_ARG otherwise).  `workspace` must hold moba_decode_workspace_bytes
+ * and be 256-byte aligned (MOBA_ERR_WORKSPACE, MOBA_ERR_INVALID_ARG).  Enqueued on
+ * `stream` without synchronising; capturable like moba_forward. */
+size_t moba_decode_workspace_bytes(int batch, int n_new, int kv_len, int hq, int hkv,
+                                   int head_dim);
+int moba_decode(const void* q, const void* k, const void* v, int batch, int n_new,
+                int kv_len, int hq, int hkv, int head_dim, float scale, void* out,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward of moba_forward_varlen (packed sequences, each with its own block grid):
  * the same gradients as moba_backward run on each sequence alone.  q, k, v, out, dout,
  * dq, dk, dv in the packed [total, heads, d] layout; lse [hq, total]; idx

@@ -112,3 +112,23 @@ def test_forward_rejects_bad_args_before_any_launch(moba):
     assert lib.moba_forward_timed(*args, None) == -1
     ev = (ctypes.c_void_p * (len(moba.STAGES) + 1))(*([1] * len(moba.STAGES) + [None]))
     assert lib.moba_forward_timed(*args, ev) == -1
+
+
+def test_decode_args_and_workspace(moba):
+    lib = moba.lib
+    ws = moba.decode_workspace_bytes(1, 1, 131072, 32, 8, 128)
+    # fp32 partials of 4 rows per kv-head and split, and their lse: small next to the
+    # 537 MB the cache holds
+    assert 0 < ws < 64 << 20
+    assert moba.decode_workspace_bytes(1, 8, 1000, 4, 1, 64) > 0        # G * n = 32
+    assert moba.decode_workspace_bytes(1, 9, 1000, 4, 1, 64) == 0       # G * n = 36
+    assert moba.decode_workspace_bytes(1, 5, 4, 1, 1, 64) == 0          # n > kv_len
+    assert moba.decode_workspace_bytes(1, 1, 100, 6, 4, 64) == 0        # hq % hkv
+    assert moba.decode_workspace_bytes(1, 1, 100, 4, 1, 96) == 0        # head_dim 96
+    # shape rules first, then the pointers, all on the host
+    assert lib.moba_decode(None, None, None, 1, 1, 100, 4, 1, 96, 0.125, None, None, None,
+                           0, None) == -2
+    assert lib.moba_decode(None, None, None, 1, 1, 100, 4, 1, 64, 0.125, None, None, None,
+                           0, None) == -1
+    assert lib.moba_decode(None, None, None, 1, 2, 1, 4, 1, 64, 0.125, None, None, None,
+                           0, None) == -1
