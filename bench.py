@@ -142,6 +142,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip timing dense causal attention on the same inputs")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip timing the full-attention decode step on the same cache")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip timing the short key convolution")
     ap.add_argument("--no-varlen", action="store_true",
@@ -302,6 +304,40 @@ def main(argv=None):
         }
         print(f"[bench] dense causal {dms:.2f} ms", file=sys.stderr, flush=True)
         del out_d, lse_d
+    if not a.no_decode:
+        # the hand-off after the prefill: one new token per sequence decoded with full
+        # attention over the whole K/V cache (the last query row stands in for it).
+        # HBM-bound: every cached key and value is read once.
+        qd = q[:, -1:].contiguous()
+        dws = torch.empty(max(moba.decode_workspace_bytes(w.batch, 1, w.seqlen, w.hq, w.hkv,
+                                                          w.head_dim), 256),
+                          dtype=torch.uint8, device=dev)
+        od = torch.empty_like(qd)
+        ld = torch.empty((w.batch, w.hq, 1), dtype=torch.float32, device=dev)
+
+        def dstep():
+            moba.decode(qd, k, v, w.sm_scale, workspace=dws, out=od, lse=ld)
+
+        dstep()
+        torch.cuda.synchronize()
+        n_dec = 50
+        e0.record(stream)
+        for _ in range(n_dec):
+            dstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / n_dec
+        # algorithmic bytes: the cache's keys and values, the query and output rows
+        dbytes = 2 * (2 * w.batch * w.seqlen * w.hkv * w.head_dim + 2 * w.batch * w.hq
+                      * w.head_dim)
+        result["decode"] = {
+            "us": dec_ms * 1e3, "gbs": dbytes / (dec_ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": dbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "new_tokens": 1, "kv_len": w.seqlen, "algorithmic_bytes": dbytes,
+            "note": "moba_decode: one new token against the 128K cache (full attention)",
+        }
+        print(f"[bench] decode {dec_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del qd, dws, od, ld
     if not a.no_conv:
         # short key convolution within blocks (width 4, synthetic weights): HBM-bound,
         # every key read once and written once

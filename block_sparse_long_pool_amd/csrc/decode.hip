@@ -14,15 +14,15 @@
 // (lane = key), computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16, lane = query), runs
 // the online softmax in the log2 domain, stages the V rows in LDS and reads V^T with
 // the transpose read ds_read_b64_tr_b16 in the key order the score registers hold, so
-// that O^T += V^T P^T takes P^T straight from registers.  Latency is hidden by many
-// resident wavefronts rather than by prefetch registers.
+// that O^T += V^T P^T takes P^T straight from registers.  The next subtile's loads are
+// in flight while one is computed.
 #include "moba_internal.h"
 
 namespace moba {
 namespace {
 
 constexpr int kDecRows = 32;          // query rows per kv-head (one MFMA tile)
-constexpr int kDecTargetWaves = 4096; // split the keys until about this many wavefronts
+constexpr int kDecTargetWaves = 2048; // split the keys until about this many wavefronts
 
 typedef short dec_s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) dec_s16x4_t dec_lds_s16x4_t;
@@ -89,32 +89,40 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(
   const char* vp = vt + (4 * hf + ((lane & 15) >> 2)) * VS +
                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
-  for (int sub = sub0; sub < sub1; ++sub) {
-    const int kb = sub * 32;
-    const int nvalid = min(32, Tk - kb);
-    // rows past the end of the cache read as zeros (and are masked below)
-    const int bytes = (int)(nvalid * rs * sizeof(uint16_t));
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kbase + (size_t)kb * rs), (short)0, bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rvv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vbase + (size_t)kb * rs), (short)0, bytes, 0x00020000);
-    u32x4_t ka[KS], vc[CPL];
+  // global -> registers: the K operands (lane = key) or this lane's V chunks of a
+  // subtile; rows past the end of the cache read as zeros (and are masked)
+  auto rsrc = [&](const uint16_t* base, int kb) {
+    const int bytes = (int)(min(32, Tk - kb) * rs * sizeof(uint16_t));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (size_t)kb * rs),
+                                             (short)0, bytes, 0x00020000);
+  };
+  auto load_k = [&](int sub, u32x4_t (&ka)[KS]) {
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, sub * 32);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       ka[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                rk, (int)((n32 * rs + 16 * ks + 8 * hf) * 2), 0, 0));
+  };
+  auto load_v = [&](int sub, u32x4_t (&vc)[CPL]) {
+    const __amdgpu_buffer_rsrc_t rvv = rsrc(vbase, sub * 32);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int x = lane + 64 * c;
       vc[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                               rvv, (int)(((x / CPR) * rs + (x % CPR) * 8) * 2), 0, 0));
     }
+  };
+  // subtile sub from K operands ka and V chunks vc; once vc is in LDS, the V chunks of
+  // subtile vnext (when in range) are loaded into it
+  auto compute = [&](int sub, const u32x4_t (&ka)[KS], u32x4_t (&vc)[CPL], int vnext) {
+    const int kb = sub * 32;
     // the previous subtile's V^T reads are complete (their MFMAs have issued): rewrite
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int x = lane + 64 * c;
       *reinterpret_cast<u32x4_t*>(vt + (x / CPR) * VS + (x % CPR) * 16) = vc[c];
     }
+    if (vnext < sub1) load_v(vnext, vc);
     // S^T = K Q^T: lane holds query n32, keys (e/4)*8 + hf*4 + e%4
     f32x16_t sc = {};
 #pragma unroll
@@ -159,6 +167,20 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(
         const u32x2_t hi = dec_tr16(vp + (16 * ks + 8) * VS + dt * 64);
         o[dt] = mfma32x32x16(as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o[dt]);
       }
+  };
+  // the next subtile's K (second register set) and V (reloaded into the V registers
+  // once they are in LDS) are in flight while one subtile is computed
+  u32x4_t ka0[KS], ka1[KS], vc[CPL];
+  if (sub0 < sub1) {
+    load_k(sub0, ka0);
+    load_v(sub0, vc);
+  }
+  for (int sub = sub0; sub < sub1; sub += 2) {
+    if (sub + 1 < sub1) load_k(sub + 1, ka1);
+    compute(sub, ka0, vc, sub + 1);
+    if (sub + 1 >= sub1) break;
+    if (sub + 2 < sub1) load_k(sub + 2, ka0);
+    compute(sub + 1, ka1, vc, sub + 2);
   }
 
   // partial of this split: o normalised (fp32), lse in natural log; a row that saw no
@@ -181,30 +203,75 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(
     part_lse[pr] = seen ? (m + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
 }
 
-// One workgroup per (row, kv-head, sequence), one thread per dim: the log-sum-exp merge
-// of the row's split partials, written as bf16 out (nearest even) and fp32 lse.
+// One workgroup per (row, kv-head, sequence): the log-sum-exp merge of the row's split
+// partials, written as bf16 out (nearest even) and fp32 lse.  Thread t reads dims
+// 4*(t % (D/4)) .. +3 of splits t / (D/4), t / (D/4) + GROUPS, ..., kMergeBatch at a
+// time; the split groups are then summed through LDS in a fixed order.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeBatch = 8;         // splits whose loads a thread issues together
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_lse,
-                                                         int n, int hq, int hkv, int nsplit,
-                                                         uint16_t* __restrict__ out,
-                                                         float* __restrict__ lse) {
-  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z, dim = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int n, int hq,
+    int hkv, int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int LANES = D / 4, GROUPS = kMergeThreads / LANES;
+  __shared__ float red[kMergeThreads];
+  __shared__ f32x4_t racc[kMergeThreads];
+  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int G = hq / hkv, R = G * n;
   const int i = r / G, h = g * G + r % G;
   const size_t p0 = (size_t)(b * hkv + g) * nsplit * R + r;   // split s: p0 + s * R
+  // the largest split lse of the row
   float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[p0 + (size_t)s * R]);
-  float den = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ls = part_lse[p0 + (size_t)s * R];
-    if (ls == -INFINITY) continue;     // the split saw no key of this row
-    const float w = expf(ls - mx);
-    den += w;
-    acc = fmaf(w, part_o[(p0 + (size_t)s * R) * D + dim], acc);
+  for (int s = t; s < nsplit; s += kMergeThreads) mx = fmaxf(mx, part_lse[p0 + (size_t)s * R]);
+  red[t] = mx;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
   }
-  out[(((size_t)b * n + i) * hq + h) * D + dim] = (uint16_t)f32_to_bf16_rne(acc / den);
-  if (dim == 0) lse[((size_t)b * hq + h) * n + i] = mx + logf(den);
+  mx = red[0];
+  __syncthreads();
+  const int c4 = t % LANES, sg = t / LANES;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s0 = sg; s0 < nsplit; s0 += GROUPS * kMergeBatch) {
+    float ls[kMergeBatch];
+    f32x4_t x[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s0 + u * GROUPS;
+      ls[u] = s < nsplit ? part_lse[p0 + (size_t)s * R] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s0 + u * GROUPS;
+      // a split that saw no key of this row (lse = -inf) has weight 0
+      x[u] = ls[u] != -INFINITY ? *reinterpret_cast<const f32x4_t*>(
+                                      part_o + (p0 + (size_t)s * R) * D + 4 * c4)
+                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = ls[u] != -INFINITY ? expf(ls[u] - mx) : 0.f;
+      den += w;
+      acc += w * x[u];
+    }
+  }
+  red[t] = den;
+  racc[t] = acc;
+  __syncthreads();
+  if (sg != 0) return;
+  for (int q2 = 1; q2 < GROUPS; ++q2) {
+    den += red[q2 * LANES + c4];
+    acc += racc[q2 * LANES + c4];
+  }
+  const float inv = 1.f / den;
+  uint16_t* orow = out + (((size_t)b * n + i) * hq + h) * D + 4 * c4;
+  const u32x2_t pk = {f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16),
+                      f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16)};
+  *reinterpret_cast<u32x2_t*>(orow) = pk;
+  if (c4 == 0) lse[((size_t)b * hq + h) * n + i] = mx + logf(den);
 }
 
 }  // namespace
@@ -236,13 +303,13 @@ hipError_t launch_decode(int b, int n, int Tk, int hq, int hkv, int d, float sca
   if (d == 128) {
     hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(64), 0, st, q, k, v, n, Tk, hq,
                        hkv, sl, p.spt, part_o, part_lse);
-    hipLaunchKernelGGL((decode_merge_kernel<128>), mgrid, dim3(128), 0, st, part_o, part_lse,
-                       n, hq, hkv, p.nsplit, out, lse);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), mgrid, dim3(kMergeThreads), 0, st, part_o,
+                       part_lse, n, hq, hkv, p.nsplit, out, lse);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(64), 0, st, q, k, v, n, Tk, hq,
                        hkv, sl, p.spt, part_o, part_lse);
-    hipLaunchKernelGGL((decode_merge_kernel<64>), mgrid, dim3(64), 0, st, part_o, part_lse,
-                       n, hq, hkv, p.nsplit, out, lse);
+    hipLaunchKernelGGL((decode_merge_kernel<64>), mgrid, dim3(kMergeThreads), 0, st, part_o,
+                       part_lse, n, hq, hkv, p.nsplit, out, lse);
   }
   return hipGetLastError();
 }

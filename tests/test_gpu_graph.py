@@ -1,4 +1,5 @@
-"""The library's forward and backward captured in a HIP graph (torch.cuda.CUDAGraph).
+"""The library's forward, backward and decode captured in a HIP graph
+(torch.cuda.CUDAGraph).
 
 The library allocates nothing, copies nothing and clears nothing with memset: every
 launch goes to the caller's stream and every workspace word it reads is written by an
@@ -96,3 +97,31 @@ def test_backward_graph_replays(moba):
         moba.backward(q, k, v, out, lse, idx, dout2, 128, 5, workspace=ws)
         torch.cuda.synchronize()
     assert np.isfinite(ref[0].float().cpu().numpy()).all()
+
+
+def test_decode_graph_replays(moba):
+    rng = np.random.default_rng(93)
+    from workloads import f32_to_bf16_bits
+    say("[graph] decode b=1 n=2 Tk=3000 hq=8 hkv=2 d=128")
+    qb = f32_to_bf16_bits(rng.standard_normal((1, 2, 8, 128), dtype=np.float32))
+    kb = f32_to_bf16_bits(rng.standard_normal((1, 3000, 2, 128), dtype=np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((1, 3000, 2, 128), dtype=np.float32))
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    ws = torch.empty(moba.decode_workspace_bytes(1, 2, 3000, 8, 2, 128), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 8, 2), dtype=torch.float32, device="cuda")
+    moba.decode(q, k, v, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ref = [out.clone(), lse.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moba.decode(q, k, v, workspace=ws, out=out, lse=lse)
+    for r in range(REPLAYS):
+        out.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {r}"
+        moba.decode(-q, k, v, workspace=ws)
+        torch.cuda.synchronize()
