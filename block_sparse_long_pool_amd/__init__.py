@@ -1,4 +1,5 @@
-"""MoBA prefill forward on MI355X (gfx950): thin Python binding over libmoba.so.
+"""MoBA (Mixture of Block Attention) on MI355X (gfx950): thin Python binding over
+libmoba.so (prefill forward and backward, packed sequences, dense and decode paths).
 
 Every step of the path runs in the library's HIP kernels; this module only checks
 tensor arguments, allocates outputs and the workspace with torch, and passes raw
@@ -22,7 +23,8 @@ __all__ = [
     "pool_centroids", "gate_topk", "index_entries", "build_index", "strerror",
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
     "backward", "backward_workspace_bytes", "forward_varlen", "varlen_workspace_bytes",
-    "key_short_conv", "backward_varlen", "backward_varlen_workspace_bytes",
+    "key_short_conv", "backward_varlen", "backward_varlen_workspace_bytes", "decode",
+    "decode_workspace_bytes",
 ]
 
 # names of the steps timed by profile=True, in the library's order

@@ -1,5 +1,7 @@
-// Host side of libmoba: argument checks, workspace layout, and the launch sequence
-// of the MoBA prefill forward pass.  Every check runs before the first launch.
+// Host side of libmoba: argument checks, workspace layouts and launch sequences of the
+// MoBA prefill forward (batched and packed), its backward, the dense causal and decode
+// paths, the key convolution and the stage entry points.  Every check runs before the
+// first launch.
 #include <math.h>
 #include <string.h>
 

@@ -1,5 +1,6 @@
 /*
- * moba.h - C ABI of libmoba.so, the MI355X (gfx950) MoBA prefill forward pass.
+ * moba.h - C ABI of libmoba.so: MoBA (Mixture of Block Attention) on MI355X (gfx950),
+ * the prefill forward with its backward, packed sequences, dense and decode paths.
  *
  * MoBA (Mixture of Block Attention): the keys of a sequence are cut into blocks of
  * `block` tokens, each block is mean-pooled into a centroid, every query is scored
