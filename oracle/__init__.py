@@ -1,4 +1,6 @@
-"""CPU oracle for the MoBA prefill forward pass and its backward (float64, NumPy).
+"""CPU oracle for the MoBA prefill forward pass, its backward, packed sequences, the
+short key convolution and the full-attention decode that follows a prefill (float64,
+NumPy).
 
 TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by
 ``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``, and by
