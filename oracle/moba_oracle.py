@@ -1,4 +1,5 @@
-"""The plain float64 definition of MoBA prefill forward (and its gradient).
+"""The plain float64 definition of MoBA prefill forward, its gradient, packed sequences,
+the short key convolution and the full-attention decode after a prefill.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the product.
 
