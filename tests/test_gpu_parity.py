@@ -477,3 +477,40 @@ def test_llama8b_1m(moba):
     stats = compare_rows(_Bf16Rows(inp["q"]), K, V, w.block, w.topk, w.sm_scale, rows, go,
                          gl, gi[bi_, h_, t_], C=C)
     say(f"[big] {w.name}: {stats}")
+
+
+def test_edge_sizes(moba):
+    """The largest block count the library accepts (2048 blocks of 16 tokens), every
+    row's selection and sampled rows' out/lse; and a one-token sequence."""
+    w = small_workload("max_blocks", 1, 2, 1, 64, 32768, 16, 6, "offset", seed=18)
+    assert w.num_blocks == 2048
+    inp = make_inputs(w)
+    say(f"[edge] {w.name}: T={w.seqlen} B={w.block} nb={w.num_blocks} k={w.topk}")
+    go_t, gl_t, gi_t = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), w.block,
+                                    w.topk, w.sm_scale)
+    torch.cuda.synchronize()
+    gi = gi_t.cpu().numpy()
+    check_idx_rows(gi, w.block, w.topk)
+    Q, K, V = (bf16_to_f64(inp[x]) for x in "qkv")
+    rows = sample_rows(1, w.seqlen, w.hq, w.block, per_block=1, seed=6,
+                       extra=[(0, w.seqlen - 1, 1), (0, 0, 0)])
+    bi_, t_, h_ = (np.array(x) for x in zip(*rows))
+    ib, it, ih = (torch.as_tensor(x, device="cuda") for x in (bi_, t_, h_))
+    stats = compare_rows(Q, K, V, w.block, w.topk, w.sm_scale, rows,
+                         go_t[ib, it, ih].float().cpu().numpy(), gl_t[ib, ih, it].cpu().numpy(),
+                         gi[bi_, h_, t_])
+    say(f"       {stats}")
+    # one token: it attends itself only
+    w1 = small_workload("one_token", 2, 4, 2, 128, 1, 16, 3, "iid", seed=19)
+    inp1 = make_inputs(w1)
+    o1, l1, i1 = moba.forward(dev(inp1["q"]), dev(inp1["k"]), dev(inp1["v"]), 16, 3)
+    torch.cuda.synchronize()
+    V1 = bf16_to_f64(inp1["v"])
+    Q1, K1 = bf16_to_f64(inp1["q"]), bf16_to_f64(inp1["k"])
+    for b in range(2):
+        for h in range(4):
+            assert i1[b, h, 0].tolist() == [0, -1, -1]
+            np.testing.assert_allclose(o1[b, 0, h].float().cpu().numpy(), V1[b, 0, h // 2],
+                                       atol=1e-2)
+            np.testing.assert_allclose(l1[b, h, 0].item(),
+                                       w1.sm_scale * Q1[b, 0, h] @ K1[b, 0, h // 2], atol=1e-3)
