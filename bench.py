@@ -74,10 +74,11 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def read_traffic():
+def read_traffic(workload: str):
     """HBM bytes per history-attention dispatch from the committed rocprofv3 counter
-    summary, or None when there is none or the kernel source changed since."""
-    if not os.path.exists(COUNTERS_FILE):
+    summary, or None when there is none, it was taken on another workload, or the
+    kernel source changed since."""
+    if not os.path.exists(COUNTERS_FILE) or workload not in os.path.basename(COUNTERS_FILE):
         return None
     text = open(COUNTERS_FILE).read()
     m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
@@ -142,6 +143,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip timing dense causal attention on the same inputs")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step captured in a HIP graph")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip timing the full-attention decode step on the same cache")
     ap.add_argument("--no-conv", action="store_true",
@@ -208,6 +211,23 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
 
+    graph_ms = None
+    if not a.no_graph:
+        # the same step captured once in a HIP graph and replayed: no per-kernel launch
+        # cost (the library allocates, copies and clears nothing, so it captures as is)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / a.steps
+        del g
+
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.bfloat16, device=dev)
@@ -246,7 +266,7 @@ def main(argv=None):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": hist_tflops / PEAK_BF16_TFLOPS if hist_tflops else None,
-        "traffic": read_traffic() if one_launch else None,
+        "traffic": read_traffic(w.name) if one_launch else None,
         "algorithmic_per_launch": f"{flop_hist:.4e} FLOP = 4 * d * {heads} heads * "
                                   f"{hist} history pairs per head",
     }
@@ -281,6 +301,12 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if graph_ms is not None:
+        result["graph_replay"] = {
+            "ms_per_step": graph_ms, "tflops": flop / (graph_ms * 1e-3) / 1e12,
+            "note": "the same step captured once in a HIP graph (torch.cuda.CUDAGraph) "
+                    "and replayed: no per-launch cost",
+        }
     if not a.no_dense:
         # the full-attention layer of a hybrid model on the same inputs: context for the
         # sparse path (not the metric)
