@@ -144,6 +144,14 @@ def _need(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _one_device(*tensors):
+    """Every tensor argument of a call lives on the first one's device."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError(f"all tensors must be on {dev} (got one on {t.device})")
+
+
 def _alloc_workspace(nbytes, device):
     torch = _torch()
     # torch's caching allocator returns 512-byte aligned blocks
@@ -209,6 +217,7 @@ def forward(q, k, v, block: int, topk: int, scale: float | None = None, workspac
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv, d, block, topk,
             float(scale), out.data_ptr(), lse.data_ptr(), idx.data_ptr(),
             workspace.data_ptr(), workspace.numel(), _stream_ptr())
+    _one_device(q, k, v, out, lse, idx, workspace)
     with torch.cuda.device(q.device):
         if profile:
             ms = (ctypes.c_float * len(STAGES))()
@@ -247,6 +256,7 @@ def dense_forward(q, k, v, scale: float | None = None, out=None, lse=None):
     _need(lse, "lse", torch.float32, 3)
     if out.shape != q.shape or lse.shape != (b, hq, T):
         raise ValueError("output shapes do not match the inputs")
+    _one_device(q, k, v, out, lse)
     with torch.cuda.device(q.device):
         st = lib.moba_dense_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv,
                                     d, float(scale), out.data_ptr(), lse.data_ptr(),
@@ -294,6 +304,7 @@ def decode(q, k, v, scale: float | None = None, workspace=None, out=None, lse=No
     _need(lse, "lse", torch.float32, 3)
     if out.shape != q.shape or lse.shape != (b, hq, n):
         raise ValueError("output shapes do not match the inputs")
+    _one_device(q, k, v, out, lse, workspace)
     with torch.cuda.device(q.device):
         st = lib.moba_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, n, Tk, hq, hkv, d,
                              float(scale), out.data_ptr(), lse.data_ptr(),
@@ -359,6 +370,7 @@ def forward_varlen(q, k, v, cu_seqlens, block: int, topk: int, scale: float | No
     _need(idx, "idx", torch.int32, 3)
     if out.shape != q.shape or lse.shape != (hq, total) or idx.shape != (hq, total, topk):
         raise ValueError("output shapes do not match the inputs")
+    _one_device(q, k, v, out, lse, idx, workspace)
     with torch.cuda.device(q.device):
         st = lib.moba_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      cu_dev.data_ptr(), nseq, total, max_seqlen, hq, hkv, d,
@@ -456,6 +468,7 @@ def backward_varlen(q, k, v, out, lse, idx, dout, cu_seqlens, block: int, topk: 
         _need(workspace, "workspace", torch.uint8, 1)
     cu_dev = cu_host.to(device=q.device, dtype=torch.int32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _one_device(q, k, v, out, lse, idx, dout, workspace)
     with torch.cuda.device(q.device):
         st = lib.moba_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       lse.data_ptr(), idx.data_ptr(), dout.data_ptr(),
@@ -515,6 +528,7 @@ def backward(q, k, v, out, lse, idx, dout, block: int, topk: int, scale: float |
     _need(dv, "dv", torch.bfloat16, 4)
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
         raise ValueError("gradient shapes do not match the inputs")
+    _one_device(q, k, v, out, lse, idx, dout, workspace)
     with torch.cuda.device(q.device):
         st = lib.moba_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), idx.data_ptr(), dout.data_ptr(), b, T, hq, hkv,
