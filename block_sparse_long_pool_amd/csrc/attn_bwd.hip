@@ -162,22 +162,28 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     t = (int)(ent >> 5) / G;
     hl = (int)(ent >> 5) % G;
   } else {
-    // blockIdx.x: 32*kBwdWaves/G-token tile of block blockIdx.y (from the end of the
-    // block, longest first); wave w takes head w % G and token sub-tile w / G
+    // blockIdx.x: a 32*TS-token tile of block blockIdx.y (from the end of the block,
+    // longest first) for the GA heads hg*GA .. of kv-head group gi; wave w takes head
+    // w % GA and token sub-tile w / GA.  Waves past GA*TS (G not dividing the wave
+    // count) and heads past G run on zero rows, so every wave reaches every barrier.
     const int c = blockIdx.y;
-    gi = blockIdx.z % ng;
-    b = blockIdx.z / ng;
-    const int TS = kBwdWaves / G;                   // G divides kBwdWaves (checked)
+    const int GA = G < kBwdWaves ? G : kBwdWaves;   // heads per workgroup
+    const int HG = (G + GA - 1) / GA;               // head groups per kv-head
+    const int TS = kBwdWaves / GA;                  // 32-token sub-tiles per workgroup
     const int TT = 32 * TS;
+    const int hg = blockIdx.z % HG;
+    gi = (blockIdx.z / HG) % ng;
+    b = blockIdx.z / (HG * ng);
     const int x = gridDim.x - 1 - blockIdx.x;
     const int t0 = c * block + x * TT;
-    hl = wave % G;
-    t = t0 + (wave / G) * 32 + n;
+    const bool active = wave < GA * TS && hg * GA + wave % GA < G;
+    hl = active ? hg * GA + wave % GA : 0;
+    t = t0 + (wave / GA) * 32 + n;
     kbeg = c * block;
     // a partial last block, or a block past the end of a shorter packed sequence
     kend = min(min(t0 + TT, (c + 1) * block), sq.len(b));
     if (t0 >= kend) return;
-    valid = t < kend;
+    valid = active && t < kend;
     if (!valid) t = c * block;
   }
   const int g = g0 + gi, h = g * G + hl;
@@ -384,7 +390,7 @@ struct KvLds {
   static constexpr int TOTAL = 2 * BUF + PX;
 };
 
-template <int D>
+template <int D, bool POW2>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
@@ -438,7 +444,16 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   constexpr int CHUNKS = 2 * 32 * CPR;
   constexpr int NC = CHUNKS / kKvThreads;
   static_assert(CHUNKS % kKvThreads == 0, "every thread moves whole chunks");
-  const int gshift = __builtin_ctz((unsigned)G);   // G is a power of two
+  // own-block row rc is token kc0 + rc / G, head rc % G (shifts when G is a power of 2)
+  const int gshift = __builtin_ctz((unsigned)G);
+  auto rtok = [&](int rc) {
+    if constexpr (POW2) return rc >> gshift;
+    else return rc / G;
+  };
+  auto rhead = [&](int rc) {
+    if constexpr (POW2) return rc & (G - 1);
+    else return rc % G;
+  };
   const size_t row_base = (size_t)tok0 * hq + g * G;   // row of (b, t = 0, head g*G)
   const size_t meta_base = sq.lrow(b, g * G, hq);     // lse/delta of (b, g*G, t = 0)
   const int lhs = sq.lhead();                          // lse stride between heads
@@ -459,7 +474,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   // the q (dO) row of current row r >= nhist (clamped to the last row past the end)
   auto cur_row = [&](int r) -> size_t {
     const int rc = min(r, nrows - 1) - nhist;
-    return row_base + (size_t)(kc0 + (rc >> gshift)) * hq + (rc & (G - 1));
+    return row_base + (size_t)(kc0 + rtok(rc)) * hq + rhead(rc);
   };
   auto fetch_rows = [&](int r0, Rows& rd) {
 #pragma unroll
@@ -477,13 +492,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
       dv0 = m[1];
     } else {
       const int rc = min(r, nrows - 1) - nhist;
-      const size_t at = meta_base + (size_t)(rc & (G - 1)) * lhs + kc0 + (rc >> gshift);
+      const size_t at = meta_base + (size_t)rhead(rc) * lhs + kc0 + rtok(rc);
       lv = lse[at];
       dv0 = delta[at];
     }
     rd.f = r < nrows ? lv * kLog2e : INFINITY;   // p = 0 for rows past the end
     rd.d = r < nrows ? dv0 : 0.f;
-    rd.t = r < nhist ? 0x7fffffff : kc0 + ((min(r, nrows - 1) - nhist) >> gshift);
+    rd.t = r < nhist ? 0x7fffffff : kc0 + rtok(min(r, nrows - 1) - nhist);
   };
   auto store_rows = [&](const Rows& rd, int buf) {
     char* base = lds + buf * L::BUF;
@@ -623,7 +638,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
 int bwd_tile_rows() { return kBwdWaves * 32; }
 
 // the current-block dQ tiles put the G heads of a kv-head on different waves
-bool bwd_supported(const Shape& s) { return kBwdWaves % s.G() == 0; }
+bool bwd_supported(const Shape& s) { return s.G() >= 1; }
 
 hipError_t launch_bwd_delta(const Shape& s, const uint16_t* out, const uint16_t* dout,
                             float* delta, hipStream_t st) {
@@ -655,8 +670,10 @@ hipError_t launch_bwd_dq_current(const Shape& s, const uint16_t* q, const uint16
                                  const float* delta, float scale, int g0, int ng,
                                  const float* dq_part, uint16_t* dq, hipStream_t st) {
   const float sl = scale * kLog2e;
-  const int TT = 32 * (kBwdWaves / s.G());
-  dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng);
+  const int GA = s.G() < kBwdWaves ? s.G() : kBwdWaves;     // heads per workgroup
+  const int HG = (s.G() + GA - 1) / GA;                     // head groups per kv-head
+  const int TT = 32 * (kBwdWaves / GA);
+  dim3 grid((s.block + TT - 1) / TT, s.nb(), s.b * ng * HG);
 #define MOBA_DQC(DD)                                                                       \
   hipLaunchKernelGGL((bwd_dq_kernel<DD, true>), grid, dim3(kBwdThreads), 0, st, q, k, v,     \
                      dout, lse, delta, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, scale, g0, \
@@ -692,12 +709,18 @@ hipError_t launch_bwd_dkdv(const Shape& s, const uint16_t* q, const uint16_t* k,
   const float sl = scale * kLog2e;
   const int kpw = 32 * kKvTiles;
   dim3 grid((s.block + kpw - 1) / kpw, s.nb(), s.b * ng);
-#define MOBA_KV(DD)                                                                        \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DD>), grid, dim3(kKvThreads), 0, st, q, k, v, dout,    \
-                     lse, delta, s.seqs(), s.hq, s.hkv, s.block, sl, scale, g0, ng, s.nb(),   \
-                     list_offsets, dense_rows, dense_meta, dk, dv)
-  if (s.d == 128) MOBA_KV(128);
-  else MOBA_KV(64);
+#define MOBA_KV(DD, P2)                                                                    \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, P2>), grid, dim3(kKvThreads), 0, st, q, k, v,      \
+                     dout, lse, delta, s.seqs(), s.hq, s.hkv, s.block, sl, scale, g0, ng,     \
+                     s.nb(), list_offsets, dense_rows, dense_meta, dk, dv)
+  const bool pow2 = (s.G() & (s.G() - 1)) == 0;
+  if (s.d == 128) {
+    if (pow2) MOBA_KV(128, true);
+    else MOBA_KV(128, false);
+  } else {
+    if (pow2) MOBA_KV(64, true);
+    else MOBA_KV(64, false);
+  }
 #undef MOBA_KV
   return hipGetLastError();
 }

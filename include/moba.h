@@ -158,8 +158,8 @@ size_t moba_backward_workspace_bytes(int batch, int seqlen, int hq, int hkv,
  *   dk, dv                   [b, T, hkv, d] bf16, written (every element)
  * Accumulation is float32; dq sums fp32 per-history-block parts in slot order and dk,
  * dv are each summed by one workgroup in a fixed row order: deterministic.  Shape
- * limits are moba_forward's (a partial last block included) plus G = hq / hkv in
- * {1, 2, 4, 8} (MOBA_ERR_UNSUPPORTED otherwise).  `workspace` must hold at least the minimum of
+ * limits are moba_forward's (a partial last block included; any G = hq / hkv).
+ * `workspace` must hold at least the minimum of
  * moba_backward_workspace_bytes and be 256-byte aligned (MOBA_ERR_WORKSPACE,
  * MOBA_ERR_INVALID_ARG).  Enqueued on `stream` without synchronising. */
 int moba_backward(const void* q, const void* k, const void* v, const void* out,
@@ -193,7 +193,7 @@ int moba_decode(const void* q, const void* k, const void* v, int batch, int n_ne
  * the same gradients as moba_backward run on each sequence alone.  q, k, v, out, dout,
  * dq, dk, dv in the packed [total, heads, d] layout; lse [hq, total]; idx
  * [hq, total, topk]; cu_seqlens as for moba_forward_varlen (DEVICE, unchecked
- * contents).  Limits as moba_forward_varlen's plus moba_backward's G rule. */
+ * contents).  Limits as moba_forward_varlen's. */
 size_t moba_backward_varlen_workspace_bytes(int nseq, int total, int max_seqlen, int hq,
                                             int hkv, int head_dim, int block, int topk,
                                             size_t* min_bytes);

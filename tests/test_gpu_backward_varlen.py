@@ -73,6 +73,7 @@ PACKED = [
     ((16, 17, 15, 700, 33), 16, 2, 128, 16, 6),
     ((2500,), 4, 2, 128, 512, 2),
     ((0, 640, 0, 129), 4, 1, 128, 128, 3),       # empty sequences in the pack
+    ((300, 129, 700), 6, 2, 128, 128, 4),        # G = 3
 ]
 
 

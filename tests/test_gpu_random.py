@@ -75,7 +75,7 @@ def test_forward_random_shape(moba, seed):
 def test_backward_random_shape(moba, seed):
     """The oracle's gradients with the GPU's selection held fixed (each idx row checked
     valid first), so near ties in the gate cannot make the comparison fail."""
-    b, T, hq, hkv, d, B, k = draw(seed, groups=(1, 2, 4, 8), max_rows=6000)
+    b, T, hq, hkv, d, B, k = draw(seed, groups=(1, 2, 3, 4, 5, 7, 8), max_rows=6000)
     say(f"[random bwd] seed={seed}: b={b} T={T} hq={hq} hkv={hkv} d={d} B={B} k={k}")
     w = small_workload("rndb", b, hq, hkv, d, T, B, k, "offset", seed=seed)
     inp = make_inputs(w)
