@@ -4,9 +4,9 @@
 // Attention for Long-Context LLMs", paper summary page, "Limitations"; README bullet
 // "Seamlessly Transition between Full and Sparse Attention").
 //
-// HBM-bound: every key and value of the cache is read once.  The G*n query rows of a
-// kv-head (G query heads per kv-head, n new tokens; G*n <= 32) form one 32-row MFMA
-// tile, so each key row read serves all of them.  The key range is split over many
+// HBM-bound: every key and value of the cache is read once per 32 query rows.  The
+// G*n query rows of a kv-head (G query heads per kv-head, n new tokens) form 32-row
+// MFMA tiles (one for decode: G*n <= 32), so each key row read serves a whole tile.  The key range is split over many
 // single-wavefront workgroups (split-K), each writing an fp32 (o, lse) partial for its
 // rows; a second kernel merges the partials by log-sum-exp.
 //
@@ -21,7 +21,7 @@
 namespace moba {
 namespace {
 
-constexpr int kDecRows = 32;          // query rows per kv-head (one MFMA tile)
+constexpr int kDecMaxRows = 1024;     // query rows per kv-head (32 per MFMA tile)
 constexpr int kDecTargetWaves = 2048; // split the keys until about this many wavefronts
 
 typedef short dec_s16x4_t __attribute__((ext_vector_type(4)));
@@ -45,8 +45,9 @@ __device__ __forceinline__ float dec_pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One wavefront: rows r = i*G + hl (new token i, query head g*G + hl) of kv-head g of
-// sequence b against 32-key subtiles [s*spt, min((s+1)*spt, nsub)).
+// One wavefront: the 32 rows rg*32 .. of the rows r = i*G + hl (new token i, query head
+// g*G + hl) of kv-head g of sequence b, blockIdx.y = g * RG + rg, against 32-key subtiles
+// [s*spt, min((s+1)*spt, nsub)).
 template <int D>
 __global__ __launch_bounds__(64, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -57,11 +58,12 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int CPL = 32 * CPR / 64;   // V chunks per lane per subtile
   __shared__ __attribute__((aligned(16))) char vt[32 * VS];
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z, nsplit = gridDim.x;
+  const int s = blockIdx.x, b = blockIdx.z, nsplit = gridDim.x;
   const int lane = threadIdx.x, n32 = lane & 31, hf = lane >> 5;
-  const int G = hq / hkv, R = G * n;
-  const bool rv = n32 < R;
-  const int i = rv ? n32 / G : 0, hl = rv ? n32 % G : 0;
+  const int G = hq / hkv, R = G * n, RG = (R + 31) / 32;
+  const int g = blockIdx.y / RG, r = (blockIdx.y % RG) * 32 + n32;
+  const bool rv = r < R;
+  const int i = rv ? r / G : 0, hl = rv ? r % G : 0;
   const int pos = Tk - n + i;          // this row's position among the keys
 
   // Q^T operand: query n32, dims 16ks + 8hf .. +7 (zero for padding rows)
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(
   // key of the split gets lse = -inf and o = 0
   const float ltot = dec_pair_sum(l);
   if (!rv) return;
-  const size_t pr = ((size_t)(b * hkv + g) * nsplit + s) * R + n32;
+  const size_t pr = ((size_t)(b * hkv + g) * nsplit + s) * R + r;
   const bool seen = ltot > 0.f;
   const float inv = seen ? 1.f / ltot : 0.f;
   float* po = part_o + pr * D + hf * 4;
@@ -279,26 +281,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
 DecodePlan decode_plan(int b, int n, int Tk, int hq, int hkv, int d) {
   DecodePlan p{};
   const int nsub = (Tk + 31) / 32;
-  const long groups = (long)b * hkv;
+  const long groups = (long)b * hkv * ((hq / hkv * n + 31) / 32);   // row tiles
   int nsplit = (int)((kDecTargetWaves + groups - 1) / groups);
   if (nsplit > nsub) nsplit = nsub;
   if (nsplit < 1) nsplit = 1;
   p.spt = (nsub + nsplit - 1) / nsplit;
   p.nsplit = (nsub + p.spt - 1) / p.spt;
-  const size_t rows = (size_t)groups * p.nsplit * (hq / hkv) * n;
+  const size_t rows = (size_t)b * hkv * p.nsplit * (hq / hkv) * n;
   p.part_o_bytes = rows * d * sizeof(float);
   p.part_lse_bytes = rows * sizeof(float);
   return p;
 }
 
-int decode_max_rows() { return kDecRows; }
+int decode_max_rows() { return kDecMaxRows; }
 
 hipError_t launch_decode(int b, int n, int Tk, int hq, int hkv, int d, float scale,
                          const DecodePlan& p, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, float* part_o, float* part_lse, uint16_t* out,
                          float* lse, hipStream_t st) {
   const float sl = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)p.nsplit, (unsigned)hkv, (unsigned)b);
+  const int RG = ((hq / hkv) * n + 31) / 32;
+  const dim3 grid((unsigned)p.nsplit, (unsigned)(hkv * RG), (unsigned)b);
   const dim3 mgrid((unsigned)((hq / hkv) * n), (unsigned)hkv, (unsigned)b);
   if (d == 128) {
     hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(64), 0, st, q, k, v, n, Tk, hq,

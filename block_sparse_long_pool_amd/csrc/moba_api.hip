@@ -444,7 +444,8 @@ int decode_check(int batch, int n_new, int kv_len, int hq, int hkv, int head_dim
   if (scale <= 0.f) return MOBA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return MOBA_ERR_UNSUPPORTED;
   if ((long long)(hq / hkv) * n_new > moba::decode_max_rows()) return MOBA_ERR_UNSUPPORTED;
-  if (batch > 65535 || hkv > 65535) return MOBA_ERR_UNSUPPORTED;
+  if (batch > 65535 || (long long)hkv * (((hq / hkv) * n_new + 31) / 32) > 65535)
+    return MOBA_ERR_UNSUPPORTED;
   // 32-bit buffer offsets within a 32-key subtile, and int token counts
   if ((long long)32 * hkv * head_dim * 2 >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
   if ((long long)batch * kv_len >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;

@@ -135,7 +135,7 @@ struct DecodePlan {
   size_t part_o_bytes, part_lse_bytes;
 };
 DecodePlan decode_plan(int b, int n, int Tk, int hq, int hkv, int d);
-int decode_max_rows();                 // bound on (hq / hkv) * n
+int decode_max_rows();                 // bound on (hq / hkv) * n (query rows per kv-head)
 hipError_t launch_decode(int b, int n, int Tk, int hq, int hkv, int d, float scale,
                          const DecodePlan& p, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, float* part_o, float* part_lse, uint16_t* out,

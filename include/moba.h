@@ -178,8 +178,10 @@ int moba_backward(const void* q, const void* k, const void* v, const void* out,
  *   out        [b, n_new, hq, d] bf16, written
  *   lse        [b, hq, n_new] float32, natural log, written
  * The keys are split over many wavefronts that write fp32 partials to the workspace,
- * merged by log-sum-exp in a second kernel.  Limits: head_dim 64 or 128,
- * (hq / hkv) * n_new <= 32, 1 <= n_new <= kv_len (MOBA_ERR_UNSUPPORTED or
+ * merged by log-sum-exp in a second kernel.  The (hq / hkv) * n_new query rows of a
+ * kv-head go in tiles of 32, each tile reading the cache once (one tile for decode).
+ * Limits: head_dim 64 or 128, (hq / hkv) * n_new <= 1024, 1 <= n_new <= kv_len
+ * (MOBA_ERR_UNSUPPORTED or
  * MOBA_ERR_INVALID_ARG otherwise).  `workspace` must hold moba_decode_workspace_bytes
  * and be 256-byte aligned (MOBA_ERR_WORKSPACE, MOBA_ERR_INVALID_ARG).  Enqueued on
  * `stream` without synchronising; capturable like moba_forward. */

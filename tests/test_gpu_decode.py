@@ -57,6 +57,9 @@ def check(go, gl, ro, rl, label):
     (3, 2, 5000, 16, 4, 64),
     (1, 32, 700, 1, 1, 128),       # G = 1, 32 new tokens
     (1, 1, 20000, 32, 1, 128),     # G = 32
+    (1, 33, 500, 1, 1, 128),       # 33 rows: two row tiles, the second with one row
+    (1, 1, 3000, 64, 1, 128),      # G = 64: two row tiles of one new token
+    (2, 16, 2000, 8, 2, 64),       # 128 rows per kv-head: four row tiles
 ])
 def test_decode_all_rows(moba, b, n, Tk, hq, hkv, d):
     say(f"[decode] b={b} n={n} Tk={Tk} hq={hq} hkv={hkv} d={d}")
@@ -111,8 +114,8 @@ def test_decode_deterministic(moba):
 
 def test_decode_rejects_bad_args(moba):
     k = dev(bits(31, 1, 64, 1, 128))
-    with pytest.raises(ValueError):            # G * n = 64 > 32 rows
-        moba.decode(dev(bits(32, 1, 2, 32, 128)), k, k)
+    with pytest.raises(ValueError):            # G * n = 2048 > 1024 rows
+        moba.decode(dev(bits(32, 1, 2, 1024, 128)), k, k)
     with pytest.raises(ValueError):            # more new tokens than cached keys
         moba.decode(dev(bits(33, 1, 65, 1, 128)), k, k)
     small = torch.empty(256, dtype=torch.uint8, device="cuda")

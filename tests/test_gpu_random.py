@@ -118,7 +118,7 @@ def test_decode_random_shape(moba, seed):
     hkv = int(r.choice([1, 2, 8]))
     d = int(r.choice([64, 128]))
     b = int(r.choice([1, 2]))
-    n = int(r.integers(1, 32 // G + 1))
+    n = int(r.integers(1, 64 // G + 1))      # up to two 32-row tiles
     Tk = int(r.integers(n, 6000))
     say(f"[random decode] seed={seed}: b={b} n={n} Tk={Tk} hq={G * hkv} hkv={hkv} d={d}")
     qb, kb, vb = bits(seed, b, n, G * hkv, d), bits(seed + 1, b, Tk, hkv, d), bits(seed + 2, b, Tk, hkv, d)
