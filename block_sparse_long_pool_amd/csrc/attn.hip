@@ -518,11 +518,12 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
 // Log-sum-exp merge of a row's current-block result (in registers) with its nh history
 // partials, written as the final output: L = ln(e^lse_c + sum_s e^lse_s), out =
 // e^(lse_c - L) o_c + sum_s e^(lse_s - L) o_s (bf16, round to nearest even), lse = L.
-// Lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row.
+// Lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row; the row's part lse of
+// slot s is pl[s * ls].
 template <int D, int QT>
 __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, bool valid,
                                             int nh, const uint16_t* __restrict__ po,
-                                            const float* __restrict__ pl,
+                                            const float* __restrict__ pl, size_t ls,
                                             uint16_t* __restrict__ orow, float* __restrict__ lrow) {
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const float lc = pair_sum(st.l[qt]);
@@ -539,7 +540,7 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
   for (int s0 = 0; s0 < nh; s0 += CH) {
     float v[CH];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) v[u] = pl[min(s0 + u, nh - 1)];
+    for (int u = 0; u < CH; ++u) v[u] = pl[(size_t)min(s0 + u, nh - 1) * ls];
 #pragma unroll
     for (int u = 0; u < CH; ++u) mx = fmaxf(mx, v[u]);
   }
@@ -547,7 +548,7 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
   for (int s0 = 0; s0 < nh; s0 += CH) {
     float v[CH];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) v[u] = pl[min(s0 + u, nh - 1)];
+    for (int u = 0; u < CH; ++u) v[u] = pl[(size_t)min(s0 + u, nh - 1) * ls];
 #pragma unroll
     for (int u = 0; u < CH; ++u)
       if (s0 + u < nh) den += expf(v[u] - mx);
@@ -570,7 +571,7 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
       const uint16_t* ps = po + (size_t)sc * D + hf * (D / 2);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) x[u][c] = *reinterpret_cast<const u32x4_t*>(ps + c * 8);
-      w[u] = s0 + u < nh ? expf(pl[sc] - L) : 0.f;
+      w[u] = s0 + u < nh ? expf(pl[(size_t)sc * ls] - L) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < CH; ++u)
@@ -619,7 +620,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
     const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, size_t ls) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int tile_id = blockIdx.x;
   if (tile_id >= *tile_count) return;
@@ -658,9 +659,9 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
   const int ngq = ng * G;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const size_t prow =
-        (sq.prow(b, gi * G + hlq[qt], ngq) + tq[qt]) * (topk - 1) + slq[qt];
-    store_partial(st, qt, vq[qt], part_o + prow * D, part_lse + prow);
+    const size_t row = sq.prow(b, gi * G + hlq[qt], ngq) + tq[qt];
+    store_partial(st, qt, vq[qt], part_o + (row * (topk - 1) + slq[qt]) * D,
+                  part_lse + (size_t)slq[qt] * ls + row);
   }
 }
 
@@ -679,7 +680,8 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, const uint16_t* __restrict__ part_o,
-    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const float* __restrict__ part_lse, size_t ls, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
   const int c = blockIdx.y;
   const int gi = blockIdx.z % ng, b = blockIdx.z / ng;
@@ -727,8 +729,8 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const int t = vq[qt] ? tpos[qt] : 0;
-        const size_t prow = (sq.prow(b, gi * G + hl, ngq) + t) * (topk - 1);
-        merge_store(st, qt, vq[qt], nh, part_o + prow * D, part_lse + prow,
+        const size_t row = sq.prow(b, gi * G + hl, ngq) + t;
+        merge_store(st, qt, vq[qt], nh, part_o + row * (topk - 1) * D, part_lse + row, ls,
                     out + ((size_t)((size_t)tok0 + t) * hq + g * G + hl) * D,
                     lse + sq.lrow(b, g * G + hl, hq) + t);
       }
@@ -740,6 +742,14 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
 constexpr int kQT = MOBA_ATTN_QT;
 int history_tile_rows() { return kAttnWaves * 32 * kQT; }
 
+// History partials of one pass (ng kv-heads): o is [row][slot][d] and lse [slot][row],
+// rows as SeqMap::prow numbers them.  The lse of one slot are contiguous over rows, so
+// the 32 rows of a wavefront (mostly consecutive tokens with the same slot) write and
+// read whole 32-byte runs instead of one 4-byte word per (k-1)-float row.
+static size_t part_lse_slot_stride(const Shape& s, int ng) {
+  return s.cu ? (size_t)ng * s.G() * s.total : (size_t)s.b * ng * s.G() * s.T;
+}
+
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
                                const int4* tiles, const int32_t* tile_count,
@@ -750,11 +760,13 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
   if (s.d == 128)
     hipLaunchKernelGGL((attn_history_kernel<128, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
                        st, q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng,
-                       s.nb(), tiles, tile_count, entries, part_o, part_lse);
+                       s.nb(), tiles, tile_count, entries, part_o, part_lse,
+                       part_lse_slot_stride(s, ng));
   else
     hipLaunchKernelGGL((attn_history_kernel<64, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
                        st, q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng,
-                       s.nb(), tiles, tile_count, entries, part_o, part_lse);
+                       s.nb(), tiles, tile_count, entries, part_o, part_lse,
+                       part_lse_slot_stride(s, ng));
   return hipGetLastError();
 }
 
@@ -768,11 +780,11 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
   if (s.d == 128)
     hipLaunchKernelGGL((attn_current_kernel<128, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
                        v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o,
-                       part_lse, out, lse);
+                       part_lse, part_lse_slot_stride(s, ng), out, lse);
   else
     hipLaunchKernelGGL((attn_current_kernel<64, kQT>), grid, dim3(kAttnThreads), 0, st, q, k,
                        v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng, part_o,
-                       part_lse, out, lse);
+                       part_lse, part_lse_slot_stride(s, ng), out, lse);
   return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ Layout make_layout(const Shape& s, int ng) {
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
   const size_t prow = group_part_rows(s, ng);   // history slots only
   L.part_o = take(prow * s.d * sizeof(uint16_t));   // bf16 partial outputs
-  L.part_lse = take(prow * sizeof(float));
+  L.part_lse = take(prow * sizeof(float));          // fp32, slot-major [k-1][rows]
   L.total = off;
   return L;
 }
