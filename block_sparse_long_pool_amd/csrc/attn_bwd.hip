@@ -166,15 +166,27 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     // longest first) for the GA heads hg*GA .. of kv-head group gi; wave w takes head
     // w % GA and token sub-tile w / GA.  Waves past GA*TS (G not dividing the wave
     // count) and heads past G run on zero rows, so every wave reaches every barrier.
-    const int c = blockIdx.y;
+    // Workgroup L (x fastest) runs on XCD L % 8; when the (block, head group) lists
+    // number a multiple of 8, each XCD takes whole lists, so the workgroups that stage
+    // one block's K/V share one L2 (as the forward's current-block kernel does).
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    if ((gridDim.y * gridDim.z) % 8 == 0) {
+      const int L = bx + gridDim.x * (by + gridDim.y * bz);
+      const int xcd = L % 8, i = L / 8;
+      const int list = xcd + 8 * (i / gridDim.x);
+      bx = i % gridDim.x;
+      by = list % gridDim.y;
+      bz = list / gridDim.y;
+    }
+    const int c = by;
     const int GA = G < kBwdWaves ? G : kBwdWaves;   // heads per workgroup
     const int HG = (G + GA - 1) / GA;               // head groups per kv-head
     const int TS = kBwdWaves / GA;                  // 32-token sub-tiles per workgroup
     const int TT = 32 * TS;
-    const int hg = blockIdx.z % HG;
-    gi = (blockIdx.z / HG) % ng;
-    b = blockIdx.z / (HG * ng);
-    const int x = gridDim.x - 1 - blockIdx.x;
+    const int hg = bz % HG;
+    gi = (bz / HG) % ng;
+    b = bz / (HG * ng);
+    const int x = gridDim.x - 1 - bx;
     const int t0 = c * block + x * TT;
     const bool active = wave < GA * TS && hg * GA + wave % GA < G;
     hl = active ? hg * GA + wave % GA : 0;
