@@ -89,46 +89,226 @@ def read_traffic(workload: str):
 
 
 # ------------------------------------------------------------------ CPU oracle
-def cpu_baseline(w, inp, budget_s: float):
-    """The float64 oracle, as it is, on a bounded stratified sample of the workload's
-    rows, one thread; the rate is scaled to the whole workload's algorithmic FLOP."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_worker(job):
+    """One process of the CPU baseline: the oracle, as it is, on its query heads:
+    full gating (centroids of its kv-heads, then the selection of every row of its
+    heads), then attention of a stratified sample of its heads' rows until the
+    deadline.  Inputs come from shared memory as bf16 bits."""
     import numpy as np
+    from multiprocessing import shared_memory
     from threadpoolctl import threadpool_limits
     import oracle
     from workloads import bf16_to_f64
 
-    with threadpool_limits(limits=1):
-        K = bf16_to_f64(inp["k"])
-        V = bf16_to_f64(inp["v"])
-        Q = bf16_to_f64(inp["q"])
-        t0 = time.perf_counter()
-        C = oracle.centroids(K, w.block)
-        t_cent = time.perf_counter() - t0
-        rng = np.random.default_rng(12345)
-        nb = w.seqlen // w.block
-        done, flop, t_rows = 0, 0, 0.0
-        start = time.perf_counter()
-        while time.perf_counter() - start < budget_s:
-            c = done % nb                      # round-robin over query blocks
-            row = (0, int(c * w.block + rng.integers(w.block)), int(rng.integers(w.hq)))
+    (names, shapes, heads, G, B, k, scale, rows, t_attn) = job
+    shm = [shared_memory.SharedMemory(name=n) for n in names]
+    try:
+        q, kk, vv = (np.ndarray(sh, np.uint16, buffer=m.buf) for sh, m in zip(shapes, shm))
+        out = {"gate_s": 0.0, "attn_s": 0.0, "rows": 0, "pairs": 0}
+        with threadpool_limits(limits=1):
+            cache, qs = {}, {}
+            t0 = time.perf_counter()
+            for h in heads:
+                g = h // G
+                if g not in cache:
+                    K = bf16_to_f64(kk[:, :, g:g + 1])
+                    cache[g] = (K, bf16_to_f64(vv[:, :, g:g + 1]), oracle.centroids(K, B))
+                qs[h] = bf16_to_f64(q[:, :, h:h + 1])
+                oracle.select_blocks(qs[h], cache[g][2], B, k)
+            out["gate_s"] = time.perf_counter() - t0
             t1 = time.perf_counter()
-            _, _, sels, _ = oracle.moba_rows(Q, K, V, w.block, w.topk, w.sm_scale, [row], C=C)
-            t_rows += time.perf_counter() - t1
-            n_keys = oracle.attended_keys(sels[0], row[1], w.block, w.seqlen).size
-            flop += 4 * w.head_dim * n_keys
-            done += 1
+            T = q.shape[1]
+            for (t, h) in rows:
+                if time.perf_counter() - t1 > t_attn:
+                    break
+                K, V, C = cache[h // G]
+                # the row's selection from its own gate scores, then one softmax over its
+                # attended keys (the oracle's row functions, as the parity tests use them)
+                _, _, sels, _ = oracle.moba_rows(qs[h], K, V, B, k, scale, [(0, t, 0)], C=C)
+                out["pairs"] += oracle.attended_keys(sels[0], t, B, T).size
+                out["rows"] += 1
+            out["attn_s"] = time.perf_counter() - t1
+        return out
+    finally:
+        for m in shm:
+            m.close()
+
+
+def cpu_baseline(w, inp, budget_s: float, workers: int):
+    """The float64 oracle, as it is, over a process pool on the host's cores: full
+    gating of every row, and attention on a stratified sample of rows (every query
+    block, random token and head) for about ``budget_s`` seconds, extrapolated to the
+    whole workload by attended (query, key) pairs."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    import numpy as np
+
+    arrays = [inp["q"], inp["k"], inp["v"]]
+    shm = []
+    try:
+        for a in arrays:
+            m = shared_memory.SharedMemory(create=True, size=a.nbytes)
+            np.ndarray(a.shape, np.uint16, buffer=m.buf)[...] = a
+            shm.append(m)
+        names = [m.name for m in shm]
+        shapes = [a.shape for a in arrays]
+        G = w.hq // w.hkv
+        rng = np.random.default_rng(12345)
+        nb = w.num_blocks
+        # stratified sample, dealt to the workers by head
+        sample = []
+        for rep in range(64):
+            for c in range(nb):
+                n = min(w.block, w.seqlen - c * w.block)
+                sample.append((int(c * w.block + rng.integers(n)), int(rng.integers(w.hq))))
+        jobs = []
+        for i in range(workers):
+            heads = list(range(i, w.hq, workers))
+            rows = [r for r in sample if r[1] in heads]
+            jobs.append((names, shapes, heads, G, w.block, w.topk, w.sm_scale, rows,
+                         budget_s))
+        jobs = [j for j in jobs if j[2]]
+        ctx = mp.get_context("spawn")
+        t0 = time.perf_counter()
+        with ctx.Pool(len(jobs)) as pool:
+            res = pool.map(_cpu_worker, jobs)
+        wall = time.perf_counter() - t0
+    finally:
+        for m in shm:
+            m.close()
+            m.unlink()
+    gate_wall = max(r["gate_s"] for r in res)
+    attn_wall = max(r["attn_s"] for r in res)
+    pairs = sum(r["pairs"] for r in res)
+    rows = sum(r["rows"] for r in res)
     hist, cur = pair_counts(w.seqlen, w.block, w.topk)
-    total_flop = 4 * w.head_dim * w.batch * w.hq * (hist + cur)
-    est_s = t_cent + t_rows * total_flop / flop
+    total_pairs = w.batch * w.hq * (hist + cur)
+    total_flop = 4 * w.head_dim * total_pairs
+    est_attn = attn_wall * total_pairs / max(pairs, 1)
+    est_s = gate_wall + est_attn
     return {
         "value": total_flop / est_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": len(jobs),
         "kind": "oracle",
-        "sample": (f"{done} rows (round-robin over the {nb} query blocks, random token and "
-                   f"head) of {w.name} in {t_rows:.1f} s plus the full centroid pool "
-                   f"({t_cent:.2f} s); whole-workload time extrapolated by attended "
-                   f"FLOP: {est_s:.0f} s"),
+        "cpu_model": _cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "gating_s": gate_wall,
+        "attention_s_extrapolated": est_attn,
+        "sample": (f"{len(jobs)} processes, one BLAS thread each: full gating of all "
+                   f"{w.batch * w.hq * w.seqlen} rows of {w.name} ({gate_wall:.1f} s), then "
+                   f"attention of {rows} stratified sample rows (every query block, random "
+                   f"token and head; {pairs} attended pairs) in {attn_wall:.1f} s, "
+                   f"extrapolated by attended pairs to {est_attn:.0f} s; whole workload "
+                   f"{est_s:.0f} s (pool wall {wall:.1f} s)"),
+    }
+
+
+# ------------------------------------------------------------------ achievable peaks
+def achievable_peaks(dev):
+    """A bf16 GEMM (torch.matmul, hipBLASLt) and a device copy, timed here, as the
+    achievable MFMA and HBM rates next to the published peaks."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 20
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 2, device=dev, dtype=torch.bfloat16).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {
+        "bf16_gemm_tflops": gemm_tflops,
+        "bf16_gemm_frac_of_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "copy_gbs": copy_gbs,
+        "copy_frac_of_peak": copy_gbs / PEAK_HBM_GBS,
+        "note": f"torch.matmul {n}x{n}x{n} bf16 and a {nbytes >> 30} GiB device copy "
+                "(read + write counted), timed in this run",
+    }
+
+
+# ------------------------------------------------------------------ one workload
+def time_forward(moba, w, inp, dev, steps: int, warmup: int):
+    """ms per whole forward and per stage on resident inputs (stage events recorded by
+    the library on the launch stream in every timed step)."""
+    import torch
+    from workloads import to_torch_bf16
+    q, k, v = (to_torch_bf16(inp[x], dev) for x in "qkv")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.hq, w.seqlen), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.batch, w.hq, w.seqlen, w.topk), dtype=torch.int32, device=dev)
+    ws = moba.alloc_workspace(q, k, w.block, w.topk)
+    for _ in range(warmup):
+        moba.forward(q, k, v, w.block, w.topk, w.sm_scale, workspace=ws, out=out, lse=lse,
+                     idx=idx)
+    stream = torch.cuda.current_stream()
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(moba.STAGES) + 1)]
+           for _ in range(steps)]
+    for evs in sev:
+        for e in evs:
+            e.record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        moba.forward(q, k, v, w.block, w.topk, w.sm_scale, workspace=ws, out=out, lse=lse,
+                     idx=idx, events=sev[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stage = {s_: sum(sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(steps)) / steps
+             for j, s_ in enumerate(moba.STAGES)}
+    return ms, stage
+
+
+def config_summary(w, ms, stage):
+    hist, cur = pair_counts(w.seqlen, w.block, w.topk)
+    flop = 4 * w.head_dim * w.batch * w.hq * (hist + cur)
+    attn_ms = stage["history"] + stage["current"]
+    gb = gate_bytes(w, needed_only=False)
+    return {
+        "ms": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attention_frac_of_bf16_peak": (flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+                                        if attn_ms > 0 else None),
+        "gate_frac_of_hbm_peak": (gb / (stage["gate"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+                                  if stage["gate"] > 0 else None),
+        "stages_ms": stage, "flop": flop,
+        "shape": {"batch": w.batch, "seq_len": w.seqlen, "q_heads": w.hq, "kv_heads": w.hkv,
+                  "head_dim": w.head_dim, "block": w.block, "topk": w.topk,
+                  "recipe": w.recipe},
     }
 
 
@@ -153,6 +333,13 @@ def main(argv=None):
                     help="skip timing packed variable-length sequences")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward pass (dQ, dK, dV) on the same inputs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the forward on the other workloads")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the bf16 GEMM and device copy (achievable peaks)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the CPU oracle baseline (default: the host's CPUs, "
+                         "at most 16)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one elementwise copy (torch.neg) of this many MiB "
                          "of bf16, a kernel of known traffic for scaling HBM counters")
@@ -511,10 +698,32 @@ def main(argv=None):
         }
         print(f"[bench] backward {bms:.2f} ms", file=sys.stderr, flush=True)
         del bws, dq, dk, dv, dout
+    if not a.no_configs:
+        # the forward on the other workloads of the benchmark plan (one GPU each); the
+        # headline line above stays the 128K one
+        del q, k, v, out, lse, idx, ws
+        torch.cuda.empty_cache()
+        result["configs"] = {}
+        for name in ("tiny_2k", "llama8b_32k", "llama8b_64k_b128"):
+            if name == w.name:
+                continue
+            wc = get_workload(name)
+            print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+            ic = make_inputs(wc)
+            cms, cstage = time_forward(moba, wc, ic, dev, steps=max(a.steps, 10), warmup=3)
+            result["configs"][name] = config_summary(wc, cms, cstage)
+            print(f"[bench] {name}: {cms:.3f} ms; stages {cstage}", file=sys.stderr,
+                  flush=True)
+            del ic
+            torch.cuda.empty_cache()
+    if not a.no_peaks:
+        result["achievable_peaks"] = achievable_peaks(dev)
+        print(f"[bench] peaks {result['achievable_peaks']}", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
-        print(f"[bench] CPU oracle baseline (~{a.cpu_seconds:.0f} s)", file=sys.stderr,
-              flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+        workers = a.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        print(f"[bench] CPU oracle baseline ({workers} processes, ~{a.cpu_seconds:.0f} s of "
+              "attention)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds, workers)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -556,7 +556,8 @@ def pool_centroids(k, block: int):
     b, T, hkv, d = k.shape
     _raise(check_args(b, T, hkv, hkv, d, block, 1, 1.0), "moba_pool_centroids")
     ws = _alloc_workspace(stage_workspace_bytes(b, T, hkv, hkv, d, block, 1), k.device)
-    cent = torch.empty((b, hkv, T // block, d), dtype=torch.float32, device=k.device)
+    # a partial last block is a block of its own: nb = ceil(T / block)
+    cent = torch.empty((b, hkv, -(-T // block), d), dtype=torch.float32, device=k.device)
     with torch.cuda.device(k.device):
         st = lib.moba_pool_centroids(k.data_ptr(), b, T, hkv, d, block, cent.data_ptr(),
                                      ws.data_ptr(), ws.numel(), _stream_ptr())
@@ -571,7 +572,7 @@ def gate_topk(q, centroids, block: int, topk: int):
     _need(centroids, "centroids", torch.float32, 4)
     b, T, hq, d = q.shape
     hkv = centroids.shape[1]
-    if centroids.shape != (b, hkv, T // block, d):
+    if centroids.shape != (b, hkv, -(-T // block), d):
         raise ValueError(f"centroids must be [b, hkv, nb, d], got {tuple(centroids.shape)}")
     _raise(check_args(b, T, hq, hkv, d, block, topk, 1.0), "moba_gate_topk")
     ws = _alloc_workspace(stage_workspace_bytes(b, T, hq, hkv, d, block, topk), q.device)
@@ -599,7 +600,7 @@ def build_index(idx, hkv: int, block: int, topk: int, kv_begin: int = 0,
     n = index_entries(b, T, hq, hkv, block, topk, kv_count)
     if n < 0:
         raise ValueError("bad kv range")
-    nb = T // block
+    nb = -(-T // block)
     ws = _alloc_workspace(stage_workspace_bytes(b, T, hq, hkv, 64, block, topk), idx.device)
     offs = torch.empty(b * kv_count * nb + 1, dtype=torch.int32, device=idx.device)
     ent = torch.empty(max(n, 1), dtype=torch.int32, device=idx.device)

@@ -647,8 +647,9 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
       const int e = tl.y + (wave * QT + qt) * 32 + n;
       vq[qt] = e < tl.z;
       const uint32_t ent = vq[qt] ? entries[e] : 0u;
-      slq[qt] = (int)(ent & 31u);
-      const int rr = (int)(ent >> 5);
+      const int sb = entry_slot_bits(topk);
+      slq[qt] = (int)(ent & ((1u << sb) - 1u));
+      const int rr = (int)(ent >> sb);
       tq[qt] = rr / G;
       hlq[qt] = rr % G;
       const uint16_t* qrow = q + ((size_t)((size_t)tok0 + tq[qt]) * hq + g * G + hlq[qt]) * D;

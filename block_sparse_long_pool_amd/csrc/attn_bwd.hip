@@ -158,9 +158,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const int e = tl.y + wave * 32 + n;
     valid = e < tl.z;
     const uint32_t ent = valid ? entries[e] : 0u;
-    slot = (int)(ent & 31u);
-    t = (int)(ent >> 5) / G;
-    hl = (int)(ent >> 5) % G;
+    const int sb = entry_slot_bits(topk);
+    slot = (int)(ent & ((1u << sb) - 1u));
+    t = (int)(ent >> sb) / G;
+    hl = (int)(ent >> sb) % G;
   } else {
     // blockIdx.x: a 32*TS-token tile of block blockIdx.y (from the end of the block,
     // longest first) for the GA heads hg*GA .. of kv-head group gi; wave w takes head
@@ -355,7 +356,7 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_densify_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, SeqMap sq, int hq, int G,
-    int g0, int ng, int nb, const int4* __restrict__ tiles,
+    int g0, int ng, int nb, int sbits, const int4* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     uint16_t* __restrict__ rows, float* __restrict__ meta) {
   constexpr int CPR = D / 8;
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(256) void bwd_densify_kernel(
   const int hb = (g0 + gi) * G, tok0 = sq.tok0(b);
   for (int x = threadIdx.x; x < ne * 2 * CPR; x += 256) {
     const int e = e0 + x / (2 * CPR), which = (x / CPR) & 1, col = (x % CPR) * 8;
-    const uint32_t rr = entries[e] >> 5;
+    const uint32_t rr = entries[e] >> sbits;
     const int t = (int)rr / G, h = hb + (int)rr % G;
     const uint16_t* src = (which ? dout : q) + (((size_t)tok0 + t) * hq + h) * D + col;
     *reinterpret_cast<u32x4_t*>(rows + ((size_t)e * 2 + which) * D + col) =
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(256) void bwd_densify_kernel(
   }
   if ((int)threadIdx.x < ne) {
     const int e = e0 + threadIdx.x;
-    const uint32_t rr = entries[e] >> 5;
+    const uint32_t rr = entries[e] >> sbits;
     const int t = (int)rr / G, h = hb + (int)rr % G;
     const size_t at = sq.lrow(b, h, hq) + t;
     meta[(size_t)e * 2] = lse[at];
@@ -704,8 +705,8 @@ hipError_t launch_bwd_densify(const Shape& s, const uint16_t* q, const uint16_t*
   if (max_tiles <= 0) return hipSuccess;
 #define MOBA_DENSE(DD)                                                                     \
   hipLaunchKernelGGL((bwd_densify_kernel<DD>), dim3(max_tiles), dim3(256), 0, st, q, dout,  \
-                     lse, delta, s.seqs(), s.hq, s.G(), g0, ng, s.nb(), tiles, tile_count,   \
-                     entries, rows, meta)
+                     lse, delta, s.seqs(), s.hq, s.G(), g0, ng, s.nb(),                     \
+                     entry_slot_bits(s.topk), tiles, tile_count, entries, rows, meta)
   if (s.d == 128) MOBA_DENSE(128);
   else MOBA_DENSE(64);
 #undef MOBA_DENSE

@@ -23,7 +23,8 @@
 // rank the lower block first.  Scores closer than ~2^-(23-nbits) relative compare
 // as equal (well inside the 1e-3-relative near-tie band).  Per 32-block tile a lane
 // sorts its keys with bitonic networks and merges them into a running sorted
-// top-KHMAX list.  No branch depends on the data, so the wavefront never diverges.
+// top-KHMAX list (KHMAX = 16, 32 or 64).  No branch depends on the data, so the
+// wavefront never diverges.
 #include "moba_internal.h"
 
 namespace moba {
@@ -248,8 +249,10 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
       }
       bitonic_merge_desc(M);
       if (jt == 0) {
+        // the first tile's keys, sorted, head the list; the rest of a longer list stays
+        // empty (0 ranks below every key), so the list is sorted for the merges below
 #pragma unroll
-        for (int p = 0; p < 32; ++p) L[KHMAX - 32 + p] = M[p];
+        for (int p = 0; p < 32; ++p) L[p] = M[p];
         continue;
       }
 #pragma unroll
@@ -304,10 +307,16 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
   }
 }
 
-// KHMAX: list length (16 or 32) >= topk-1.  D: head_dim.  One wavefront per chunk.
-// three wavefronts per SIMD: the loads of one chunk hide behind the ranking of others
+// KHMAX: list length (16, 32 or 64) >= topk-1.  D: head_dim.  One wavefront per chunk.
+// Three wavefronts per SIMD: the loads of one chunk hide behind the ranking of others;
+// the 64-long list needs the registers of two.
+template <int KHMAX>
+struct GateWaves {
+  static constexpr int value = KHMAX > 32 ? 2 : 3;
+};
+
 template <int D, int KHMAX>
-__global__ __launch_bounds__(kThreads, 3) void gate_topk_kernel(
+__global__ __launch_bounds__(kThreads, GateWaves<KHMAX>::value) void gate_topk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
     const uint16_t* __restrict__ clo, int batch, SeqMap sq, int hq, int hkv, int block,
     int nb, int topk, int nbits, int32_t* __restrict__ idx) {
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 3) void gate_topk_kernel(
 // chunks of one (batch, kv-head) group, blockIdx.y = b * hkv + g, and first copies that
 // kv-head's hi/lo centroids into LDS.
 template <int D, int KHMAX>
-__global__ __launch_bounds__(kThreads, 3) void gate_topk_lds_kernel(
+__global__ __launch_bounds__(kThreads, GateWaves<KHMAX>::value) void gate_topk_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
     const uint16_t* __restrict__ clo, int batch, SeqMap sq, int hq, int hkv, int block,
     int nb, int topk, int nbits, int32_t* __restrict__ idx) {
@@ -389,12 +398,36 @@ hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
   } while (0)
   if (s.d == 128) {
     if (KH <= 16) MOBA_GATE(128, 16);
-    else MOBA_GATE(128, 32);
+    else if (KH <= 32) MOBA_GATE(128, 32);
+    else MOBA_GATE(128, 64);
   } else {
     if (KH <= 16) MOBA_GATE(64, 16);
-    else MOBA_GATE(64, 32);
+    else if (KH <= 32) MOBA_GATE(64, 32);
+    else MOBA_GATE(64, 64);
   }
 #undef MOBA_GATE
+  return hipGetLastError();
+}
+
+int gate_max_history() { return 64; }
+
+// Rows of every (sequence, query head, token) when every causal block is selected:
+// blocks 0 .. c ascending, then -1 (README bullet "Seamlessly Transition between Full
+// and Sparse Attention": with every block selected, MoBA is full attention).
+__global__ __launch_bounds__(kThreads) void idx_all_blocks_kernel(SeqMap sq, int hq,
+                                                                  int block, int topk,
+                                                                  int32_t* __restrict__ idx) {
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (t >= sq.len(b)) return;
+  const int c = t / block;
+  int32_t* row = idx + (sq.lrow(b, h, hq) + t) * topk;
+  for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
+}
+
+hipError_t launch_idx_all_blocks(const Shape& s, int32_t* idx, hipStream_t st) {
+  hipLaunchKernelGGL(idx_all_blocks_kernel, dim3((s.T + kThreads - 1) / kThreads, s.hq, s.b),
+                     dim3(kThreads), 0, st, s.seqs(), s.hq, s.block, s.topk, idx);
   return hipGetLastError();
 }
 

@@ -18,6 +18,16 @@ namespace moba {
 
 constexpr int kChunk = 256;  // rows per chunk == threads per workgroup
 
+// A row's history slots are counted and listed only where the block id first appears
+// in the row.  A selection from the gate never repeats a block; a caller-built idx
+// that does still yields at most min(c, k-1) entries per row, so the lists, tiles and
+// entries stay within the sizes the host derives from the shape.
+__device__ __forceinline__ bool first_in_row(const int32_t* __restrict__ row, int s, int j) {
+  for (int u = 0; u < s; ++u)
+    if (row[u] == j) return false;
+  return true;
+}
+
 int index_chunks(const Shape& s) {
   const long rows = (long)s.T * s.G();
   return (int)((rows + kChunk - 1) / kChunk);
@@ -39,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void index_count_kernel(
     const int32_t* row = idx + (sq.lrow(b, h, hq) + t) * topk;
     for (int s = 0; s < topk - 1; ++s) {
       const int j = row[s];
-      if (j >= 0 && j < c) atomicAdd(&cnt[j], 1);
+      if (j >= 0 && j < c && first_in_row(row, s, j)) atomicAdd(&cnt[j], 1);
     }
   }
   __syncthreads();
@@ -132,23 +142,33 @@ __global__ __launch_bounds__(64) void index_tiles_kernel(
   }
 }
 
+// One workgroup: one chunk of rows and one range of at most kRange blocks (its LDS
+// tables hold 6 ints per block of the range); blockIdx.x = chunk + nchunks * range.
+// The rows are read once per range, so block counts beyond kRange cost extra reads
+// of idx but no more LDS.
+constexpr int kRange = 2048;
+
 __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
     const int32_t* __restrict__ idx, SeqMap sq, int hq, int G, int block, int topk, int nb,
-    int nbits, int g0, int ng, int nchunks, const int32_t* __restrict__ chunk_base,
+    int g0, int ng, int nchunks, const int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ list_offsets, uint32_t* __restrict__ entries,
     long long cap) {
   extern __shared__ int32_t lds[];
-  int32_t* base = lds;            // [nb]  absolute start of this chunk's part of list j
-  int32_t* run = lds + nb;        // [nb]  entries of this chunk already placed
-  int32_t* wcnt = lds + 2 * nb;   // [4][nb] per-wavefront counts of the current slot
-  const int chunk = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
+  const int chunk = blockIdx.x % nchunks, gi = blockIdx.y, b = blockIdx.z;
+  const int j0 = (blockIdx.x / nchunks) * kRange;       // first block of the range
+  const int nr = min(kRange, nb - j0);                   // blocks in the range
+  int32_t* base = lds;            // [nr]  absolute start of this chunk's part of list j
+  int32_t* run = lds + nr;        // [nr]  entries of this chunk already placed
+  int32_t* wcnt = lds + 2 * nr;   // [4][nr] per-wavefront counts of the current slot
+  int nbits = 1;
+  while ((1 << nbits) < nr) ++nbits;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int list0 = (b * ng + gi) * nb;
-  const int32_t* cb = chunk_base + ((size_t)(b * ng + gi) * nchunks + chunk) * nb;
-  for (int j = tid; j < nb; j += kThreads) {
+  const int list0 = (b * ng + gi) * nb + j0;
+  const int32_t* cb = chunk_base + ((size_t)(b * ng + gi) * nchunks + chunk) * nb + j0;
+  for (int j = tid; j < nr; j += kThreads) {
     base[j] = list_offsets[list0 + j] + cb[j];
     run[j] = 0;
-    wcnt[j] = wcnt[nb + j] = wcnt[2 * nb + j] = wcnt[3 * nb + j] = 0;
+    wcnt[j] = wcnt[nr + j] = wcnt[2 * nr + j] = wcnt[3 * nr + j] = 0;
   }
   __syncthreads();
   const long r = (long)chunk * kChunk + tid;
@@ -157,10 +177,11 @@ __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
   const int c = valid ? t / block : 0;
   const int32_t* row = idx + (sq.lrow(b, (g0 + gi) * G + hl, hq) + (valid ? t : 0)) * topk;
   const uint64_t below = (1ull << lane) - 1ull;
+  const int sbits = entry_slot_bits(topk);
   for (int s = 0; s < topk - 1; ++s) {
     int j = valid ? row[s] : -1;
-    const bool has = j >= 0 && j < c;
-    if (!has) j = 0;
+    const bool has = j >= j0 && j < j0 + nr && j < c && first_in_row(row, s, j);
+    j = has ? j - j0 : 0;         // the block's place in the range
     uint64_t peers = __ballot(has);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (j >> bit) & 1;
@@ -169,21 +190,21 @@ __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
     }
     const int rank = __popcll(peers & below);
     const bool leader = has && rank == 0;
-    if (leader) wcnt[wave * nb + j] = __popcll(peers);
+    if (leader) wcnt[wave * nr + j] = __popcll(peers);
     __syncthreads();
     int before = 0;
     if (has) {
-      for (int w = 0; w < wave; ++w) before += wcnt[w * nb + j];
+      for (int w = 0; w < wave; ++w) before += wcnt[w * nr + j];
       const int pos = base[j] + run[j] + before + rank;
       // a well-formed idx never reaches cap; a malformed one must not write past it
-      if (pos < cap) entries[pos] = ((uint32_t)(t * G + hl) << 5) | (uint32_t)s;
+      if (pos < cap) entries[pos] = ((uint32_t)(t * G + hl) << sbits) | (uint32_t)s;
     }
     __syncthreads();
     if (leader && before == 0) {
-      run[j] += wcnt[j] + wcnt[nb + j] + wcnt[2 * nb + j] + wcnt[3 * nb + j];
+      run[j] += wcnt[j] + wcnt[nr + j] + wcnt[2 * nr + j] + wcnt[3 * nr + j];
     }
     __syncthreads();
-    if (leader) wcnt[wave * nb + j] = 0;
+    if (leader) wcnt[wave * nr + j] = 0;
     __syncthreads();
   }
 }
@@ -194,8 +215,7 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
                         uint32_t* entries, long long cap, hipStream_t st) {
   const int nb = s.nb();
   const int nchunks = index_chunks(s);
-  int nbits = 1;
-  while ((1 << nbits) < nb) ++nbits;
+  const int nranges = (nb + kRange - 1) / kRange;
   const int nlists = s.b * ng * nb;
   dim3 grid(nchunks, ng, s.b);
   hipLaunchKernelGGL(index_count_kernel, grid, dim3(kThreads), nb * sizeof(int32_t), st,
@@ -214,9 +234,10 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
                        tile_offsets, tile_m, tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(index_scatter_kernel, grid, dim3(kThreads), 6 * nb * sizeof(int32_t),
-                     st, idx, s.seqs(), s.hq, s.G(), s.block, s.topk, nb, nbits, g0, ng,
-                     nchunks, chunk_counts, list_offsets, entries, cap);
+  const int nr = nb < kRange ? nb : kRange;
+  hipLaunchKernelGGL(index_scatter_kernel, dim3(nchunks * nranges, ng, s.b), dim3(kThreads),
+                     6 * nr * sizeof(int32_t), st, idx, s.seqs(), s.hq, s.G(), s.block,
+                     s.topk, nb, g0, ng, nchunks, chunk_counts, list_offsets, entries, cap);
   return hipGetLastError();
 }
 

@@ -13,9 +13,26 @@ using moba::Shape;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxBlocks = 2048;  // inverted-index LDS tables hold 6 ints per block
+// The gate's rank keys keep 23 - ceil(log2 nb) mantissa bits of a score: at 8192 blocks
+// that is 10 bits, a resolution below the 1e-3-relative near-tie band.
+constexpr int kMaxBlocks = 8192;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// topk >= the number of blocks of the longest sequence: every row selects every causal
+// block, so the layer is dense causal attention (README bullet "Seamlessly Transition
+// between Full and Sparse Attention").  That case runs as one block of the whole
+// sequence, with no gate, index or history partials.
+bool all_blocks(int seqlen, int block, int topk) { return (long long)topk * block >= seqlen; }
+bool all_blocks(const Shape& s) { return all_blocks(s.T, s.block, s.topk); }
+
+// the dense causal form of a shape: one block of the whole (longest) sequence, top-1
+Shape dense_shape(const Shape& s) {
+  Shape d = s;
+  d.block = (s.T + 15) / 16 * 16;
+  d.topk = 1;
+  return d;
+}
 
 int check(int batch, int seqlen, int hq, int hkv, int head_dim, int block, int topk,
           float scale) {
@@ -27,11 +44,14 @@ int check(int batch, int seqlen, int hq, int hkv, int head_dim, int block, int t
   if (scale <= 0.f) return MOBA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return MOBA_ERR_UNSUPPORTED;
   if (block < 16 || block % 16 != 0) return MOBA_ERR_UNSUPPORTED;
-  if (topk > 33) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)batch * seqlen * hq >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  if (all_blocks(seqlen, block, topk)) return MOBA_OK;
+  // sparse: topk - 1 history slots ranked by the gate, index rows of 32 - sbits bits
+  if (topk - 1 > moba::gate_max_history()) return MOBA_ERR_UNSUPPORTED;
   if ((seqlen + block - 1) / block > kMaxBlocks) return MOBA_ERR_UNSUPPORTED;
   const long long G = hq / hkv;
-  if ((long long)seqlen * G >= (1ll << 27)) return MOBA_ERR_UNSUPPORTED;
-  if ((long long)batch * seqlen * hq >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  if ((long long)seqlen * G >= (1ll << (32 - moba::entry_slot_bits(topk))))
+    return MOBA_ERR_UNSUPPORTED;
   return MOBA_OK;
 }
 
@@ -172,6 +192,10 @@ size_t moba_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim
   if (min_bytes) *min_bytes = 0;
   if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
   const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  if (all_blocks(s)) {          // dense causal: no workspace is used
+    if (min_bytes) *min_bytes = kAlign;
+    return kAlign;
+  }
   const Layout one = make_layout(s, 1);
   if (!layout_ok(one)) return 0;
   if (min_bytes) *min_bytes = one.total;
@@ -249,6 +273,26 @@ int run_forward(const Shape& s, const void* q, const void* k, const void* v, flo
                 void* const* stage_events) {
   if (!q || !k || !v || !out || !lse || !idx || !workspace) return MOBA_ERR_INVALID_ARG;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
+  hipStream_t hs0 = static_cast<hipStream_t>(stream);
+  if (all_blocks(s)) {
+    // every causal block selected: idx lists them all, and the current-block kernel over
+    // one block of the whole sequence is the attention; pool, index and history steps
+    // are empty
+    StageClock clock;
+    if (!clock.begin(hs0, stage_ms != nullptr, stage_events)) return MOBA_ERR_HIP;
+    MOBA_TRY(clock.mark(0));
+    MOBA_TRY(moba::launch_idx_all_blocks(s, idx, hs0));
+    MOBA_TRY(clock.mark(1));
+    MOBA_TRY(clock.mark(2));
+    MOBA_TRY(clock.mark(3));
+    MOBA_TRY(moba::launch_attn_current(dense_shape(s), static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k),
+                                       static_cast<const uint16_t*>(v), scale, 0, s.hkv,
+                                       nullptr, nullptr, static_cast<uint16_t*>(out), lse,
+                                       hs0));
+    MOBA_TRY(clock.mark(4));
+    return clock.finish(stage_ms);
+  }
   const int hkv = s.hkv;
   // the largest group of kv-heads whose buffers fit
   int ng = hkv;
@@ -294,6 +338,11 @@ int run_forward(const Shape& s, const void* q, const void* k, const void* v, flo
                                          tile_offsets + nlc, (int)Lc.max_tiles, entries,
                                          po, pl, hs));
       MOBA_TRY(clock.mark(3));
+    } else {
+      // no history slots: the index and history stages are empty, but their
+      // boundaries are still recorded so that every stage time is well defined
+      MOBA_TRY(clock.mark(2));
+      MOBA_TRY(clock.mark(3));
     }
     MOBA_TRY(moba::launch_attn_current(s, qb, kb, vb, scale, g0, ngc, po, pl,
                                        static_cast<uint16_t*>(out), lse, hs));
@@ -330,7 +379,9 @@ int varlen_shape(int nseq, int total, int max_seqlen, int hq, int hkv, int head_
 }
 
 // backward workspace of a validated shape: all kv-heads at once, *min_bytes one per pass
-size_t bwd_workspace(const Shape& s, size_t* min_bytes) {
+size_t bwd_workspace(const Shape& s0, size_t* min_bytes) {
+  // every causal block selected: the backward of dense causal attention
+  const Shape s = all_blocks(s0) ? dense_shape(s0) : s0;
   if (!moba::bwd_supported(s)) return 0;
   const BwdLayout one = make_bwd_layout(s, 1);
   if (!bwd_layout_ok(one)) return 0;
@@ -343,12 +394,15 @@ size_t bwd_workspace(const Shape& s, size_t* min_bytes) {
 }
 
 // the whole backward for a validated shape (a uniform batch or packed sequences)
-int run_backward(const Shape& s, const void* q, const void* k, const void* v,
+int run_backward(const Shape& s0, const void* q, const void* k, const void* v,
                  const void* out, const float* lse, const int32_t* idx, const void* dout,
                  float scale, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !out || !lse || !idx || !dout || !dq || !dk || !dv || !workspace)
     return MOBA_ERR_INVALID_ARG;
+  // every causal block selected (the only valid idx then): the backward of dense causal
+  // attention, one block of the whole sequence with no history part
+  const Shape s = all_blocks(s0) ? dense_shape(s0) : s0;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOBA_ERR_INVALID_ARG;
   if (!moba::bwd_supported(s)) return MOBA_ERR_UNSUPPORTED;
   const int hkv = s.hkv;
@@ -417,12 +471,14 @@ int moba_forward(const void* q, const void* k, const void* v, int batch, int seq
 int moba_dense_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
                        int hq, int hkv, int head_dim, float scale, void* out, float* lse,
                        void* stream) {
-  // one block of seqlen tokens and topk 1: the current-block kernel alone is dense
-  // causal attention, with no history part to merge
-  const int st = check(batch, seqlen, hq, hkv, head_dim, seqlen, 1, scale);
+  // one block of seqlen tokens (rounded up to whole 16-key subtiles; keys past seqlen
+  // are never read) and topk 1: the current-block kernel alone is dense causal
+  // attention, with no history part to merge
+  const int blk = (seqlen + 15) / 16 * 16;
+  const int st = check(batch, seqlen, hq, hkv, head_dim, blk > 0 ? blk : 16, 1, scale);
   if (st != MOBA_OK) return st;
   if (!q || !k || !v || !out || !lse) return MOBA_ERR_INVALID_ARG;
-  const Shape s{batch, seqlen, hq, hkv, head_dim, seqlen, 1};
+  const Shape s{batch, seqlen, hq, hkv, head_dim, blk, 1};
   if (moba::launch_attn_current(s, static_cast<const uint16_t*>(q),
                                 static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), scale, 0, hkv, nullptr,
@@ -513,6 +569,10 @@ size_t moba_varlen_workspace_bytes(int nseq, int total, int max_seqlen, int hq, 
   if (varlen_shape(nseq, total, max_seqlen, hq, hkv, head_dim, block, topk, 1.f, &kDummy,
                    &s) != MOBA_OK)
     return 0;
+  if (all_blocks(s)) {          // dense causal: no workspace is used
+    if (min_bytes) *min_bytes = kAlign;
+    return kAlign;
+  }
   const Layout one = make_layout(s, 1);
   if (!layout_ok(one)) return 0;
   if (min_bytes) *min_bytes = one.total;
@@ -559,7 +619,20 @@ int moba_key_short_conv(const void* k, const float* weight, const int32_t* cu_se
                                           static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
 // ------------------------------------------------------------------- stages
+namespace {
+// The index stage packs a slot into 5 or 6 bits: at most 64 history slots, and the
+// limits of a sparse shape (which check() waives when every block is selected).
+bool index_unsupported(int seqlen, int hq, int hkv, int block, int topk) {
+  if (topk - 1 > moba::gate_max_history()) return true;
+  if ((seqlen + block - 1) / block > kMaxBlocks) return true;
+  return (long long)seqlen * (hq / hkv) >= (1ll << (32 - moba::entry_slot_bits(topk)));
+}
+}  // namespace
+
+extern "C" {
 size_t moba_stage_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim,
                                   int block, int topk) {
   if (check(batch, seqlen, hq, hkv, head_dim, block, topk, 1.f) != MOBA_OK) return 0;
@@ -595,6 +668,8 @@ int moba_gate_topk(const void* q, const float* centroids, int batch, int seqlen,
   if (st != MOBA_OK) return st;
   if (!q || !centroids || !idx || !workspace) return MOBA_ERR_INVALID_ARG;
   const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  if (all_blocks(s)) return hip_status(moba::launch_idx_all_blocks(s, idx,
+                                                                   static_cast<hipStream_t>(stream)));
   const size_t n = (size_t)s.b * s.hkv * s.nb() * s.d;
   const size_t half = align_up(n * sizeof(uint16_t));
   if (2 * half > workspace_bytes) return MOBA_ERR_WORKSPACE;
@@ -609,6 +684,7 @@ int moba_gate_topk(const void* q, const float* centroids, int batch, int seqlen,
 int64_t moba_index_entries(int batch, int seqlen, int hq, int hkv, int block, int topk,
                            int kv_count) {
   if (check(batch, seqlen, hq, hkv, 64, block, topk, 1.f) != MOBA_OK) return -1;
+  if (index_unsupported(seqlen, hq, hkv, block, topk)) return -1;
   if (kv_count <= 0 || kv_count > hkv) return -1;
   const Shape s{batch, seqlen, hq, hkv, 64, block, topk};
   return (int64_t)s.b * kv_count * s.G() * entries_per_head(s);
@@ -623,6 +699,7 @@ int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
   if (!idx || !list_offsets || !entries || !workspace) return MOBA_ERR_INVALID_ARG;
   if (kv_begin < 0 || kv_count <= 0 || kv_begin + kv_count > hkv) return MOBA_ERR_INVALID_ARG;
   if (topk < 2) return MOBA_ERR_UNSUPPORTED;  // no history slots, no index
+  if (index_unsupported(seqlen, hq, hkv, block, topk)) return MOBA_ERR_UNSUPPORTED;
   const Shape s{batch, seqlen, hq, hkv, 64, block, topk};
   const size_t nlists = (size_t)s.b * kv_count * s.nb();
   const size_t cc = align_up((size_t)s.b * kv_count * moba::index_chunks(s) * s.nb() *

@@ -88,6 +88,13 @@ struct SeqMap {
   }
 };
 
+// Inverted-index entries pack (r << sbits) | slot, r = t*G + h%G the row of a kv-head
+// and slot < topk - 1 the position of the block in the row's selection.  Up to 32
+// history slots take 5 bits, up to 64 take 6 (rows then have 26 bits).
+__host__ __device__ __forceinline__ int entry_slot_bits(int topk) {
+  return topk - 1 > 32 ? 6 : 5;
+}
+
 struct Shape {
   int b, T, hq, hkv, d, block, topk;
   const int32_t* cu = nullptr;   // packed sequences (device), see SeqMap
@@ -108,6 +115,10 @@ hipError_t launch_centroid_split(const Shape& s, const float* cent, uint16_t* ch
 // (a2) gate + top-k
 hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
                        const uint16_t* clo, int32_t* idx, hipStream_t st);
+// every row selects all of its causal blocks (topk >= the number of blocks): blocks
+// 0 .. t / block ascending, then -1 up to topk
+hipError_t launch_idx_all_blocks(const Shape& s, int32_t* idx, hipStream_t st);
+int gate_max_history();                // the most history slots the gate ranks
 // (a3) inverted index over kv-heads [g0, g0 + ng)
 int index_chunks(const Shape& s);
 hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int tile_m,

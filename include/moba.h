@@ -38,10 +38,16 @@
  *   centroids    [b, hkv, nb, d] float32
  *
  * Supported shapes: head_dim 64 or 128; hq % hkv == 0; block >= 16 and a multiple of
- * 16; 1 <= topk <= 33 (topk counts the current block); scale finite and > 0;
- * seqlen * G < 2^27; at most 2048 blocks.  seqlen need not be a multiple of block: the
- * last block is then partial.  It is only ever a current block (no later token routes
- * to it), so routing is unchanged; its centroid is the mean of the keys present.
+ * 16; scale finite and > 0; batch * seqlen * hq < 2^31; topk >= 1 (topk counts the
+ * current block).  seqlen need not be a multiple of block: the last block is then
+ * partial.  It is only ever a current block (no later token routes to it), so routing
+ * is unchanged; its centroid is the mean of the keys present.
+ *   topk >= nb: every row selects every causal block, so the layer is dense causal
+ *     attention (README bullet "Seamlessly Transition between Full and Sparse
+ *     Attention"); any such topk is accepted, idx lists blocks 0 .. c then -1, and the
+ *     library runs the dense kernel without gate, index or workspace.
+ *   topk < nb: at most 64 history slots (topk <= 65), at most 8192 blocks, and
+ *     seqlen * G < 2^27 (2^26 with more than 32 history slots).
  * Anything else returns MOBA_ERR_UNSUPPORTED or MOBA_ERR_INVALID_ARG before any device
  * work.
  *
@@ -67,15 +73,22 @@ typedef enum {
   MOBA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } moba_status;
 
-/* Validates a problem shape on the host (touches no device).  Returns MOBA_OK,
+/* Validates a problem shape on the host (touches no device): the block partition, the
+ * top-k routing with the current block counted, and the grouped query heads that
+ * moba_forward computes ("MoBA: Mixture of Block Attention for Long-Context LLMs",
+ * paper summary page, "Approach"), against the limits listed above.  Returns MOBA_OK,
  * MOBA_ERR_INVALID_ARG or MOBA_ERR_UNSUPPORTED. */
 int moba_check_args(int batch, int seqlen, int hq, int hkv, int head_dim, int block,
                     int topk, float scale);
 
-/* Bytes of device workspace moba_forward uses.  Returns the size that processes all
- * kv-heads in one pass, and stores in *min_bytes (if not NULL) the size that
- * processes one kv-head per pass.  Any size in between also works: moba_forward
- * then loops over groups of kv-heads.  Returns 0 if the shape is not supported. */
+/* Bytes of device workspace moba_forward uses: the centroids, the inverted index of
+ * the gathered query tiles and their partial results (FlashMoBA story, paragraph on
+ * Gather-and-Densify: the queries that chose a block are gathered and run as one dense
+ * tile).  Returns the size that processes all kv-heads in one pass, and stores in
+ * *min_bytes (if not NULL) the size that processes one kv-head per pass.  Any size in
+ * between also works: moba_forward then loops over groups of kv-heads.  With
+ * topk >= nb (dense causal attention) no workspace is used and both sizes are 256.
+ * Returns 0 if the shape is not supported. */
 size_t moba_workspace_bytes(int batch, int seqlen, int hq, int hkv, int head_dim,
                             int block, int topk, size_t* min_bytes);
 
@@ -108,8 +121,8 @@ int moba_forward_profile(const void* q, const void* k, const void* v, int batch,
  * selected, the layer is full attention).  The same result as moba_forward with
  * topk >= seqlen / block, without gating or index: out[b,t,h] = softmax over keys
  * u <= t of scale * q.k_u, times V; lse as for moba_forward.  Layouts, dtypes and
- * stream semantics as for moba_forward; needs no workspace.  seqlen must be a
- * multiple of 16; the other shape limits are moba_forward's with block = seqlen. */
+ * stream semantics as for moba_forward; needs no workspace.  Any seqlen >= 1; the
+ * other shape limits are moba_forward's. */
 int moba_dense_forward(const void* q, const void* k, const void* v, int batch, int seqlen,
                        int hq, int hkv, int head_dim, float scale, void* out, float* lse,
                        void* stream);
@@ -255,7 +268,9 @@ int moba_key_short_conv(const void* k, const float* weight, const int32_t* cu_se
                         int batch, int seqlen, int total, int hkv, int head_dim, int block,
                         int width, void* out, void* stream);
 
-/* A static, human-readable message for a status code. */
+/* A static, human-readable message for a status code returned by any entry point of
+ * this library (the error reporting of the calls above; it computes nothing of the
+ * method itself).  Never NULL; unknown codes give "unknown status". */
 const char* moba_strerror(int status);
 
 /* ---------------------------------------------------------------------------
@@ -297,8 +312,10 @@ int64_t moba_index_entries(int batch, int seqlen, int hq, int hkv, int block, in
  *   list_offsets  int32 [batch * kv_count * nb + 1]: list L = (b * kv_count +
  *                 (g - kv_begin)) * nb + j holds entries[list_offsets[L] ..
  *                 list_offsets[L + 1]).
- *   entries       uint32 [moba_index_entries(...)]: ((t * G + h % G) << 5) | slot,
- *                 slot = the position of j in the row of idx.
+ *   entries       uint32 [moba_index_entries(...)]: ((t * G + h % G) << sb) | slot,
+ *                 slot = the position of j in the row of idx, sb = 5 bits for up to
+ *                 32 history slots (topk <= 33) and 6 beyond.  A block id that a row
+ *                 repeats is listed at its first slot only.  topk <= 65. 
  * Lists are ordered by (chunk of 256 rows, slot, row), rows being r = t * G + h % G:
  * a deterministic order, identical on every run. */
 int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,

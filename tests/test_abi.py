@@ -48,16 +48,25 @@ def test_check_args_codes(moba):
     assert moba.check_args(1, 128, 1, 1, 96, 16, 1, 1.0) == E_UNS          # head_dim
     assert moba.check_args(1, 128, 1, 1, 64, 24, 1, 1.0) == E_UNS          # block % 16
     assert moba.check_args(1, 130, 1, 1, 64, 16, 1, 1.0) == ok             # partial last block
-    assert moba.check_args(1, 16 * 2049, 1, 1, 64, 16, 1, 1.0) == E_UNS    # > 2048 blocks
+    assert moba.check_args(1, 16 * 8192, 1, 1, 64, 16, 2, 1.0) == ok       # 8192 blocks
+    assert moba.check_args(1, 16 * 8193, 1, 1, 64, 16, 2, 1.0) == E_UNS    # > 8192 blocks
+    # topk >= the number of blocks: dense causal attention, any topk and block count
+    assert moba.check_args(1, 16 * 8193, 1, 1, 64, 16, 8193, 1.0) == ok
+    assert moba.check_args(1, 4096, 4, 2, 128, 128, 40, 1.0) == ok         # topk 40 > 32 blocks
     # the backward takes a partial last block as well
     assert moba.backward_workspace_bytes(1, 130, 1, 1, 64, 16, 2)[0] > 0
     assert moba.backward_workspace_bytes(1, 128, 1, 1, 64, 16, 2)[0] > 0
     assert moba.backward_varlen_workspace_bytes(2, 300, 200, 4, 2, 64, 16, 3)[0] > 0
     assert moba.backward_varlen_workspace_bytes(2, 300, 400, 4, 2, 64, 16, 3) == (0, 0)
-    assert moba.check_args(1, 128, 1, 1, 64, 16, 34, 1.0) == E_UNS         # topk > 33
-    assert moba.check_args(1, 128, 1, 1, 64, 16, 33, 1.0) == 0
+    assert moba.check_args(1, 2048, 1, 1, 64, 16, 65, 1.0) == 0            # 64 history slots
+    assert moba.check_args(1, 2048, 1, 1, 64, 16, 66, 1.0) == E_UNS        # 65 history slots
+    assert moba.check_args(1, 2048, 1, 1, 64, 16, 128, 1.0) == 0           # topk = nb: dense
+    assert moba.check_args(1, 128, 1, 1, 64, 16, 34, 1.0) == 0             # topk > nb
     assert moba.check_args(1, 128, 1, 1, 64, 16, 2, -1.0) == E_UNS         # scale <= 0
     assert moba.check_args(1, 1 << 27, 1, 1, 64, 1 << 20, 2, 1.0) == E_UNS  # T*G too big
+    # 33 .. 64 history slots take 6 slot bits: rows t*G + h%G must fit 26 bits
+    assert moba.check_args(1, (1 << 26) // 4, 4, 1, 64, 4096, 40, 1.0) == E_UNS
+    assert moba.check_args(1, (1 << 26) // 4 - 16, 4, 1, 64, 4096, 40, 1.0) == 0
 
 
 def test_workspace_sizes(moba):
@@ -68,6 +77,13 @@ def test_workspace_sizes(moba):
     assert mn < full / 4
     assert moba.workspace_bytes(1, 130, 1, 1, 64, 16, 2)[0] > 0    # partial last block
     assert moba.workspace_bytes(1, 130, 1, 1, 96, 16, 2) == (0, 0)    # head_dim 96
+    # topk >= the number of blocks runs as dense causal attention and uses no workspace
+    assert moba.workspace_bytes(1, 131072, 32, 8, 128, 4096, 32) == (256, 256)
+    assert moba.workspace_bytes(1, 131072, 32, 8, 128, 4096, 31)[0] > 256
+    # the backward of that case needs D = rowsum(dO * out), Hq * T floats, and a few
+    # aligned words of an empty index
+    full, mn = moba.backward_workspace_bytes(1, 1000, 4, 2, 64, 128, 8)
+    assert full == mn and 4 * 1000 * 4 <= full <= 4 * 1000 * 4 + 8 * 256
 
 
 def test_index_entry_count_closed_form(moba):
@@ -75,6 +91,9 @@ def test_index_entry_count_closed_form(moba):
     assert moba.index_entries(1, 131072, 32, 8, 4096, 12, 8) == 37_486_592
     assert moba.index_entries(1, 131072, 32, 8, 4096, 12, 1) == 37_486_592 // 8
     assert moba.index_entries(1, 131072, 32, 8, 4096, 12, 9) == -1
+    # the index packs at most 64 history slots
+    assert moba.index_entries(1, 16 * 65, 1, 1, 16, 65, 1) > 0
+    assert moba.index_entries(1, 16 * 66, 1, 1, 16, 66, 1) == -1
 
 
 def test_strerror(moba):
@@ -102,8 +121,11 @@ def test_forward_rejects_bad_args_before_any_launch(moba):
     assert lib.moba_varlen_workspace_bytes(2, 300, 200, 1, 1, 96, 16, 2, None) == 0
     assert lib.moba_varlen_workspace_bytes(2, 300, 400, 1, 1, 64, 16, 2, None) == 0
     assert lib.moba_varlen_workspace_bytes(2, 300, 200, 1, 1, 64, 16, 2, None) > 0
-    # dense causal attention: seqlen a multiple of 16, pointers checked on the host
+    # dense causal attention: any seqlen (130 is not a multiple of 16), pointers checked
+    # on the host
     assert lib.moba_dense_forward(None, None, None, 1, 130, 1, 1, 64, 0.125, None, None,
+                                  None) == -1
+    assert lib.moba_dense_forward(None, None, None, 1, 130, 1, 1, 96, 0.125, None, None,
                                   None) == -2
     assert lib.moba_dense_forward(None, None, None, 1, 128, 1, 1, 64, 0.125, None, None,
                                   None) == -1

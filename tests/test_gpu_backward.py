@@ -217,3 +217,124 @@ def test_backward_32k_sampled_rows_and_sums(moba):
         # each of T bf16 elements carries <= u relative rounding: bound by u * sum |.|
         assert np.all(np.abs(got_v - want_v) <= U * np.abs(dv[0, :, g]).sum(axis=0) + 1e-6)
         assert np.all(np.abs(got_k) <= U * np.abs(dk[0, :, g]).sum(axis=0) + 1e-6)
+
+
+def _rows_with_oracle_selection(Q, C, gi, B, topk, cand):
+    """The candidate rows [(t, h)] whose GPU selection equals the oracle's, with that
+    selection; rows at a near tie (where the two may legitimately differ) are left out,
+    and any other difference fails."""
+    from parity_util import check_selection_row
+    rows = [(0, int(t), int(h)) for t, h in cand]
+    scores = oracle.gate_scores_rows(Q, C, B, rows)
+    sels = oracle.select_rows(scores, [t // B for _, t, _ in rows], topk)
+    keep = []
+    for (_, t, h), S, s in zip(rows, sels, scores):
+        g = gi[0, h, t]
+        if np.array_equal(np.asarray(S), g[g >= 0]):
+            keep.append((t, h, S))
+        else:
+            ok, exempt, _ = check_selection_row(g, s, t // B, topk)
+            assert ok and exempt, (t, h, g.tolist(), S)
+    return keep
+
+
+def test_backward_128k_sampled_and_sparse_upstream(moba):
+    """Llama-3.1-8B heads at 128K (B=4096, top-12), the configuration the benchmark
+    times, where one block's list holds up to ~360K gathered rows.
+
+    1. dout i.i.d. N(0,1): dq of sampled rows in every query block (the first and last
+       token of blocks 11, 12 and 31 among them) against the oracle row by row, and
+       for every kv-head the sums over keys, which hold at any size:
+       sum_u dv_u = sum of dout over the group's rows, sum_u dk_u = 0.
+    2. dout zero except on a sample R of rows spread over all query blocks: every
+       gradient is then a sum over R alone (dk_u, dv_u collect scale p (dO.v - D) q and
+       p dO only from rows with dO != 0, and dq_t = 0 wherever dO_t = 0), so the oracle
+       gives dk and dv of EVERY key and every kv-head, while the GPU still builds and
+       walks the full-length lists of the history blocks."""
+    w = get_workload("llama8b_128k")
+    B, T, G, sc, k_ = w.block, w.seqlen, w.hq // w.hkv, w.sm_scale, w.topk
+    say("[bwd128k] generating inputs")
+    inp = make_inputs(w)
+    g_bits = make_output_grad(w)
+    q, k, v = (dev(inp[x]) for x in "qkv")
+    say("[bwd128k] GPU forward + backward (dense dout)")
+    out, lse, idx = moba.forward(q, k, v, B, k_, sc)
+    dq, dk, dv = moba.backward(q, k, v, out, lse, idx, dev(g_bits), B, k_, sc)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    dq_s = dq.float().cpu().numpy()
+    dk_f, dv_f = f64(dk), f64(dv)
+    del dq, dk, dv
+    K, V = bf16_to_f64(inp["k"]), bf16_to_f64(inp["v"])
+    Q = bf16_to_f64(inp["q"])
+    C = oracle.centroids(K, B)
+    rng = np.random.default_rng(128)
+
+    # 1. sampled dq rows under the dense upstream gradient, and the key sums
+    cand = [(int(c * B + rng.integers(B)), int(rng.integers(w.hq)))
+            for c in range(w.num_blocks) for _ in range(4)]
+    cand += [(t, int(rng.integers(w.hq))) for c in (11, 12, 31) for t in (c * B, c * B + B - 1)]
+    rows = _rows_with_oracle_selection(Q, C, gi, B, k_, cand)
+    assert len(rows) >= len(cand) - 8
+    say(f"[bwd128k] dq of {len(rows)} sampled rows")
+    got, ref = [], []
+    for t, h, S in rows:
+        keys = oracle.attended_keys(S, t, B, T)
+        r, _, _ = oracle.attend_row_grad(Q[0, t, h], K[0, :, h // G], V[0, :, h // G], keys,
+                                         sc, bf16_to_f64(g_bits[0, t, h]))
+        got.append(dq_s[0, t, h])
+        ref.append(r)
+    s = grad_stats("dq rows", np.array(got, np.float64), np.array(ref))
+    assert s["max_rel"] <= MAX_REL and s["mean_rel"] <= MEAN_REL
+    say("[bwd128k] sums over keys, every kv-head")
+    for g in range(w.hkv):
+        want_v = bf16_to_f64(g_bits[0, :, g * G:(g + 1) * G]).sum(axis=(0, 1))
+        assert np.all(np.abs(dv_f[0, :, g].sum(axis=0) - want_v)
+                      <= U * np.abs(dv_f[0, :, g]).sum(axis=0) + 1e-6)
+        assert np.all(np.abs(dk_f[0, :, g].sum(axis=0))
+                      <= U * np.abs(dk_f[0, :, g]).sum(axis=0) + 1e-6)
+    del dk_f, dv_f, dq_s
+
+    # 2. the upstream gradient on a sample R of rows only
+    cand = [(int(c * B + rng.integers(B)), int(rng.integers(w.hq)))
+            for c in range(w.num_blocks) for _ in range(3)]
+    cand += [(c * B, 0) for c in (11, 12)] + [(T - 1, w.hq - 1)]
+    R = _rows_with_oracle_selection(Q, C, gi, B, k_, dict.fromkeys(cand))
+    sparse = np.zeros_like(g_bits)
+    for t, h, _ in R:
+        sparse[0, t, h] = g_bits[0, t, h]
+    say(f"[bwd128k] GPU backward with dout on {len(R)} rows only")
+    dq2, dk2, dv2 = moba.backward(q, k, v, out, lse, idx, dev(sparse), B, k_, sc)
+    torch.cuda.synchronize()
+    in_r = torch.zeros((T, w.hq), dtype=torch.bool, device="cuda")
+    for t, h, _ in R:
+        in_r[t, h] = True
+    assert bool((dq2[0][~in_r] == 0).all()), "dq of a row without upstream gradient"
+    dq_r = {(t, h): dq2[0, t, h].float().cpu().numpy().astype(np.float64) for t, h, _ in R}
+    del dq2, in_r
+    dk2, dv2 = f64(dk2), f64(dv2)
+    rk = np.zeros(K.shape[1:])
+    rv = np.zeros(V.shape[1:])
+    touched = np.zeros(K.shape[1:3], bool)
+    got, ref = [], []
+    for t, h, S in R:
+        g = h // G
+        keys = oracle.attended_keys(S, t, B, T)
+        dqr, dkr, dvr = oracle.attend_row_grad(Q[0, t, h], K[0, :, g], V[0, :, g], keys, sc,
+                                               bf16_to_f64(sparse[0, t, h]))
+        rk[keys, g] += dkr
+        rv[keys, g] += dvr
+        touched[keys, g] = True
+        got.append(dq_r[(t, h)])
+        ref.append(dqr)
+    s = grad_stats("dq of R", np.array(got), np.array(ref))
+    assert s["max_rel"] <= MAX_REL and s["mean_rel"] <= MEAN_REL
+    say(f"[bwd128k] dk, dv of every key ({int(touched.sum())} (key, kv-head) pairs "
+        "touched by R)")
+    assert np.all(dk2[0][~touched] == 0) and np.all(dv2[0][~touched] == 0)
+    for g in range(w.hkv):
+        m = touched[:, g]
+        sk = grad_stats(f"dk g{g}", dk2[0, m, g], rk[m, g])
+        sv = grad_stats(f"dv g{g}", dv2[0, m, g], rv[m, g])
+        for s in (sk, sv):
+            assert s["max_rel"] <= MAX_REL and s["mean_rel"] <= MEAN_REL

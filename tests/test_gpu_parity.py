@@ -32,6 +32,10 @@ def moba():
     return m
 
 
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to("cuda")
+
+
 def dev(bits):
     return to_torch_bf16(bits, "cuda")
 
@@ -159,7 +163,7 @@ def cpu_index(idx, hkv, B, topk, kv_begin, kv_count, chunk=256):
     """The documented list order, (chunk of 256 rows, slot, row), built on the CPU."""
     b, hq, T, _ = idx.shape
     G = hq // hkv
-    nb = T // B
+    nb = -(-T // B)
     lists = [[] for _ in range(b * kv_count * nb)]
     for bi in range(b):
         for gi in range(kv_count):
@@ -171,7 +175,9 @@ def cpu_index(idx, hkv, B, topk, kv_begin, kv_count, chunk=256):
                 for s in range(topk - 1):
                     js = rows[c0:c0 + chunk, s]
                     cs = c[c0:c0 + chunk]
-                    for rr in np.nonzero((js >= 0) & (js < cs))[0]:
+                    # a block id repeated within a row is listed at its first slot only
+                    first = ~(rows[c0:c0 + chunk, :s] == js[:, None]).any(axis=1)
+                    for rr in np.nonzero((js >= 0) & (js < cs) & first)[0]:
                         r = c0 + rr
                         lists[(bi * kv_count + gi) * nb + js[rr]].append((r << 5) | s)
     offs = np.zeros(len(lists) + 1, np.int64)
@@ -197,6 +203,57 @@ def test_inverted_index(moba, b, T, hq, hkv, B, k, kv_begin, kv_count):
     torch.cuda.synchronize()
     assert torch.equal(offs, offs2) and torch.equal(ent, ent2)        # deterministic
     ref_offs, ref_ent = cpu_index(idx_t.cpu().numpy(), hkv, B, k, kv_begin, kv_count)
+    assert np.array_equal(offs.cpu().numpy().astype(np.int64), ref_offs)
+    assert np.array_equal(ent.cpu().numpy().astype(np.int64) & 0xFFFFFFFF, ref_ent)
+
+
+def test_index_repeated_block_ids(moba):
+    """A caller-built idx that repeats a block id within a row: the repeat is listed at
+    its first slot only, so the lists never hold more than the shape's entry count."""
+    b, T, hq, hkv, B, k = 1, 4096, 8, 2, 128, 6
+    w = small_workload("dup_idx", b, hq, hkv, 64, T, B, k, "iid", seed=21)
+    inp = make_inputs(w)
+    cent = moba.pool_centroids(dev(inp["k"]), B)
+    idx = moba.gate_topk(dev(inp["q"]), cent, B, k).cpu().numpy()
+    rng = np.random.default_rng(5)
+    bad = idx.copy()
+    rows = rng.integers(0, T, 400)
+    for t, h in zip(rows, rng.integers(0, hq, 400)):
+        if t // B >= k:                        # rows with k-1 history slots filled
+            bad[0, h, t, 1:k - 1] = bad[0, h, t, 0]   # every history slot = slot 0's block
+    offs, ent = moba.build_index(dev_i32(bad), hkv, B, k, 0, hkv)
+    torch.cuda.synchronize()
+    ref_offs, ref_ent = cpu_index(bad, hkv, B, k, 0, hkv)
+    assert np.array_equal(offs.cpu().numpy().astype(np.int64), ref_offs)
+    # the entry buffer has the shape's capacity; the lists fill its first offs[-1] words
+    n = int(ref_offs[-1])
+    assert n < ent.numel() == moba.index_entries(b, T, hq, hkv, B, k, hkv)
+    assert np.array_equal(ent[:n].cpu().numpy().astype(np.int64) & 0xFFFFFFFF, ref_ent)
+
+
+def test_stages_ragged_last_block(moba):
+    """The stage entry points with T % B != 0 (a partial last block of 104 tokens):
+    centroids of every block (the last one the mean of the keys present), the gate's
+    selection of every row, and the inverted index."""
+    b, T, hq, hkv, d, B, k = 1, 1000, 4, 2, 128, 128, 4
+    w = small_workload("ragged_stages", b, hq, hkv, d, T, B, k, "offset", seed=23)
+    inp = make_inputs(w)
+    cent = moba.pool_centroids(dev(inp["k"]), B)
+    assert cent.shape == (b, hkv, 8, d)
+    K, Q = bf16_to_f64(inp["k"]), bf16_to_f64(inp["q"])
+    C = oracle.centroids(K, B)
+    np.testing.assert_allclose(cent.cpu().numpy().astype(np.float64), C, rtol=2e-6, atol=2e-6)
+    idx_t = moba.gate_topk(dev(inp["q"]), cent, B, k)
+    idx = idx_t.cpu().numpy()
+    ref = oracle.select_blocks(Q, C, B, k)
+    mism = np.argwhere((idx != ref).any(axis=-1))
+    for bi, h, t in mism:
+        s_ = oracle.gate_scores_rows(Q, C, B, [(bi, t, h)])[0]
+        ok, _, _ = check_selection_row(idx[bi, h, t], s_, t // B, k)
+        assert ok, (bi, h, t)
+    offs, ent = moba.build_index(idx_t, hkv, B, k)
+    torch.cuda.synchronize()
+    ref_offs, ref_ent = cpu_index(idx, hkv, B, k, 0, hkv)
     assert np.array_equal(offs.cpu().numpy().astype(np.int64), ref_offs)
     assert np.array_equal(ent.cpu().numpy().astype(np.int64) & 0xFFFFFFFF, ref_ent)
 
@@ -320,6 +377,20 @@ def test_forward_timed_events(moba):
         assert torch.equal(x, y)
     stages = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(moba.STAGES))]
     assert all(t >= 0.0 for t in stages) and stages[3] > 0.0   # history ran
+    assert sum(stages) <= start.elapsed_time(end) + 0.05
+    # top-1 (no history slots): the index and history stages are empty, and every
+    # event is still recorded within this call
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    start.record()
+    moba.forward(q, k, v, w.block, 1, events=evs)
+    end.record()
+    torch.cuda.synchronize()
+    assert start.elapsed_time(evs[0]) >= 0.0 and evs[-1].elapsed_time(end) >= 0.0
+    stages = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(moba.STAGES))]
+    assert all(t >= 0.0 for t in stages) and stages[4] > 0.0
+    assert stages[2] < 0.05 and stages[3] < 0.05
     assert sum(stages) <= start.elapsed_time(end) + 0.05
 
 
