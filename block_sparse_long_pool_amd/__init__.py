@@ -24,7 +24,7 @@ __all__ = [
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
     "backward", "backward_workspace_bytes", "forward_varlen", "varlen_workspace_bytes",
     "key_short_conv", "backward_varlen", "backward_varlen_workspace_bytes", "decode",
-    "decode_workspace_bytes",
+    "decode_workspace_bytes", "forward_noalloc",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -46,6 +46,8 @@ _SIGS = {
     "moba_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "moba_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
                           _vp, _sz, _vp]),
+    "moba_forward_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                  _vp, _vp]),
     "moba_forward_profile": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                   _vp, _vp, _sz, _vp, ctypes.POINTER(_f)]),
     "moba_forward_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp,
@@ -232,6 +234,42 @@ def forward(q, k, v, block: int, topk: int, scale: float | None = None, workspac
     _raise(st, "moba_forward")
     if profile:
         return out, lse, idx, dict(zip(STAGES, (float(x) for x in ms)))
+    return out, lse, idx
+
+
+def forward_noalloc(q, k, v, block: int, topk: int, scale: float | None = None, out=None,
+                    lse=None, idx=None):
+    """``forward`` through moba_forward_noalloc: the library uses its own fixed 128 MiB
+    device scratch (one per GPU) instead of a workspace, and allocates nothing.  Raises
+    MobaError when one kv-head's workspace would exceed that scratch.  Outputs are
+    allocated here with torch unless given."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    b, T, hq, d = q.shape
+    if k.shape[0] != b or k.shape[1] != T or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _raise(check_args(b, T, hq, hkv, d, block, topk, scale), "moba_forward_noalloc")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((b, hq, T), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((b, hq, T, topk), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(idx, "idx", torch.int32, 4)
+    if out.shape != q.shape or lse.shape != (b, hq, T) or idx.shape != (b, hq, T, topk):
+        raise ValueError("output shapes do not match the inputs")
+    _one_device(q, k, v, out, lse, idx)
+    with torch.cuda.device(q.device):
+        st = lib.moba_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv,
+                                      d, block, topk, float(scale), out.data_ptr(),
+                                      lse.data_ptr(), idx.data_ptr(), _stream_ptr())
+    _raise(st, "moba_forward_noalloc")
     return out, lse, idx
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moba.h"
 #include "moba_internal.h"
 
@@ -761,6 +763,64 @@ int moba_backward_varlen(const void* q, const void* k, const void* v, const void
   if (st != MOBA_OK) return st;
   return run_backward(s, q, k, v, out, lse, idx, dout, scale, dq, dk, dv, workspace,
                       workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------- no-allocation forward
+// moba_forward for callers that cannot allocate: the workspace is a fixed device array of
+// the library, one copy per GPU, which lives until the process ends.  Host code never
+// passes the array's name to a kernel or a HIP call (it stands for a host-side shadow,
+// not for device memory): the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used afterwards.
+static constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch address on the current device, looked up on the first call there
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOBA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOBA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOBA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moba_forward_noalloc(const void* q, const void* k, const void* v, int batch, int seqlen,
+                         int hq, int hkv, int head_dim, int block, int topk, float scale,
+                         void* out, float* lse, int32_t* idx, void* stream) {
+  const int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out || !lse || !idx) return MOBA_ERR_INVALID_ARG;
+  // the one-kv-head-per-pass size must fit the scratch; this is decided on the host
+  // before any device work, like every other check
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  if (!all_blocks(s)) {
+    const Layout one = make_layout(s, 1);
+    if (!layout_ok(one)) return MOBA_ERR_UNSUPPORTED;
+    if (one.total > kScratchBytes) return MOBA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const int sa = scratch_address(&ws);
+  if (sa != MOBA_OK) return sa;
+  return run_forward(s, q, k, v, scale, out, lse, idx, ws, kScratchBytes, stream, nullptr,
+                     nullptr);
 }
 
 }  // extern "C"

@@ -102,6 +102,23 @@ int moba_forward(const void* q, const void* k, const void* v, int batch, int seq
                  void* out, float* lse, int32_t* idx, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* moba_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace
+ * argument and calls no allocating routine; its workspace is a fixed 128 MiB device
+ * array inside the library, one per GPU, kept from the first call on that GPU until the
+ * process ends.  The array of the CURRENT device (hipGetDevice) is used, so `stream`
+ * must belong to that device.  Inputs, outputs, layouts and results are those of
+ * moba_forward (the same kernels; kv-heads run in groups sized to the 128 MiB).
+ * Returns MOBA_ERR_WORKSPACE, before any device work, when one kv-head's workspace
+ * (the min_bytes of moba_workspace_bytes) exceeds 128 MiB.  Every call on a GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  No word of the array needs to start
+ * at zero: every word a call reads it writes first.  This entry point, unlike the
+ * others, keeps state: the array and its per-device address. */
+int moba_forward_noalloc(const void* q, const void* k, const void* v, int batch, int seqlen,
+                         int hq, int hkv, int head_dim, int block, int topk, float scale,
+                         void* out, float* lse, int32_t* idx, void* stream);
+
 /* moba_forward, then a wait for `stream`, and the GPU time of each step measured with
  * HIP events recorded on `stream` between the steps, in milliseconds, summed over
  * kv-head groups:
