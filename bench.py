@@ -168,7 +168,7 @@ def cpu_baseline(w, inp, budget_s: float, workers: int):
         nb = w.num_blocks
         # stratified sample, dealt to the workers by head
         sample = []
-        for rep in range(64):
+        for rep in range(max(64, 65536 // nb)):   # more rows than the deadline allows
             for c in range(nb):
                 n = min(w.block, w.seqlen - c * w.block)
                 sample.append((int(c * w.block + rng.integers(n)), int(rng.integers(w.hq))))

@@ -21,8 +21,12 @@ constexpr int kChunk = 256;  // rows per chunk == threads per workgroup
 // A row's history slots are counted and listed only where the block id first appears
 // in the row.  A selection from the gate never repeats a block; a caller-built idx
 // that does still yields at most min(c, k-1) entries per row, so the lists, tiles and
-// entries stay within the sizes the host derives from the shape.
-__device__ __forceinline__ bool first_in_row(const int32_t* __restrict__ row, int s, int j) {
+// entries stay within the sizes the host derives from the shape.  `above` is the
+// largest id of slots 0 .. s-1: an id above it is new without a look back, which is
+// every slot of an ascending row (the gate's order).
+__device__ __forceinline__ bool first_in_row(const int32_t* __restrict__ row, int s, int j,
+                                             int above) {
+  if (j > above) return true;
   for (int u = 0; u < s; ++u)
     if (row[u] == j) return false;
   return true;
@@ -47,9 +51,11 @@ __global__ __launch_bounds__(kThreads) void index_count_kernel(
     const int c = t / block;
     const int h = (g0 + gi) * G + hl;
     const int32_t* row = idx + (sq.lrow(b, h, hq) + t) * topk;
+    int above = -1;
     for (int s = 0; s < topk - 1; ++s) {
       const int j = row[s];
-      if (j >= 0 && j < c && first_in_row(row, s, j)) atomicAdd(&cnt[j], 1);
+      if (j >= 0 && j < c && first_in_row(row, s, j, above)) atomicAdd(&cnt[j], 1);
+      above = max(above, j);
     }
   }
   __syncthreads();
@@ -178,9 +184,11 @@ __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
   const int32_t* row = idx + (sq.lrow(b, (g0 + gi) * G + hl, hq) + (valid ? t : 0)) * topk;
   const uint64_t below = (1ull << lane) - 1ull;
   const int sbits = entry_slot_bits(topk);
+  int above = -1;
   for (int s = 0; s < topk - 1; ++s) {
     int j = valid ? row[s] : -1;
-    const bool has = j >= j0 && j < j0 + nr && j < c && first_in_row(row, s, j);
+    const bool has = j >= j0 && j < j0 + nr && j < c && first_in_row(row, s, j, above);
+    above = max(above, j);
     j = has ? j - j0 : 0;         // the block's place in the range
     uint64_t peers = __ballot(has);
     for (int bit = 0; bit < nbits; ++bit) {
