@@ -30,6 +30,7 @@ METRIC = "MoBA prefill fwd ms + effective TFLOP/s at 128K, % bf16 MFMA peak (1 G
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_history_llama8b_128k_counters.txt")
+CURRENT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_current_llama8b_128k_counters.txt")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_long_pool_amd", "csrc", "attn.hip")
 
 
@@ -74,18 +75,21 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def read_traffic(workload: str):
-    """HBM bytes per history-attention dispatch from the committed rocprofv3 counter
-    summary, or None when there is none, it was taken on another workload, or the
-    kernel source changed since."""
-    if not os.path.exists(COUNTERS_FILE) or workload not in os.path.basename(COUNTERS_FILE):
+def read_counters(path: str, workload: str):
+    """{'traffic': HBM bytes per dispatch, 'mfma_busy': fraction of SIMD cycles} from a
+    committed rocprofv3 counter summary, or None when there is none, it was taken on
+    another workload, or the kernel source changed since."""
+    if not os.path.exists(path) or workload not in os.path.basename(path):
         return None
-    text = open(COUNTERS_FILE).read()
+    text = open(path).read()
     m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     m_t = re.search(r"traffic_bytes_per_dispatch:\s*([0-9.eE+]+)", text)
+    m_b = re.search(r"mfma_busy:\s*([0-9.eE+]+)", text)
     if not m_h or not m_t or m_h.group(1) != source_hash(ATTN_SOURCE):
         return None
-    return float(m_t.group(1))
+    return {"traffic": float(m_t.group(1)),
+            "mfma_busy": float(m_b.group(1)) if m_b else None,
+            "file": os.path.relpath(path, ROOT)}
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -446,6 +450,8 @@ def main(argv=None):
     # history attention runs once per kv-head group; one launch covers all of them when
     # the workspace holds every head (it does for this workload)
     one_launch = ws.numel() >= full_ws
+    hist_ctr = read_counters(COUNTERS_FILE, w.name) if one_launch else None
+    cur_ctr = read_counters(CURRENT_COUNTERS_FILE, w.name) if one_launch else None
     roofline = {
         "bound": "mfma",
         "kernel": "attn_history_kernel (history attention, gathered query tiles)",
@@ -453,7 +459,9 @@ def main(argv=None):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": hist_tflops / PEAK_BF16_TFLOPS if hist_tflops else None,
-        "traffic": read_traffic(w.name) if one_launch else None,
+        "traffic": hist_ctr["traffic"] if hist_ctr else None,
+        "mfma_busy": hist_ctr["mfma_busy"] if hist_ctr else None,
+        "counters": hist_ctr["file"] if hist_ctr else None,
         "algorithmic_per_launch": f"{flop_hist:.4e} FLOP = 4 * d * {heads} heads * "
                                   f"{hist} history pairs per head",
     }
@@ -486,6 +494,16 @@ def main(argv=None):
         "gate_needed_frac_of_hbm_peak": (gate_gbs_needed / PEAK_HBM_GBS
                                          if gate_gbs_needed else None),
         "roofline": roofline,
+        "current_kernel": {
+            "ms": stage["current"],
+            "tflops": flop_cur / (stage["current"] * 1e-3) / 1e12 if stage["current"] else None,
+            "frac_of_bf16_peak": (flop_cur / (stage["current"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+                                  if stage["current"] else None),
+            "traffic": cur_ctr["traffic"] if cur_ctr else None,
+            "mfma_busy": cur_ctr["mfma_busy"] if cur_ctr else None,
+            "note": "attn_current_kernel: causal current block fused with the merge of the "
+                    "history partials",
+        },
         "cpu_baseline": None,
     }
     if graph_ms is not None:
