@@ -54,6 +54,39 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_asan(out_dir: str | None = None, jobs: int | None = None) -> str:
+    """The same library with its HOST code built with AddressSanitizer (the device code
+    is unchanged): libmoba_asan.so, for the CPU tests of the argument checks and the
+    workspace arithmetic.  Load it in a process that preloads the clang ASan runtime
+    (asan_runtime())."""
+    out_dir = out_dir or os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+    def compile_one(src):
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        _run([HIPCC, *COMMON, *san, "-c", os.path.join(CSRC, src), "-o", obj], False)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    lib = os.path.join(out_dir, "libmoba_asan.so")
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+          "-fsanitize=address", "-o", lib, *objs], False)
+    return lib
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that matches hipcc's host compiler."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang ASan runtime not found")
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)

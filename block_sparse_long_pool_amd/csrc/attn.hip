@@ -666,6 +666,189 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
   }
 }
 
+// ------------------------------------------------- history, blocks of <= 128 keys (a4)
+// For small blocks (FlashMoBA story, paragraph on running many small blocks: short
+// tiles, scattered access and task granularity) the whole block, K and V, fits in LDS
+// (75.8 KB at 128 keys and d = 128, so two workgroups share a CU).  A workgroup of
+// four waves stages its block once and then streams the block's gathered query rows
+// through it: each wave takes 32-row groups in turn and, for each, computes the scores
+// of all NH*32 keys, the exact row max, the exponentials, P V and the normalised
+// partial.  After the staging there is no barrier, so the two waves of a SIMD (from
+// the two workgroups) drift out of phase and overlap one's exponentials with the
+// other's MFMAs; the next group's entries and query rows are loaded ahead.  A tile of
+// the index holds up to kResidentTileRows rows, 8x the streaming kernel's, so a block
+// is staged once per 2048 rows instead of once per 256.  Keys past the block's end (a
+// block of 16, 48, ... keys) are masked and read zero rows.
+constexpr int kResidentWaves = 4;
+constexpr int kResidentTileRows = 2048;
+
+template <int D, int NH>
+struct ResidentLds {
+  using L = Lds<D>;
+  static constexpr int KEYS = 32 * NH;
+  static constexpr int KBYTES = KEYS * L::KS;
+  static constexpr int TOTAL = KEYS * (L::KS + L::VS);
+};
+
+template <int D, int NH>
+__global__ __launch_bounds__(64 * kResidentWaves, 2) void attn_history_resident_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
+    float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, size_t ls) {
+  using L = Lds<D>;
+  using RL = ResidentLds<D, NH>;
+  constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
+  constexpr int NPK = 2 * NH;                 // 16-key k-steps of P V
+  __shared__ __attribute__((aligned(16))) char lds[RL::TOTAL];
+  char* kl = lds;
+  char* vl = lds + RL::KBYTES;
+  const int tile_id = blockIdx.x;
+  if (tile_id >= *tile_count) return;
+  const int4 tl = tiles[tile_id];
+  const int list = tl.x;
+  const int j = list % nb, gi = (list / nb) % ng, b = list / (nb * ng);
+  const int tok0 = sq.tok0(b);
+  const int G = hq / hkv, g = g0 + gi;
+  const size_t rs = (size_t)hkv * D;
+  const int key0 = j * block;
+  const int nkeys = min(block, sq.len(b) - key0);   // a history block is whole; be safe
+
+  // stage K and V of the block into padded LDS rows; rows past nkeys are zero
+  {
+    constexpr int CPR = D / 8;
+    for (int c = threadIdx.x; c < RL::KEYS * CPR; c += 64 * kResidentWaves) {
+      const int row = c / CPR, col = c % CPR;
+      u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+      if (row < nkeys) {
+        const size_t off = ((size_t)tok0 + key0 + row) * rs + (size_t)g * D + col * 8;
+        kx = *reinterpret_cast<const u32x4_t*>(k + off);
+        vx = *reinterpret_cast<const u32x4_t*>(v + off);
+      }
+      *reinterpret_cast<u32x4_t*>(kl + row * L::KS + col * 16) = kx;
+      *reinterpret_cast<u32x4_t*>(vl + row * L::VS + col * 16) = vx;
+    }
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  const int ngq = ng * G;
+  const int sb = entry_slot_bits(topk);
+  const int ngroups = (tl.z - tl.y + 31) / 32;
+  const char* kp = kl + n * L::KS + hf * 16;
+  const char* vp = vl + (4 * hf + ((lane & 15) >> 2)) * L::VS +
+                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+  // entry of this lane's row in group rg, and that row's query operands
+  auto entry_of = [&](int rg) -> uint32_t {
+    const int e = tl.y + rg * 32 + n;
+    return (rg < ngroups && e < tl.z) ? entries[e] : 0xffffffffu;
+  };
+  auto load_qops = [&](uint32_t ent, bf16x8_t (&bq)[KS]) {
+    const bool valid = ent != 0xffffffffu;
+    const int rr = valid ? (int)(ent >> sb) : 0;
+    const uint16_t* qrow = q + ((size_t)((size_t)tok0 + rr / G) * hq + g * G + rr % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (valid) x = *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks + 8 * hf);
+      bq[ks] = as_bf16x8(x);
+    }
+  };
+
+  int rg = wave;
+  uint32_t ent = entry_of(rg);
+  uint32_t ent_next = entry_of(rg + kResidentWaves);
+  bf16x8_t bq[KS];
+  load_qops(ent, bq);
+  for (; rg < ngroups; rg += kResidentWaves) {
+    // scores S^T = K Q^T over every key of the block
+    f32x16_t sc[NH];
+#pragma unroll
+    for (int kk = 0; kk < NH; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[kk][i] = 0.f;
+    {
+      // MFMA j takes k-step j / NH of key half j % NH (the NH accumulators alternate);
+      // the K operand reads run PF ahead
+      constexpr int NQ = KS * NH, PF = 4;
+      auto kread = [&](int jj) {
+        return as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + (jj % NH) * 32 * L::KS +
+                                                            (jj / NH) * 32));
+      };
+      bf16x8_t ka[NQ];
+#pragma unroll
+      for (int jj = 0; jj < PF && jj < NQ; ++jj) ka[jj] = kread(jj);
+#pragma unroll
+      for (int jj = 0; jj < NQ; ++jj) {
+        if (jj + PF < NQ) ka[jj + PF] = kread(jj + PF);
+        sc[jj % NH] = mfma32x32x16(ka[jj], bq[jj / NH], sc[jj % NH]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the next group's query rows load while this group finishes
+    const uint32_t ent_cur = ent;
+    ent = ent_next;
+    ent_next = entry_of(rg + 2 * kResidentWaves);
+    load_qops(ent, bq);
+    // keys past the block's end
+    if (nkeys < RL::KEYS) {
+#pragma unroll
+      for (int kk = 0; kk < NH; ++kk)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kk * 32 + (e >> 2) * 8 + hf * 4 + (e & 3) >= nkeys) sc[kk][e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < NH; ++kk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kk][e]);
+    const float m = pair_max(mx) * sl;
+    // exponentials 16 keys at a time, each slice packed and taken by its P V MFMAs at
+    // once (O^T = V^T P^T), so only one slice of P is ever held
+    float rsum = 0.f;
+    WaveState<D, 1> st;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[0][dt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NPK; ++ks) {
+      // the slice's V^T operands first: its exponentials cover their LDS latency
+      u32x4_t va[D / 32];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * L::VS + dt * 64);
+        const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * L::VS + dt * 64);
+        va[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int x = 8 * ks + e;
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sc[x >> 4][x & 15], sl, -m));
+        rsum += p[e];
+      }
+      const bf16x8_t pb = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        st.o[0][dt] = mfma32x32x16(as_bf16x8(va[dt]), pb, st.o[0][dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st.m[0] = m;
+    st.l[0] = rsum;
+    const bool valid = ent_cur != 0xffffffffu;
+    const int rr = valid ? (int)(ent_cur >> sb) : 0;
+    const int slot = (int)(ent_cur & ((1u << sb) - 1u));
+    const size_t row = sq.prow(b, gi * G + rr % G, ngq) + rr / G;
+    store_partial(st, 0, valid, part_o + (row * (topk - 1) + slot) * D,
+                  part_lse + (size_t)slot * ls + row);
+  }
+}
+
 // ---------------------------------------------------------------- current (a5)
 // One workgroup = a run of consecutive tokens of block c for the query heads of
 // kv-head g; all its waves share every staged K/V subtile.  With G heads per kv-head
@@ -757,6 +940,16 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_current_kern
 // ---------------------------------------------------------------- launchers
 constexpr int kQT = MOBA_ATTN_QT;
 int history_tile_rows() { return kAttnWaves * 32 * kQT; }
+// Blocks of at most 128 keys run the resident kernel.  Its tiles are as long as
+// kResidentTileRows while the launch still has >= 1024 of them (four per CU slot of
+// its two workgroups per CU), and shorter, down to 128 rows, for small problems.
+static bool history_resident(const Shape& s) { return s.block <= 128; }
+int history_tile_rows(const Shape& s, long long n_entries) {
+  if (!history_resident(s)) return history_tile_rows();
+  int tm = kResidentTileRows;
+  while (tm > 128 && n_entries / tm < 1024) tm /= 2;
+  return tm;
+}
 
 // History partials of one pass (ng kv-heads): o is [row][slot][d] and lse [slot][row],
 // rows as SeqMap::prow numbers them.  The lse of one slot are contiguous over rows, so
@@ -773,6 +966,26 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
                                float* part_lse, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const float sl = scale * 1.4426950408889634f;
+  if (history_resident(s)) {
+    const int nh = (s.block + 31) / 32;
+#define MOBA_RES(DD, NN)                                                                     \
+  hipLaunchKernelGGL((attn_history_resident_kernel<DD, NN>), dim3(max_tiles),                  \
+                     dim3(64 * kResidentWaves), 0, st, q, k, v, s.seqs(), s.hq, s.hkv, s.block, \
+                     s.topk, sl, g0, ng, s.nb(), tiles, tile_count, entries, part_o, part_lse, \
+                     part_lse_slot_stride(s, ng))
+#define MOBA_RES_D(DD)            \
+  do {                            \
+    if (nh == 1) MOBA_RES(DD, 1); \
+    else if (nh == 2) MOBA_RES(DD, 2); \
+    else if (nh == 3) MOBA_RES(DD, 3); \
+    else MOBA_RES(DD, 4);         \
+  } while (0)
+    if (s.d == 128) MOBA_RES_D(128);
+    else MOBA_RES_D(64);
+#undef MOBA_RES_D
+#undef MOBA_RES
+    return hipGetLastError();
+  }
   if (s.d == 128)
     hipLaunchKernelGGL((attn_history_kernel<128, kQT>), dim3(max_tiles), dim3(kAttnThreads), 0,
                        st, q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng,

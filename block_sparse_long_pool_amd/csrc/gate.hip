@@ -142,17 +142,22 @@ __device__ __forceinline__ GateChunk gate_chunk_make(const SeqMap& sq, int b, in
   k.T = sq.len(b);
   k.tok0 = sq.tok0(b);
   k.lrow = sq.lrow(b, h, hq);
-  k.compete = min(k.t0 + 63, k.T - 1) / block > KH;
+  k.compete = KH > 0 && min(k.t0 + 63, k.T - 1) / block > KH;
   return k;
 }
 
-// rows of a chunk whose every causal block is selected: 0..c, then -1
+// rows of a chunk that need no score: with history slots, rows whose every causal
+// block is selected (0..c, then -1); with none (topk == 1), just the current block
 __device__ __forceinline__ void gate_all_blocks(const GateChunk& k, int block, int topk,
                                                 int32_t* __restrict__ idx) {
   const int t = k.t0 + (threadIdx.x & 63);
   if (t < k.T) {
     const int c = t / block;
     int32_t* row = idx + (k.lrow + t) * topk;
+    if (topk == 1) {
+      row[0] = c;
+      return;
+    }
     for (int p = 0; p < topk; ++p) row[p] = p <= c ? p : -1;
   }
 }

@@ -90,9 +90,12 @@ struct Layout {
   size_t total;
   long long n_entries;
   long long max_tiles;
+  int tile_rows;               // rows per history-attention tile
 };
 
-Layout make_layout(const Shape& s, int ng) {
+// tile_rows 0: the history tile length for this group size; else the given one (every
+// pass of a forward uses the first group's, for which the tile buffer is sized)
+Layout make_layout(const Shape& s, int ng, int tile_rows = 0) {
   Layout L{};
   const size_t nb = s.nb();
   const size_t splits = moba::pool_splits(s);
@@ -110,7 +113,8 @@ Layout make_layout(const Shape& s, int ng) {
   const size_t nlists = (size_t)s.b * ng * nb;
   const size_t nchunks = moba::index_chunks(s);
   L.n_entries = group_entries(s, ng);
-  const int tm = moba::history_tile_rows();
+  L.tile_rows = tile_rows > 0 ? tile_rows : moba::history_tile_rows(s, L.n_entries);
+  const int tm = L.tile_rows;
   L.max_tiles = (L.n_entries + tm - 1) / tm + (long long)nlists;
   L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
   L.list_count = take(nlists * sizeof(int32_t));
@@ -314,8 +318,8 @@ int run_forward(const Shape& s, const void* q, const void* k, const void* v, flo
   StageClock clock;
   if (!clock.begin(hs, stage_ms != nullptr, stage_events)) return MOBA_ERR_HIP;
 
-  MOBA_TRY(moba::launch_pool(s, kb, reinterpret_cast<float*>(ws + L.pool_partial), cent, hs));
-  MOBA_TRY(moba::launch_centroid_split(s, cent, chi, clo, hs));
+  MOBA_TRY(moba::launch_pool(s, kb, reinterpret_cast<float*>(ws + L.pool_partial), cent, chi,
+                             clo, hs));
   MOBA_TRY(clock.mark(0));
   MOBA_TRY(moba::launch_gate(s, qb, chi, clo, idx, hs));
   MOBA_TRY(clock.mark(1));
@@ -329,13 +333,13 @@ int run_forward(const Shape& s, const void* q, const void* k, const void* v, flo
       int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
       int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
       uint32_t* entries = reinterpret_cast<uint32_t*>(ws + L.entries);
-      MOBA_TRY(moba::launch_index(s, idx, g0, ngc, moba::history_tile_rows(),
+      const Layout Lc = make_layout(s, ngc, L.tile_rows);
+      MOBA_TRY(moba::launch_index(s, idx, g0, ngc, L.tile_rows,
                                   reinterpret_cast<int32_t*>(ws + L.chunk_counts),
                                   reinterpret_cast<int32_t*>(ws + L.list_count),
                                   reinterpret_cast<int32_t*>(ws + L.list_offsets),
                                   tile_offsets, tiles, entries, L.n_entries, hs));
       MOBA_TRY(clock.mark(2));
-      const Layout Lc = make_layout(s, ngc);
       MOBA_TRY(moba::launch_attn_history(s, qb, kb, vb, scale, g0, ngc, tiles,
                                          tile_offsets + nlc, (int)Lc.max_tiles, entries,
                                          po, pl, hs));
@@ -659,8 +663,8 @@ int moba_pool_centroids(const void* k, int batch, int seqlen, int hkv, int head_
   const Layout L = make_layout(s, 1);
   if (L.cent > workspace_bytes) return MOBA_ERR_WORKSPACE;
   return hip_status(moba::launch_pool(s, static_cast<const uint16_t*>(k),
-                                      reinterpret_cast<float*>(workspace), centroids,
-                                      static_cast<hipStream_t>(stream)));
+                                      reinterpret_cast<float*>(workspace), centroids, nullptr,
+                                      nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moba_gate_topk(const void* q, const float* centroids, int batch, int seqlen, int hq,

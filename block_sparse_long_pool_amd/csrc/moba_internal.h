@@ -107,8 +107,9 @@ struct Shape {
 
 // (a1) centroid mean-pool
 int pool_splits(const Shape& s);
+// with chi/clo non-null the same pass also writes the centroids' bf16 hi + lo split
 hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float* cent,
-                       hipStream_t st);
+                       uint16_t* chi, uint16_t* clo, hipStream_t st);
 // fp32 centroids -> bf16 hi + bf16 lo (c ~= hi + lo to ~2^-17 relative)
 hipError_t launch_centroid_split(const Shape& s, const float* cent, uint16_t* chi,
                                  uint16_t* clo, hipStream_t st);
@@ -137,7 +138,9 @@ hipError_t launch_attn_current(const Shape& s, const uint16_t* q, const uint16_t
                                const uint16_t* v, float scale, int g0, int ng,
                                const uint16_t* part_o, const float* part_lse, uint16_t* out,
                                float* lse, hipStream_t st);
-int history_tile_rows();
+int history_tile_rows();                    // rows per tile of the streaming kernel
+// rows per tile of the kernel s runs on, for a pass of n_entries index entries
+int history_tile_rows(const Shape& s, long long n_entries);
 
 // full-attention decode: n new queries at the last n positions of a Tk-key cache, the
 // keys split over many wavefronts (fp32 (o, lse) partials per split), then a merge

@@ -12,6 +12,13 @@
 
 namespace moba {
 
+// c -> bf16 hi + bf16 lo, c ~= hi + lo to ~2^-17 relative (c - hi is exact in fp32)
+__device__ __forceinline__ void split_hi_lo(float c, uint16_t* hi_out, uint16_t* lo_out) {
+  const uint32_t hi = f32_to_bf16_rne(c);
+  *hi_out = (uint16_t)hi;
+  *lo_out = (uint16_t)f32_to_bf16_rne(c - __uint_as_float(hi << 16));
+}
+
 __global__ __launch_bounds__(kThreads) void pool_partial_kernel(
     const uint16_t* __restrict__ k, SeqMap sq, int cols, int block, int rows_per_split,
     float* __restrict__ partial) {
@@ -64,10 +71,12 @@ __global__ __launch_bounds__(kThreads) void pool_partial_kernel(
 }
 
 // sum the split partials in order, divide by the block's token count (a block past
-// the end of a shorter packed sequence gets 0; no query ever scores it)
+// the end of a shorter packed sequence gets 0; no query ever scores it); with chi/clo,
+// also the bf16 hi + lo split the gate reads (c ~= hi + lo to ~2^-17 relative)
 __global__ __launch_bounds__(kThreads) void pool_finalize_kernel(
     const float* __restrict__ partial, int b_, SeqMap sq, int hkv, int d, int block, int nb,
-    int splits, float* __restrict__ cent) {
+    int splits, float* __restrict__ cent, uint16_t* __restrict__ chi,
+    uint16_t* __restrict__ clo) {
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const size_t total = (size_t)b_ * hkv * nb * d;
   if (i >= total) return;
@@ -80,7 +89,9 @@ __global__ __launch_bounds__(kThreads) void pool_finalize_kernel(
   float sum = 0.f;
   for (int s = 0; s < splits; ++s) sum += p[(size_t)s * cols];
   const int n = min(block, sq.len(b) - j * block);
-  cent[i] = n > 0 ? sum / (float)n : 0.f;  // layout [b][hkv][nb][d] == i
+  const float c = n > 0 ? sum / (float)n : 0.f;
+  cent[i] = c;  // layout [b][hkv][nb][d] == i
+  if (chi != nullptr) split_hi_lo(c, chi + i, clo + i);
 }
 
 __global__ __launch_bounds__(kThreads) void centroid_split_kernel(
@@ -88,11 +99,7 @@ __global__ __launch_bounds__(kThreads) void centroid_split_kernel(
     uint16_t* __restrict__ clo) {
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= total) return;
-  const float c = cent[i];
-  const uint32_t hi = f32_to_bf16_rne(c);
-  const float rest = c - __uint_as_float(hi << 16);  // exact in float32
-  chi[i] = (uint16_t)hi;
-  clo[i] = (uint16_t)f32_to_bf16_rne(rest);
+  split_hi_lo(cent[i], chi + i, clo + i);
 }
 
 int pool_splits(const Shape& s) {
@@ -103,7 +110,7 @@ int pool_splits(const Shape& s) {
 }
 
 hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float* cent,
-                       hipStream_t st) {
+                       uint16_t* chi, uint16_t* clo, hipStream_t st) {
   const int nb = s.nb();
   const int splits = pool_splits(s);
   const int rows_per_split = (s.block + splits - 1) / splits;
@@ -116,7 +123,7 @@ hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float*
   const size_t total = (size_t)s.b * s.hkv * nb * s.d;
   hipLaunchKernelGGL(pool_finalize_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, st, partial, s.b, s.seqs(), s.hkv, s.d, s.block, nb,
-                     splits, cent);
+                     splits, cent, chi, clo);
   return hipGetLastError();
 }
 

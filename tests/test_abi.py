@@ -155,3 +155,80 @@ def test_decode_args_and_workspace(moba):
                            0, None) == -1
     assert lib.moba_decode(None, None, None, 1, 2, 1, 4, 1, 64, 0.125, None, None, None,
                            0, None) == -1
+
+
+_ASAN_DRIVER = r"""
+import ctypes, sys
+lib = ctypes.CDLL(sys.argv[1])
+i, f, vp, sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+lib.moba_check_args.argtypes = [i] * 7 + [f]
+lib.moba_workspace_bytes.restype = sz
+lib.moba_workspace_bytes.argtypes = [i] * 7 + [ctypes.POINTER(sz)]
+lib.moba_backward_workspace_bytes.restype = sz
+lib.moba_backward_workspace_bytes.argtypes = [i] * 7 + [ctypes.POINTER(sz)]
+lib.moba_varlen_workspace_bytes.restype = sz
+lib.moba_varlen_workspace_bytes.argtypes = [i] * 8 + [ctypes.POINTER(sz)]
+lib.moba_backward_varlen_workspace_bytes.restype = sz
+lib.moba_backward_varlen_workspace_bytes.argtypes = [i] * 8 + [ctypes.POINTER(sz)]
+lib.moba_decode_workspace_bytes.restype = sz
+lib.moba_decode_workspace_bytes.argtypes = [i] * 6
+lib.moba_stage_workspace_bytes.restype = sz
+lib.moba_stage_workspace_bytes.argtypes = [i] * 7
+lib.moba_index_entries.restype = ctypes.c_int64
+lib.moba_index_entries.argtypes = [i] * 7
+lib.moba_strerror.restype = ctypes.c_char_p
+lib.moba_forward.argtypes = [vp] * 3 + [i] * 7 + [f] + [vp] * 4 + [sz, vp]
+lib.moba_forward_noalloc.argtypes = [vp] * 3 + [i] * 7 + [f] + [vp] * 4
+lib.moba_dense_forward.argtypes = [vp] * 3 + [i] * 5 + [f] + [vp] * 3
+mn = sz(0)
+shapes = [(1, 131072, 32, 8, 128, 4096, 12), (2, 1000, 4, 2, 64, 128, 4), (1, 48005, 2, 1, 64, 16, 8),
+          (1, 4096, 4, 2, 128, 128, 40), (1, 777, 8, 2, 128, 16, 200), (3, 1, 4, 2, 128, 16, 3),
+          (1, 65536, 32, 8, 128, 128, 16), (1, 16 * 8193, 1, 1, 64, 16, 2), (1, 128, 3, 2, 64, 16, 1),
+          (0, 128, 1, 1, 64, 16, 1), (1, 1 << 27, 1, 1, 64, 1 << 20, 2), (1, 4480, 2, 1, 64, 64, 65)]
+n = 0
+for s in shapes:
+    lib.moba_check_args(*s, 0.125)
+    lib.moba_workspace_bytes(*s, ctypes.byref(mn))
+    lib.moba_backward_workspace_bytes(*s, ctypes.byref(mn))
+    lib.moba_stage_workspace_bytes(*s)
+    b, T, hq, hkv, d, B, k = s
+    lib.moba_varlen_workspace_bytes(max(b, 1), max(b, 1) * T, T, hq, hkv, d, B, k, ctypes.byref(mn))
+    lib.moba_backward_varlen_workspace_bytes(max(b, 1), max(b, 1) * T, T, hq, hkv, d, B, k,
+                                             ctypes.byref(mn))
+    lib.moba_index_entries(b, T, hq, hkv, B, k, hkv)
+    lib.moba_decode_workspace_bytes(b, 1, T, hq, hkv, d)
+    # every pointer NULL: rejected on the host before any device work
+    assert lib.moba_forward(None, None, None, *s, 0.125, None, None, None, None, 0, None) < 0
+    assert lib.moba_forward_noalloc(None, None, None, *s, 0.125, None, None, None, None) < 0
+    assert lib.moba_dense_forward(None, None, None, b, T, hq, hkv, d, 0.125, None, None, None) < 0
+    n += 1
+for st in range(-6, 2):
+    assert lib.moba_strerror(st)
+print("asan driver ok", n)
+"""
+
+
+def test_host_code_under_address_sanitizer(tmp_path):
+    """The host code (argument checks, workspace layouts, the entry points' early
+    rejections) built with AddressSanitizer and driven over edge shapes in a process
+    that preloads the ASan runtime: any out-of-bounds access or use after free on the
+    host aborts it."""
+    import importlib.util
+    import subprocess
+    import sys
+    spec = importlib.util.spec_from_file_location(
+        "_moba_build", os.path.join(ROOT, "block_sparse_long_pool_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    try:
+        rt = b.asan_runtime()
+    except RuntimeError:
+        pytest.skip("no clang ASan runtime in this image")
+    lib = b.build_host_asan(str(tmp_path / "asan"))
+    drv = tmp_path / "drive.py"
+    drv.write_text(_ASAN_DRIVER)
+    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    r = subprocess.run([sys.executable, str(drv), lib], capture_output=True, text=True,
+                       env=env, timeout=300)
+    assert r.returncode == 0 and "asan driver ok" in r.stdout, r.stderr[-3000:]
+    assert "AddressSanitizer" not in r.stderr
