@@ -757,12 +757,10 @@ __global__ __launch_bounds__(64 * kResidentWaves, 2) void attn_history_resident_
     }
   };
 
-  int rg = wave;
-  uint32_t ent = entry_of(rg);
-  uint32_t ent_next = entry_of(rg + kResidentWaves);
-  bf16x8_t bq[KS];
-  load_qops(ent, bq);
-  for (; rg < ngroups; rg += kResidentWaves) {
+  // One 32-row group with query operands bq: scores, softmax, P V, partial store.
+  // `refill` runs right after the QK MFMAs, when bq is free: it loads a later group's
+  // query rows into bq.
+  auto group = [&](int rg, uint32_t ent_cur, bf16x8_t (&bq)[KS], auto&& refill) {
     // scores S^T = K Q^T over every key of the block
     f32x16_t sc[NH];
 #pragma unroll
@@ -787,11 +785,7 @@ __global__ __launch_bounds__(64 * kResidentWaves, 2) void attn_history_resident_
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the next group's query rows load while this group finishes
-    const uint32_t ent_cur = ent;
-    ent = ent_next;
-    ent_next = entry_of(rg + 2 * kResidentWaves);
-    load_qops(ent, bq);
+    refill();
     // keys past the block's end
     if (nkeys < RL::KEYS) {
 #pragma unroll
@@ -846,6 +840,27 @@ __global__ __launch_bounds__(64 * kResidentWaves, 2) void attn_history_resident_
     const size_t row = sq.prow(b, gi * G + rr % G, ngq) + rr / G;
     store_partial(st, 0, valid, part_o + (row * (topk - 1) + slot) * D,
                   part_lse + (size_t)slot * ls + row);
+  };
+
+  constexpr int W = kResidentWaves;
+  // Groups in pairs, two buffers of query operands: group rg computes on qa while qb
+  // holds group rg + W; after rg's QK, qa takes group rg + 2W.  Entries run four
+  // groups ahead, so neither the entry nor the query rows it names is waited for in
+  // the group that needs them.
+  uint32_t e0 = entry_of(wave), e1 = entry_of(wave + W);
+  uint32_t e2 = entry_of(wave + 2 * W), e3 = entry_of(wave + 3 * W);
+  bf16x8_t qa[KS], qb[KS];
+  load_qops(e0, qa);
+  load_qops(e1, qb);
+  for (int rg = wave; rg < ngroups; rg += 2 * W) {
+    const uint32_t c0 = e0, c1 = e1;
+    e0 = e2;
+    e1 = e3;
+    e2 = entry_of(rg + 4 * W);
+    e3 = entry_of(rg + 5 * W);
+    group(rg, c0, qa, [&] { load_qops(e0, qa); });
+    if (rg + W >= ngroups) break;
+    group(rg + W, c1, qb, [&] { load_qops(e1, qb); });
   }
 }
 
