@@ -59,7 +59,8 @@ struct Lds {
   static constexpr int VS = D * 2 + 64;          // V row stride (bytes)
   static constexpr int KBYTES = KN * KS;
   static constexpr int VBYTES = KN * VS;
-  static constexpr int TOTAL = 2 * (KBYTES + VBYTES);  // two K and two V buffers
+  static constexpr int NBUF = 3;                 // K and V subtile buffers each
+  static constexpr int TOTAL = NBUF * (KBYTES + VBYTES);
 };
 
 template <int D, int QT>
@@ -110,25 +111,17 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& r, const TileOffsets<D>& 
   }
 }
 
-// rows as they are, into padded LDS rows of STRIDE bytes
-template <int D, int STRIDE>
-__device__ __forceinline__ void tile_store(const TileRegs<D>& r, char* dst) {
-  using R = TileRegs<D>;
-  constexpr bool kAllThreads = (KN * R::CPR) % kAttnThreads == 0;
-#pragma unroll
-  for (int i = 0; i < R::NC; ++i) {
-    const int ci = threadIdx.x + i * kAttnThreads;
-    if (kAllThreads || ci < KN * R::CPR)
-      *reinterpret_cast<u32x4_t*>(dst + (ci / R::CPR) * STRIDE + (ci % R::CPR) * 16) = r.c[i];
-  }
-}
-
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) char lds_char;   // a byte of LDS
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i%4 of
 // the 8 bytes addressed by lanes 4j + i/4, j = 0..3.
 __device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+__device__ __forceinline__ u32x2_t lds_read_tr16(const lds_char* p) {
   const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
   return __builtin_bit_cast(u32x2_t, r);
 }
@@ -157,84 +150,121 @@ __device__ __forceinline__ void state_init(WaveState<D, QT>& st) {
   }
 }
 
-// Key-range walker, two wave groups in ping-pong.  The workgroup's waves form two
-// groups (the two waves that share a SIMD are in different groups).  Every wave runs
-// the same sequence of phases, separated by barriers:
-//   P      QK^T of subtile 0, its mask and row max;
-//   A(i)   the MFMAs of QK^T for subtile i+1 next to the exp/sum/pack of subtile i;
-//   B(i)   the PV MFMAs of subtile i next to the mask and row max of subtile i+1,
-//          then the lazy-rescale decision for subtile i+1;
-// but group 1 starts one barrier later, so at every half-step h one wave of a SIMD is
-// in an exp-heavy A phase while the other is in an MFMA/LDS-heavy phase.  Phase
-// number f = 0 (P), 2i+1 (A(i)), 2i+2 (B(i)) runs at half-step h = f + group.
-// LDS holds two K and two V buffers.  At half-step h all threads stage one slice
-// each of one subtile, K(h/2 + 1) for even h and V(h/2) for odd h, from registers
-// loaded two half-steps before.  K(j) is read at half-steps 2j-1 and 2j (K(0) at 0
-// and 1) and V(i) at 2i+2 and 2i+3, so every buffer is rewritten only after both
-// groups are done with its previous subtile.  Staging past the last subtile
-// re-stages the last subtile into a buffer nobody reads again.
+// Key-range walker.  Per KN-key subtile i a wavefront runs two phases:
+//   A(i)   the QK^T MFMAs of subtile i+1 next to the exp/sum/pack of subtile i;
+//   B(i)   the PV MFMAs of subtile i next to the mask and row max of subtile i+1, then
+//          the lazy-rescale decision;
+// after a phase P (QK^T of subtile 0, its mask and row max).  The workgroup's waves form
+// two groups (the two waves that share a SIMD are in different groups), and one
+// barrier per subtile ends an interval:
+//   group 0:  P | A(0) B(0) | A(1) B(1) | ... | A(n-1) B(n-1)
+//   group 1:  P A(0) | B(0) A(1) | B(1) A(2) | ... | B(n-1)
+// so in every interval one wave of a SIMD starts in an exp-heavy phase while the other
+// starts in an MFMA/LDS-heavy one, and the two swap half-way without a barrier.
+// LDS holds three K and three V subtile buffers (subtile i in buffer i % 3).  Interval
+// n reads K(n), K(n+1), V(n-1) and V(n); it stages K(n+2) and V(n+1) from registers
+// loaded in interval n-1, so a subtile is visible an interval before it is first read,
+// and a buffer is rewritten only after the interval that read its previous subtile.
+// The operand reads run PF MFMAs ahead as one stream over a wave's phases: the last
+// slots of a phase read the first operands of the next one, across the barrier too,
+// so no phase starts by waiting on the LDS.  Staging past the last subtile re-stages
+// the last subtile into buffers nobody reads again.
 template <int D, int QT>
 struct Walker {
   using L = Lds<D>;
   static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int NQK = NH * KSTEPS;          // QK^T MFMAs per query tile
   static constexpr int NPV = (KN / 16) * (D / 32); // PV MFMAs per query tile
-#ifndef MOBA_ATTN_PFK
-#define MOBA_ATTN_PFK 3
+#ifndef MOBA_ATTN_PF
+#define MOBA_ATTN_PF 4
 #endif
-#ifndef MOBA_ATTN_PFV
-#define MOBA_ATTN_PFV 4
-#endif
-  static constexpr int PFK = MOBA_ATTN_PFK, PFV = MOBA_ATTN_PFV;  // operand reads in flight
+  static constexpr int PF = MOBA_ATTN_PF;          // operand reads in flight
+  static_assert(NQK % PF == 0 && NPV % PF == 0, "every phase starts at the ring's head");
   static constexpr int NC = TileRegs<D>::NC;
+#ifndef MOBA_ATTN_SS
+#define MOBA_ATTN_SS 2
+#endif
+  static constexpr int SS = MOBA_ATTN_SS;          // first staging slot of an interval
+  static_assert(SS + 2 * NC < NQK && SS + 2 * NC < NPV, "staging fits in one phase");
   using Scores = f32x16_t[NH][QT];
   using POps = bf16x8_t[QT][KN / 16];
-  char* lds;
+  using Ops = u32x4_t[PF];
+  lds_char* lds;
   const uint16_t* kbase;
   const uint16_t* vbase;
   size_t rs;
   int key_begin, key_end, nsub, diag_from;
   float sl;
-  int grp;                     // 0 leads, 1 trails by one half-step
+  int grp;                     // 0: A before B in an interval, 1: B before A
+  uint32_t kl, vl;             // the lane's byte offsets of its K and V operand reads
   TileOffsets<D> to;
-  TileRegs<D> bank[2];         // staging registers of even / odd phases
+  TileRegs<D> kst, vst, pre;   // staging registers (pre: K(1) in the prologue only)
 
-  __device__ __forceinline__ char* kbuf(int i) const { return lds + (i & 1) * L::KBYTES; }
-  __device__ __forceinline__ char* vbuf(int i) const {
-    return lds + 2 * L::KBYTES + (i & 1) * L::VBYTES;
+  // The buffer offsets pass through an empty asm so that the compiler adds them to the
+  // lane's base address at run time: folded into the reads' 16-bit immediate offsets,
+  // the upper buffers' constants overflow it, and the compiler then keeps one address
+  // register per (buffer, read) live across the whole walk.
+  __device__ __forceinline__ lds_char* kbuf(int i) const {
+    int off = (i % L::NBUF) * L::KBYTES;
+    asm("" : "+s"(off));
+    return lds + off;
+  }
+  __device__ __forceinline__ lds_char* vbuf(int i) const {
+    int off = L::NBUF * L::KBYTES + (i % L::NBUF) * L::VBYTES;
+    asm("" : "+s"(off));
+    return lds + off;
   }
   __device__ __forceinline__ int kb(int i) const { return key_begin + i * KN; }
   __device__ __forceinline__ int nvalid(int i) const { return min(KN, key_end - kb(i)); }
   __device__ __forceinline__ bool masked(int i) const {
     return kb(i) + KN > key_end || kb(i) + KN - 1 > diag_from;
   }
-  // global -> registers: the subtile staged at half-step h
-  __device__ __forceinline__ void stage_load(TileRegs<D>& r, int h) {
-    const bool isv = h & 1;
-    const int t = min(isv ? h / 2 : h / 2 + 1, nsub - 1);
-    tile_load<D>(r, to, (isv ? vbase : kbase) + (size_t)kb(t) * rs, rs, nvalid(t));
+  // global -> registers: subtile i (the last one past the end) of K or V
+  __device__ __forceinline__ void load_sub(TileRegs<D>& r, const uint16_t* base, int i) {
+    const int t = min(i, nsub - 1);
+    tile_load<D>(r, to, base + (size_t)kb(t) * rs, rs, nvalid(t));
   }
-  // registers -> LDS: chunk c of the subtile staged at half-step h
-  __device__ __forceinline__ void stage_store(const TileRegs<D>& r, int c, int h) {
+  // registers -> LDS: chunk c of a subtile into a buffer of row stride STRIDE
+  template <int STRIDE>
+  __device__ __forceinline__ static void store_chunk(const TileRegs<D>& r, int c, lds_char* buf) {
     constexpr bool kAllThreads = (KN * TileRegs<D>::CPR) % kAttnThreads == 0;
     const int ci = threadIdx.x + c * kAttnThreads;
-    if (kAllThreads || ci < KN * TileRegs<D>::CPR) {
-      const int row = ci / TileRegs<D>::CPR, col = (ci % TileRegs<D>::CPR) * 16;
-      const bool isv = h & 1;
-      char* dst = isv ? vbuf(h / 2) + row * L::VS : kbuf(h / 2 + 1) + row * L::KS;
-      *reinterpret_cast<u32x4_t*>(dst + col) = r.c[c];
-    }
+    if (kAllThreads || ci < KN * TileRegs<D>::CPR)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(buf + (ci / TileRegs<D>::CPR) * STRIDE +
+                                  (ci % TileRegs<D>::CPR) * 16) = r.c[c];
   }
-  // the staging work of a phase, spread over its MFMA slots: the stores of the
-  // subtile for half-step h, then the loads for half-step h + 2 into the same registers
-  template <int BANK>
-  __device__ __forceinline__ void stage_slot(int j, int h) {
-    if (j < NC) stage_store(bank[BANK], j, h);
-    else if (j == NC) stage_load(bank[BANK], h + 2);
+  // slot j of interval n's first phase: K(n+2) and V(n+1) go from the registers into
+  // LDS chunk by chunk, then K(n+3) and V(n+2) are loaded into the same registers
+  __device__ __forceinline__ void stage_slot(int j, int n) {
+    const int s = j - SS;
+    if (s >= 0 && s < 2 * NC) {
+      if (s & 1) store_chunk<L::VS>(vst, s >> 1, vbuf(n + 1));
+      else store_chunk<L::KS>(kst, s >> 1, kbuf(n + 2));
+    } else if (s == 2 * NC) {
+      load_sub(kst, kbase, n + 3);
+      load_sub(vst, vbase, n + 2);
+    }
   }
 
   __device__ __forceinline__ static int k_off(int j) {
     return (j / KSTEPS) * 32 * L::KS + (j % KSTEPS) * 32;
+  }
+  // K operand of QK^T MFMA j of a subtile in buffer kbufp
+  __device__ __forceinline__ u32x4_t kread(const lds_char* kbufp, int j) const {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(kbufp + kl + k_off(j));
+  }
+  // V^T operand of PV MFMA j of a subtile in buffer vbufp
+  __device__ __forceinline__ u32x4_t vread(const lds_char* vbufp, int j) const {
+    const int ks = j / (D / 32), dt = j % (D / 32);
+    const lds_char* p = vbufp + vl + (16 * ks) * L::VS + dt * 64;
+    const u32x2_t lo = lds_read_tr16(p);
+    const u32x2_t hi = lds_read_tr16(p + 8 * L::VS);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
+  // operand j of the next phase: NX = 1 its K, 2 its V
+  template <int NX>
+  __device__ __forceinline__ u32x4_t nread(const lds_char* bufp, int j) const {
+    return NX == 1 ? kread(bufp, j) : vread(bufp, j);
   }
 
   __device__ __forceinline__ void mask_scores(Scores& s, int i, const int (&tpos)[QT]) const {
@@ -287,21 +317,17 @@ struct Walker {
     rescale(st, mxs);
   }
 
-  // Phase A(i) (EXP) or P (!EXP, i = -1): QK^T of subtile i+1 into nxt (when NEXT) and
-  // exp/sum/pack of cur into pb, next to the staging of half-step h.
-  template <bool NEXT, bool EXP, int BANK>
+  // Phase A(i) (EXP) or P (!EXP): QK^T of the subtile in buffer kq into nxt (when NEXT)
+  // next to the exp/sum/pack of cur into pb.  ops holds the first PF K operands; the
+  // last PF slots read the next phase's first operands from buffer nb (NX = 1: K,
+  // 2: V; 0: ops is left as it is).  With STAGE the phase carries interval n's staging.
+  template <bool NEXT, bool EXP, int NX, bool STAGE>
   __device__ __forceinline__ void phase_a(WaveState<D, QT>& st, const Scores& cur,
-                                          Scores& nxt, POps& pb, int i, int h) {
-    const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+                                          Scores& nxt, POps& pb, Ops& ops, const lds_char* kq,
+                                          const lds_char* nb, int n) {
     constexpr int EPS = 16 * NH / NQK;  // exp elements per slot and query tile
     static_assert(EPS * NQK == 16 * NH && 8 % EPS == 0, "the exps split evenly over slots");
-    const char* kp = kbuf(i + 1) + n * L::KS + hf * 16;
-    bf16x8_t ka[NQK];
-    if (NEXT) {
-#pragma unroll
-      for (int j = 0; j < PFK; ++j)
-        ka[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j)));
-    }
+    static_assert(NEXT || NX == 0, "a phase without MFMAs reads no operands");
     float mref[QT], rsum[QT], p[QT][16 * NH];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -312,12 +338,13 @@ struct Walker {
 #pragma unroll
     for (int j = 0; j < NQK; ++j) {
       if (NEXT) {
-        if (j + PFK < NQK)
-          ka[j + PFK] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + k_off(j + PFK)));
         const int kk = j / KSTEPS, ks = j % KSTEPS;
+        const bf16x8_t a = as_bf16x8(ops[j % PF]);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          nxt[kk][qt] = mfma32x32x16(ka[j], st.q[qt][ks], ks == 0 ? zero : nxt[kk][qt]);
+          nxt[kk][qt] = mfma32x32x16(a, st.q[qt][ks], ks == 0 ? zero : nxt[kk][qt]);
+        if (j + PF < NQK) ops[j % PF] = kread(kq, j + PF);
+        else if (NX != 0) ops[j % PF] = nread<NX>(nb, j + PF - NQK);
       }
       if (EXP) {
 #pragma unroll
@@ -343,7 +370,7 @@ struct Walker {
           }
         }
       }
-      stage_slot<BANK>(j, h);
+      if (STAGE) stage_slot(j, n);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (EXP) {
@@ -355,24 +382,14 @@ struct Walker {
     }
   }
 
-  // Phase B(i): O^T += V^T P^T for subtile i next to the mask and row max of nxt
-  // (subtile i+1, when NEXT), then the rescale decision; staging of half-step h.
-  template <bool NEXT, int BANK>
+  // Phase B(i): O^T += V^T P^T for the subtile in buffer vq next to the mask and row max
+  // of nxt (subtile i+1, when NEXT), then the rescale decision.  Operand stream and
+  // staging as in phase_a.
+  template <bool NEXT, int NX, bool STAGE>
   __device__ __forceinline__ void phase_b(WaveState<D, QT>& st, Scores& nxt, const POps& pb,
-                                          int i, int h, const int (&tpos)[QT]) {
-    const int lane = threadIdx.x & 63, hf = lane >> 5;
+                                          Ops& ops, const lds_char* vq, const lds_char* nb, int i,
+                                          int n, const int (&tpos)[QT]) {
     if (NEXT && masked(i + 1)) mask_scores(nxt, i + 1, tpos);
-    const char* vp = vbuf(i) + (4 * hf + ((lane & 15) >> 2)) * L::VS +
-                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-    u32x4_t va[NPV];
-    auto vread = [&](int j) {
-      const int ks = j / (D / 32), dt = j % (D / 32);
-      const u32x2_t lo = lds_read_tr16(vp + (16 * ks) * L::VS + dt * 64);
-      const u32x2_t hi = lds_read_tr16(vp + (16 * ks + 8) * L::VS + dt * 64);
-      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-    };
-#pragma unroll
-    for (int j = 0; j < PFV; ++j) va[j] = vread(j);
     constexpr int MPS = 16 * NH / NPV;  // max elements per slot and query tile
     static_assert(MPS * NPV == 16 * NH, "the row max splits evenly over the PV slots");
     float mx[QT];
@@ -380,11 +397,12 @@ struct Walker {
     for (int qt = 0; qt < QT; ++qt) mx[qt] = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPV; ++j) {
-      if (j + PFV < NPV) va[j + PFV] = vread(j + PFV);
       const int ks = j / (D / 32), dt = j % (D / 32);
+      const bf16x8_t a = as_bf16x8(ops[j % PF]);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        st.o[qt][dt] = mfma32x32x16(as_bf16x8(va[j]), pb[qt][ks], st.o[qt][dt]);
+      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32x32x16(a, pb[qt][ks], st.o[qt][dt]);
+      if (j + PF < NPV) ops[j % PF] = vread(vq, j + PF);
+      else if (NX != 0) ops[j % PF] = nread<NX>(nb, j + PF - NPV);
       if (NEXT) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
@@ -394,7 +412,7 @@ struct Walker {
             mx[qt] = fmaxf(mx[qt], nxt[x >> 4][qt][x & 15]);
           }
       }
-      stage_slot<BANK>(j, h);
+      if (STAGE) stage_slot(j, n);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (NEXT) {
@@ -405,57 +423,92 @@ struct Walker {
     }
   }
 
-  // A(i) then B(i), cur = S(i), nxt = S(i+1); phases 2i+1 and 2i+2
-  template <bool NEXT>
-  __device__ __forceinline__ void step(WaveState<D, QT>& st, const Scores& cur, Scores& nxt,
-                                       POps& pb, int i, const int (&tpos)[QT]) {
-    phase_a<NEXT, true, 1>(st, cur, nxt, pb, i, 2 * i + 1 + grp);
-    __syncthreads();
-    phase_b<NEXT, 0>(st, nxt, pb, i, 2 * i + 2 + grp, tpos);
-    __syncthreads();
+  // Subtile i: A(i), then B(i).  Both groups run this same code; group 1's barrier
+  // falls between the two phases, group 0's after B.  A(i) carries the staging of
+  // interval i + 1 - grp.  KIND 0: i + 2 < nsub, 1: i = nsub - 2, 2: i = nsub - 1.
+  template <int KIND>
+  __device__ __forceinline__ void iter(WaveState<D, QT>& st, Scores& cur, Scores& nxt,
+                                       POps& pb, Ops& ops, int i, const int (&tpos)[QT]) {
+    const int n = i + 1 - grp;
+    if (KIND < 2) phase_a<true, true, 2, true>(st, cur, nxt, pb, ops, kbuf(i + 1), vbuf(i), n);
+    else phase_a<false, true, 0, true>(st, cur, nxt, pb, ops, nullptr, nullptr, n);
+    if (grp) __syncthreads();
+    if (KIND == 0)
+      phase_b<true, 1, false>(st, nxt, pb, ops, vbuf(i), kbuf(i + 2), i, n, tpos);
+    else if (KIND == 1)
+      phase_b<true, 2, false>(st, nxt, pb, ops, vbuf(i), vbuf(i + 1), i, n, tpos);
+    else
+      phase_b<false, 0, false>(st, nxt, pb, ops, vbuf(i), nullptr, i, n, tpos);
+    if (!grp) __syncthreads();
+  }
+
+  __device__ __forceinline__ static void copy_scores(Scores& dst, const Scores& src) {
+#pragma unroll
+    for (int kk = 0; kk < NH; ++kk)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) dst[kk][qt] = src[kk][qt];
   }
 
   // The first loads, which depend on nothing the caller computes, issued before the
-  // caller's query loads so that their latencies overlap: K(0), and for group 0 the
-  // subtile of its half-step 1 (V(0)), for group 1 that of half-step 0 (K(1)), which
-  // it stages in the prologue because it waits that half-step out.
+  // caller's query loads so that their latencies overlap: K(0), K(1) and V(0).
   __device__ __forceinline__ void begin() {
     to.init(rs);
     nsub = (key_end - key_begin + KN - 1) / KN;
-    tile_load<D>(bank[0], to, kbase + (size_t)kb(0) * rs, rs, nvalid(0));
-    stage_load(bank[1], grp ? 0 : 1);
+    const int lane = threadIdx.x & 63, hf = lane >> 5;
+    kl = (uint32_t)((lane & 31) * L::KS + hf * 16);
+    vl = (uint32_t)((4 * hf + ((lane & 15) >> 2)) * L::VS +
+                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+    load_sub(kst, kbase, 0);
+    load_sub(pre, kbase, 1);
+    load_sub(vst, vbase, 0);
   }
 
   __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT]) {
-    // prologue: K(0) into LDS (and K(1) for group 1), then the registers of the first
-    // two phases: the subtiles of half-steps grp and grp + 1
-    tile_store<D, L::KS>(bank[0], kbuf(0));
-    if (grp) {
-      for (int c = 0; c < NC; ++c) stage_store(bank[1], c, 0);
-      stage_load(bank[0], 1);
-      stage_load(bank[1], 2);
-    } else {
-      stage_load(bank[0], 0);
+    // prologue: K(0), K(1) and V(0) into LDS, then the registers that interval 0
+    // stages (K(2), V(1))
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      store_chunk<L::KS>(kst, c, kbuf(0));
+      store_chunk<L::KS>(pre, c, kbuf(1));
+      store_chunk<L::VS>(vst, c, vbuf(0));
     }
+    load_sub(kst, kbase, 2);
+    load_sub(vst, vbase, 1);
     __syncthreads();
-    if (grp) __syncthreads();            // group 1 trails by one half-step
     Scores sa, sb;
     POps pb;
-    phase_a<true, false, 0>(st, sa, sa, pb, -1, grp);   // P
-    max_all(st, sa, 0, tpos);
-    __syncthreads();
-    int i = 0;
-    for (; i + 2 < nsub; i += 2) {
-      step<true>(st, sa, sb, pb, i, tpos);
-      step<true>(st, sb, sa, pb, i + 1, tpos);
-    }
-    if (i + 1 < nsub) {
-      step<true>(st, sa, sb, pb, i, tpos);
-      step<false>(st, sb, sa, pb, i + 1, tpos);
+    Ops ops;
+#pragma unroll
+    for (int j = 0; j < PF; ++j) ops[j] = kread(kbuf(0), j);
+    // P carries group 0's staging of interval 0 (group 1's is in its A(0))
+    if (grp == 0) {
+      if (nsub > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
+      else phase_a<true, false, 2, true>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
     } else {
-      step<false>(st, sa, sb, pb, i, tpos);
+      if (nsub > 1) phase_a<true, false, 1, false>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
+      else phase_a<true, false, 2, false>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
     }
-    if (!grp) __syncthreads();           // group 0's share of the last half-step
+    max_all(st, sa, 0, tpos);
+    if (!grp) __syncthreads();
+    // two subtiles per iteration so that the score buffers keep their roles (S(i) in sa
+    // for even i); the last ones move S(i+1) into sa instead
+    int i = 0;
+    for (; i + 3 < nsub; i += 2) {
+      iter<0>(st, sa, sb, pb, ops, i, tpos);
+      iter<0>(st, sb, sa, pb, ops, i + 1, tpos);
+    }
+    if (i + 3 == nsub) {
+      iter<0>(st, sa, sb, pb, ops, i, tpos);
+      copy_scores(sa, sb);
+      ++i;
+    }
+    if (i + 2 == nsub) {
+      iter<1>(st, sa, sb, pb, ops, i, tpos);
+      copy_scores(sa, sb);
+      ++i;
+    }
+    iter<2>(st, sa, sb, pb, ops, i, tpos);
+    if (grp) __syncthreads();
   }
 };
 
@@ -471,7 +524,7 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
                                              int diag_from, const int (&tpos)[QT],
                                              QueryLoad&& load_queries) {
   Walker<D, QT> w;
-  w.lds = lds;
+  w.lds = (lds_char*)lds;
   w.kbase = kbase;
   w.vbase = vbase;
   w.rs = rs;
