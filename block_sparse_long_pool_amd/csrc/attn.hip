@@ -24,6 +24,8 @@
 // spreads the MFMA operand reads over all banks and lets every read use a per-lane
 // base address plus an immediate offset.
 // Online softmax in the log2 domain (scale * log2(e) folded into one FMA).
+#include <algorithm>
+
 #include "moba_internal.h"
 
 namespace moba {
@@ -169,7 +171,11 @@ __device__ __forceinline__ void state_init(WaveState<D, QT>& st) {
 // slots of a phase read the first operands of the next one, across the barrier too,
 // so no phase starts by waiting on the LDS.  Staging past the last subtile re-stages
 // the last subtile into buffers nobody reads again.
-template <int D, int QT>
+// CHAIN: the walk runs over the subtiles of all of a persistent workgroup's tiles one
+// after the other (virtual subtile i is subtile i % nsub of the workgroup's tile
+// i / nsub), so the next tile's first K/V subtiles are staged, and its query rows
+// loaded, while the current tile finishes: see attn_history_chain_kernel.
+template <int D, int QT, bool CHAIN = false>
 struct Walker {
   using L = Lds<D>;
   static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
@@ -199,6 +205,36 @@ struct Walker {
   uint32_t kl, vl;             // the lane's byte offsets of its K and V operand reads
   TileOffsets<D> to;
   TileRegs<D> kst, vst, pre;   // staging registers (pre: K(1) in the prologue only)
+  // CHAIN: the workgroup's tiles (tile s is tiles[blockIdx.x + s * gridDim.x]), their
+  // count, and what locates a tile's block (key_end - key_begin keys, a multiple of KN,
+  // so no subtile is masked); the walk's position (subtile im of tile it); the two
+  // staging streams' next subtile (local index, tile, the tile's first-key offset)
+  const int4* tiles;
+  int ntw, nb, ng, g0, hkv;
+  SeqMap sq;
+  int im, it;
+  int kt_l, kt_t, vt_l, vt_t;
+  size_t kt_off, vt_off;
+  __device__ __forceinline__ int len() const { return CHAIN ? nsub * ntw : nsub; }
+  // element offset of the first key of the block of the workgroup's tile s (the last
+  // tile past the end)
+  __device__ __forceinline__ size_t tile_keys(int s) const {
+    const int list = tiles[blockIdx.x + min(s, ntw - 1) * gridDim.x].x;
+    const int j = list % nb, gi = (list / nb) % ng, b = list / (nb * ng);
+    return (((size_t)sq.tok0(b) + (size_t)j * (key_end - key_begin)) * hkv + g0 + gi) * D;
+  }
+  // CHAIN: load a staging stream's next subtile (the last subtile of the last tile once
+  // past the end), then advance the stream by one subtile
+  __device__ __forceinline__ void load_stream(TileRegs<D>& r, bool isv, int& l, int& t,
+                                              size_t& off) {
+    const int lc = t < ntw ? l : nsub - 1;
+    tile_load<D>(r, to, (isv ? vbase : kbase) + off + (size_t)lc * KN * rs, rs, KN);
+    if (++l == nsub) {
+      l = 0;
+      ++t;
+      off = tile_keys(t);
+    }
+  }
 
   // The buffer offsets pass through an empty asm so that the compiler adds them to the
   // lane's base address at run time: folded into the reads' 16-bit immediate offsets,
@@ -214,15 +250,21 @@ struct Walker {
     asm("" : "+s"(off));
     return lds + off;
   }
-  __device__ __forceinline__ int kb(int i) const { return key_begin + i * KN; }
+  __device__ __forceinline__ int kb(int i) const {
+    return key_begin + (CHAIN ? i % nsub : i) * KN;
+  }
   __device__ __forceinline__ int nvalid(int i) const { return min(KN, key_end - kb(i)); }
   __device__ __forceinline__ bool masked(int i) const {
+    if constexpr (CHAIN) return false;
     return kb(i) + KN > key_end || kb(i) + KN - 1 > diag_from;
   }
-  // global -> registers: subtile i (the last one past the end) of K or V
-  __device__ __forceinline__ void load_sub(TileRegs<D>& r, const uint16_t* base, int i) {
-    const int t = min(i, nsub - 1);
-    tile_load<D>(r, to, base + (size_t)kb(t) * rs, rs, nvalid(t));
+  // global -> registers: subtile i (the last one past the end) of K (isv false) or V
+  __device__ __forceinline__ void load_sub(TileRegs<D>& r, bool isv, int i) {
+    const int t = min(i, len() - 1);
+    const uint16_t* p;
+    if constexpr (CHAIN) p = (isv ? vbase : kbase) + tile_keys(t / nsub) + (size_t)(kb(t) - key_begin) * rs;
+    else p = (isv ? vbase : kbase) + (size_t)kb(t) * rs;
+    tile_load<D>(r, to, p, rs, nvalid(t));
   }
   // registers -> LDS: chunk c of a subtile into a buffer of row stride STRIDE
   template <int STRIDE>
@@ -241,8 +283,13 @@ struct Walker {
       if (s & 1) store_chunk<L::VS>(vst, s >> 1, vbuf(n + 1));
       else store_chunk<L::KS>(kst, s >> 1, kbuf(n + 2));
     } else if (s == 2 * NC) {
-      load_sub(kst, kbase, n + 3);
-      load_sub(vst, vbase, n + 2);
+      if constexpr (CHAIN) {
+        load_stream(kst, false, kt_l, kt_t, kt_off);
+        load_stream(vst, true, vt_l, vt_t, vt_off);
+      } else {
+        load_sub(kst, false, n + 3);
+        load_sub(vst, true, n + 2);
+      }
     }
   }
 
@@ -385,10 +432,10 @@ struct Walker {
   // Phase B(i): O^T += V^T P^T for the subtile in buffer vq next to the mask and row max
   // of nxt (subtile i+1, when NEXT), then the rescale decision.  Operand stream and
   // staging as in phase_a.
-  template <bool NEXT, int NX, bool STAGE>
+  template <bool NEXT, int NX, bool STAGE, typename Post>
   __device__ __forceinline__ void phase_b(WaveState<D, QT>& st, Scores& nxt, const POps& pb,
                                           Ops& ops, const lds_char* vq, const lds_char* nb, int i,
-                                          int n, const int (&tpos)[QT]) {
+                                          int n, const int (&tpos)[QT], Post&& post) {
     if (NEXT && masked(i + 1)) mask_scores(nxt, i + 1, tpos);
     constexpr int MPS = 16 * NH / NPV;  // max elements per slot and query tile
     static_assert(MPS * NPV == 16 * NH, "the row max splits evenly over the PV slots");
@@ -415,31 +462,50 @@ struct Walker {
       if (STAGE) stage_slot(j, n);
       __builtin_amdgcn_sched_barrier(0);
     }
+    float mxs[QT];
     if (NEXT) {
-      float mxs[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) mxs[qt] = pair_max(mx[qt]) * sl;
-      rescale(st, mxs);
     }
+    post();
+    if (NEXT) rescale(st, mxs);
   }
 
   // Subtile i: A(i), then B(i).  Both groups run this same code; group 1's barrier
   // falls between the two phases, group 0's after B.  A(i) carries the staging of
-  // interval i + 1 - grp.  KIND 0: i + 2 < nsub, 1: i = nsub - 2, 2: i = nsub - 1.
-  template <int KIND>
+  // interval i + 1 - grp.  KIND 0: i + 2 < len, 1: i = len - 2, 2: i = len - 1.
+  // CHAIN: when A(i+1) starts the next tile (its QK^T is that tile's first), B(i)
+  // first loads the tile's query rows (next_q); when B(i) ends a tile, `bound` stores
+  // it and resets the state after the PV MFMAs, before the rescale that starts the next.
+  template <int KIND, typename NextQ, typename Bound>
   __device__ __forceinline__ void iter(WaveState<D, QT>& st, Scores& cur, Scores& nxt,
-                                       POps& pb, Ops& ops, int i, const int (&tpos)[QT]) {
+                                       POps& pb, Ops& ops, int i, const int (&tpos)[QT],
+                                       NextQ&& next_q, Bound&& bound) {
     const int n = i + 1 - grp;
     if (KIND < 2) phase_a<true, true, 2, true>(st, cur, nxt, pb, ops, kbuf(i + 1), vbuf(i), n);
     else phase_a<false, true, 0, true>(st, cur, nxt, pb, ops, nullptr, nullptr, n);
     if (grp) __syncthreads();
+    if constexpr (CHAIN && KIND == 0) {
+      if (im == nsub - 2) next_q(it + 1);
+    }
+    auto post = [&] {
+      if constexpr (CHAIN && KIND == 0) {
+        if (im == nsub - 1) bound(it);
+      }
+    };
     if (KIND == 0)
-      phase_b<true, 1, false>(st, nxt, pb, ops, vbuf(i), kbuf(i + 2), i, n, tpos);
+      phase_b<true, 1, false>(st, nxt, pb, ops, vbuf(i), kbuf(i + 2), i, n, tpos, post);
     else if (KIND == 1)
-      phase_b<true, 2, false>(st, nxt, pb, ops, vbuf(i), vbuf(i + 1), i, n, tpos);
+      phase_b<true, 2, false>(st, nxt, pb, ops, vbuf(i), vbuf(i + 1), i, n, tpos, post);
     else
-      phase_b<false, 0, false>(st, nxt, pb, ops, vbuf(i), nullptr, i, n, tpos);
+      phase_b<false, 0, false>(st, nxt, pb, ops, vbuf(i), nullptr, i, n, tpos, post);
     if (!grp) __syncthreads();
+    if constexpr (CHAIN) {
+      if (++im == nsub) {
+        im = 0;
+        ++it;
+      }
+    }
   }
 
   __device__ __forceinline__ static void copy_scores(Scores& dst, const Scores& src) {
@@ -458,12 +524,30 @@ struct Walker {
     kl = (uint32_t)((lane & 31) * L::KS + hf * 16);
     vl = (uint32_t)((4 * hf + ((lane & 15) >> 2)) * L::VS +
                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
-    load_sub(kst, kbase, 0);
-    load_sub(pre, kbase, 1);
-    load_sub(vst, vbase, 0);
+    if constexpr (CHAIN) {
+      // tile 0's first subtiles (a tile has at least three); the streams then go on
+      // from K(3) and V(2)
+      im = 0;
+      it = 0;
+      kt_off = vt_off = tile_keys(0);
+      kt_l = 0;
+      kt_t = 0;
+      vt_l = 0;
+      vt_t = 0;
+      load_stream(kst, false, kt_l, kt_t, kt_off);
+      load_stream(pre, false, kt_l, kt_t, kt_off);
+      load_stream(vst, true, vt_l, vt_t, vt_off);
+    } else {
+      load_sub(kst, false, 0);
+      load_sub(pre, false, 1);
+      load_sub(vst, true, 0);
+    }
   }
 
-  __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT]) {
+  template <typename NextQ, typename Bound>
+  __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT],
+                                      NextQ&& next_q, Bound&& bound) {
+    const int nv = len();
     // prologue: K(0), K(1) and V(0) into LDS, then the registers that interval 0
     // stages (K(2), V(1))
 #pragma unroll
@@ -472,8 +556,13 @@ struct Walker {
       store_chunk<L::KS>(pre, c, kbuf(1));
       store_chunk<L::VS>(vst, c, vbuf(0));
     }
-    load_sub(kst, kbase, 2);
-    load_sub(vst, vbase, 1);
+    if constexpr (CHAIN) {
+      load_stream(kst, false, kt_l, kt_t, kt_off);
+      load_stream(vst, true, vt_l, vt_t, vt_off);
+    } else {
+      load_sub(kst, false, 2);
+      load_sub(vst, true, 1);
+    }
     __syncthreads();
     Scores sa, sb;
     POps pb;
@@ -482,10 +571,10 @@ struct Walker {
     for (int j = 0; j < PF; ++j) ops[j] = kread(kbuf(0), j);
     // P carries group 0's staging of interval 0 (group 1's is in its A(0))
     if (grp == 0) {
-      if (nsub > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
+      if (nv > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
       else phase_a<true, false, 2, true>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
     } else {
-      if (nsub > 1) phase_a<true, false, 1, false>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
+      if (nv > 1) phase_a<true, false, 1, false>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
       else phase_a<true, false, 2, false>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
     }
     max_all(st, sa, 0, tpos);
@@ -493,21 +582,21 @@ struct Walker {
     // two subtiles per iteration so that the score buffers keep their roles (S(i) in sa
     // for even i); the last ones move S(i+1) into sa instead
     int i = 0;
-    for (; i + 3 < nsub; i += 2) {
-      iter<0>(st, sa, sb, pb, ops, i, tpos);
-      iter<0>(st, sb, sa, pb, ops, i + 1, tpos);
+    for (; i + 3 < nv; i += 2) {
+      iter<0>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
+      iter<0>(st, sb, sa, pb, ops, i + 1, tpos, next_q, bound);
     }
-    if (i + 3 == nsub) {
-      iter<0>(st, sa, sb, pb, ops, i, tpos);
+    if (i + 3 == nv) {
+      iter<0>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
       copy_scores(sa, sb);
       ++i;
     }
-    if (i + 2 == nsub) {
-      iter<1>(st, sa, sb, pb, ops, i, tpos);
+    if (i + 2 == nv) {
+      iter<1>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
       copy_scores(sa, sb);
       ++i;
     }
-    iter<2>(st, sa, sb, pb, ops, i, tpos);
+    iter<2>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
     if (grp) __syncthreads();
   }
 };
@@ -538,7 +627,7 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
   w.grp = wave / (kAttnWaves / 2);
   w.begin();
   load_queries();
-  w.run(st, tpos);
+  w.run(st, tpos, [](int) {}, [](int) {});
 }
 
 // normalise and store one query tile's partial: o rounded to bf16 (nearest even) [D],
@@ -717,6 +806,91 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
     store_partial(st, qt, vq[qt], part_o + (row * (topk - 1) + slq[qt]) * D,
                   part_lse + (size_t)slq[qt] * ls + row);
   }
+}
+
+// ------------------------------------------------------ history, persistent (a4)
+// The same attention as attn_history_kernel, but one workgroup per CU walks all of its
+// tiles (tiles[blockIdx.x + s * gridDim.x], s = 0, 1, ...) as one continuous walk: the
+// staging runs into the next tile's block while the current tile finishes, the next
+// tile's query rows load during the last PV phase of the current one, and its first
+// QK^T shares a phase with the current tile's last exponentials.  So a tile pays no
+// prologue (first K/V loads, query gather, pipeline fill) and no workgroup launch, which
+// in the one-tile-per-workgroup kernel are a fixed cost of a few microseconds per tile.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_chain_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
+    float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, size_t ls) {
+  __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
+  const int ntiles = *tile_count;
+  if ((int)blockIdx.x >= ntiles) return;
+  const int ntw = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G = hq / hkv, ngq = ng * G;
+  const int wave = threadIdx.x >> 6, n = threadIdx.x & 31;
+  const int sb = entry_slot_bits(topk);
+  // this lane's index entry in the workgroup's tile s (all ones: no row)
+  auto entry_of = [&](int s) -> uint32_t {
+    const int4 tl = tiles[blockIdx.x + s * gridDim.x];
+    const int e = tl.y + wave * 32 + n;
+    return e < tl.z ? entries[e] : 0xffffffffu;
+  };
+  auto tile_bg = [&](int s, int& b, int& gi) {
+    const int list = tiles[blockIdx.x + s * gridDim.x].x;
+    gi = (list / nb) % ng;
+    b = list / (nb * ng);
+  };
+  WaveState<D, 1> st;
+  const int tpos[1] = {0x7fffffff};    // history keys all precede the rows
+  auto load_tile_q = [&](int s, uint32_t ent) {
+    int b, gi;
+    tile_bg(s, b, gi);
+    const bool valid = ent != 0xffffffffu;
+    const int rr = valid ? (int)(ent >> sb) : 0;
+    load_q(st, 0, q + ((size_t)((size_t)sq.tok0(b) + rr / G) * hq + (g0 + gi) * G + rr % G) * D,
+           valid);
+  };
+  auto store_tile = [&](int s, uint32_t ent) {
+    int b, gi;
+    tile_bg(s, b, gi);
+    const bool valid = ent != 0xffffffffu;
+    const int rr = valid ? (int)(ent >> sb) : 0;
+    const int slot = (int)(ent & ((1u << sb) - 1u));
+    const size_t row = sq.prow(b, gi * G + rr % G, ngq) + rr / G;
+    store_partial(st, 0, valid, part_o + (row * (topk - 1) + slot) * D,
+                  part_lse + (size_t)slot * ls + row);
+  };
+  Walker<D, 1, true> w;
+  w.lds = (lds_char*)lds;
+  w.kbase = k;
+  w.vbase = v;
+  w.rs = (size_t)hkv * D;
+  w.key_begin = 0;
+  w.key_end = block;
+  w.diag_from = 0x7fffffff;
+  w.sl = sl;
+  w.grp = __builtin_amdgcn_readfirstlane(wave) / (kAttnWaves / 2);
+  w.tiles = tiles;
+  w.ntw = ntw;
+  w.nb = nb;
+  w.ng = ng;
+  w.g0 = g0;
+  w.hkv = hkv;
+  w.sq = sq;
+  w.begin();
+  uint32_t ent_cur = entry_of(0);
+  uint32_t ent_nx = ntw > 1 ? entry_of(1) : 0xffffffffu;
+  load_tile_q(0, ent_cur);
+  state_init(st);
+  w.run(st, tpos, [&](int s) { load_tile_q(s, ent_nx); },
+        [&](int s) {
+          store_tile(s, ent_cur);
+          state_init(st);
+          ent_cur = ent_nx;
+          ent_nx = s + 2 < ntw ? entry_of(s + 2) : 0xffffffffu;
+        });
+  store_tile(ntw - 1, ent_cur);
 }
 
 // ------------------------------------------------- history, blocks of <= 128 keys (a4)
@@ -1052,6 +1226,30 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
     else MOBA_RES_D(64);
 #undef MOBA_RES_D
 #undef MOBA_RES
+    return hipGetLastError();
+  }
+  // Blocks of up to 1024 keys (walks of up to 16 subtiles, where a tile's fixed cost is
+  // a large share) run the persistent chained kernel: 32K tokens with B = 512, 0.78 ->
+  // 0.72 ms.  Longer blocks keep one tile per workgroup: with 64-subtile walks the fixed
+  // cost is small, and the hardware's dynamic dispatch balances the CUs better than the
+  // chained kernel's fixed tile assignment (128K, B = 4096: 70.9 against 72.6 ms).
+  if (s.block % KN == 0 && s.block <= 16 * KN) {
+    // one persistent workgroup per CU (the kernel's LDS allows one)
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    const int grid = std::max(1, std::min(max_tiles, ncu));
+    if (s.d == 128)
+      hipLaunchKernelGGL((attn_history_chain_kernel<128>), dim3(grid), dim3(kAttnThreads), 0, st,
+                         q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng, s.nb(),
+                         tiles, tile_count, entries, part_o, part_lse,
+                         part_lse_slot_stride(s, ng));
+    else
+      hipLaunchKernelGGL((attn_history_chain_kernel<64>), dim3(grid), dim3(kAttnThreads), 0, st,
+                         q, k, v, s.seqs(), s.hq, s.hkv, s.block, s.topk, sl, g0, ng, s.nb(),
+                         tiles, tile_count, entries, part_o, part_lse,
+                         part_lse_slot_stride(s, ng));
     return hipGetLastError();
   }
   if (s.d == 128)
