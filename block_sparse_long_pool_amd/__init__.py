@@ -24,7 +24,8 @@ __all__ = [
     "stage_workspace_bytes", "lib", "STAGES", "alloc_workspace", "dense_forward", "attention",
     "backward", "backward_workspace_bytes", "forward_varlen", "varlen_workspace_bytes",
     "key_short_conv", "backward_varlen", "backward_varlen_workspace_bytes", "decode",
-    "decode_workspace_bytes", "forward_noalloc",
+    "decode_workspace_bytes", "forward_noalloc", "history_partials", "current_merge",
+    "part_dim_order",
 ]
 
 # names of the steps timed by profile=True, in the library's order
@@ -74,6 +75,10 @@ _SIGS = {
     "moba_index_entries": (ctypes.c_int64, [_i, _i, _i, _i, _i, _i, _i]),
     "moba_build_index": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz,
                               _vp]),
+    "moba_history_partials": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
+                                   _vp, ctypes.c_uint32, _vp, _vp, _vp, _sz, _vp]),
+    "moba_current_merge": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
+                                _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -648,3 +653,99 @@ def build_index(idx, hkv: int, block: int, topk: int, kv_begin: int = 0,
                                   ws.numel(), _stream_ptr())
     _raise(st, "moba_build_index")
     return offs, ent[:n]
+
+
+def part_dim_order(head_dim: int) -> list:
+    """The head dimension held at each position of a ``history_partials`` part row:
+    position p = hf*d/2 + dt*16 + ii*4 + r holds dimension dt*32 + ii*8 + hf*4 + r."""
+    half = head_dim // 2
+    order = []
+    for p in range(head_dim):
+        hf, rem = divmod(p, half)
+        dt, rem = divmod(rem, 16)
+        ii, r = divmod(rem, 4)
+        order.append(dt * 32 + ii * 8 + hf * 4 + r)
+    return order
+
+
+def history_partials(q, k, v, list_offsets, entries, block: int, topk: int,
+                     scale: float | None = None, kv_begin: int = 0,
+                     kv_count: int | None = None, tile_order_seed: int = 0,
+                     part_o=None, part_lse=None):
+    """History-attention stage over an inverted index from ``build_index`` (same kv
+    range): (part_o bf16 [b, kv_count*G, T, topk-1, d] with each row's d values in the
+    order ``part_dim_order(d)``, part_lse float32 [topk-1, b, kv_count*G, T]).  Slots a row does not have are left as they were (zero
+    when the buffers are allocated here).  ``tile_order_seed`` != 0 runs the tiles in a
+    seeded permuted order (the parts must not change)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(list_offsets, "list_offsets", torch.int32, 1)
+    _need(entries, "entries", torch.int32, 1)
+    b, T, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (b, T, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [b, T, hkv, d] matching q")
+    if kv_count is None:
+        kv_count = hkv - kv_begin
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _raise(check_args(b, T, hq, hkv, d, block, topk, scale), "moba_history_partials")
+    G = hq // hkv
+    shape_o = (b, kv_count * G, T, max(topk - 1, 1), d)
+    shape_l = (max(topk - 1, 1), b, kv_count * G, T)
+    if part_o is None:
+        part_o = torch.zeros(shape_o, dtype=torch.bfloat16, device=q.device)
+    if part_lse is None:
+        part_lse = torch.zeros(shape_l, dtype=torch.float32, device=q.device)
+    if tuple(part_o.shape) != shape_o or tuple(part_lse.shape) != shape_l:
+        raise ValueError("part_o / part_lse shapes do not match the kv range")
+    _need(part_o, "part_o", torch.bfloat16, 5)
+    _need(part_lse, "part_lse", torch.float32, 4)
+    ws = _alloc_workspace(stage_workspace_bytes(b, T, hq, hkv, d, block, topk), q.device)
+    _one_device(q, k, v, list_offsets, entries, part_o, part_lse, ws)
+    with torch.cuda.device(q.device):
+        st = lib.moba_history_partials(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv,
+                                       d, block, topk, float(scale), kv_begin, kv_count,
+                                       list_offsets.data_ptr(), entries.data_ptr(),
+                                       int(tile_order_seed) & 0xffffffff, part_o.data_ptr(),
+                                       part_lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       _stream_ptr())
+    _raise(st, "moba_history_partials")
+    return part_o, part_lse
+
+
+def current_merge(q, k, v, part_o, part_lse, block: int, topk: int,
+                  scale: float | None = None, kv_begin: int = 0, kv_count: int | None = None,
+                  out=None, lse=None):
+    """Current-block stage merged with the history parts of ``history_partials`` (same
+    kv range): writes out [b, T, Hq, d] bf16 and lse [b, Hq, T] float32 at the heads of
+    kv-heads [kv_begin, kv_begin + kv_count) and returns (out, lse)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    b, T, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (b, T, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [b, T, hkv, d] matching q")
+    if kv_count is None:
+        kv_count = hkv - kv_begin
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _raise(check_args(b, T, hq, hkv, d, block, topk, scale), "moba_current_merge")
+    if topk > 1:
+        _need(part_o, "part_o", torch.bfloat16, 5)
+        _need(part_lse, "part_lse", torch.float32, 4)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((b, hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or tuple(lse.shape) != (b, hq, T):
+        raise ValueError("out / lse shapes do not match q")
+    _one_device(q, k, v, out, lse, *([part_o, part_lse] if topk > 1 else []))
+    with torch.cuda.device(q.device):
+        st = lib.moba_current_merge(q.data_ptr(), k.data_ptr(), v.data_ptr(), b, T, hq, hkv, d,
+                                    block, topk, float(scale), kv_begin, kv_count,
+                                    part_o.data_ptr() if topk > 1 else None,
+                                    part_lse.data_ptr() if topk > 1 else None,
+                                    out.data_ptr(), lse.data_ptr(), _stream_ptr())
+    _raise(st, "moba_current_merge")
+    return out, lse

@@ -217,6 +217,76 @@ __global__ __launch_bounds__(kThreads) void index_scatter_kernel(
   }
 }
 
+// tile_offsets of lists given by their offsets alone: the exclusive scan of
+// ceil(count / tile_m) over lists, the total in tile_offsets[nlists] (one workgroup)
+__global__ __launch_bounds__(kThreads) void tiles_scan_kernel(
+    const int32_t* __restrict__ list_offsets, int nlists, int tile_m,
+    int32_t* __restrict__ tile_offsets) {
+  __shared__ int32_t sb[kThreads];
+  __shared__ int32_t cb;
+  if (threadIdx.x == 0) cb = 0;
+  __syncthreads();
+  for (int l0 = 0; l0 < nlists; l0 += kThreads) {
+    const int l = l0 + threadIdx.x;
+    const int w = l < nlists ? (list_offsets[l + 1] - list_offsets[l] + tile_m - 1) / tile_m : 0;
+    sb[threadIdx.x] = w;
+    __syncthreads();
+    for (int o = 1; o < kThreads; o <<= 1) {
+      const int y = threadIdx.x >= o ? sb[threadIdx.x - o] : 0;
+      __syncthreads();
+      sb[threadIdx.x] += y;
+      __syncthreads();
+    }
+    const int ib = sb[threadIdx.x];
+    const int b0 = cb;
+    if (l < nlists) tile_offsets[l] = b0 + ib - w;
+    __syncthreads();
+    if (threadIdx.x == kThreads - 1) cb = b0 + ib;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tile_offsets[nlists] = cb;
+}
+
+// dst[i] = src[(a * i + c) mod n] for the n tiles: a is the first number coprime to n
+// at or after a seeded start, so the map is a permutation of the tile order
+__global__ __launch_bounds__(256) void tiles_permute_kernel(const int4* __restrict__ src,
+                                                            const int32_t* __restrict__ count,
+                                                            uint32_t seed, int max_tiles,
+                                                            int4* __restrict__ dst) {
+  const int n = *count;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n || i >= max_tiles) return;
+  auto gcd = [](unsigned x, unsigned y) {
+    while (y) {
+      const unsigned r = x % y;
+      x = y;
+      y = r;
+    }
+    return x;
+  };
+  unsigned a = (unsigned)(((unsigned long long)seed * 2654435761ull) % (unsigned)n);
+  if (a == 0) a = 1;
+  while (gcd(a, (unsigned)n) != 1u) a = a + 1 == (unsigned)n ? 1u : a + 1;
+  const unsigned c = (unsigned)(((unsigned long long)seed * 40503ull + 7ull) % (unsigned)n);
+  dst[i] = src[((unsigned long long)a * (unsigned)i + c) % (unsigned)n];
+}
+
+hipError_t launch_tiles(const int32_t* list_offsets, int nlists, int tile_m, int max_tiles,
+                        int32_t* tile_offsets, int4* tiles, uint32_t perm_seed,
+                        int4* tiles_tmp, hipStream_t st) {
+  hipLaunchKernelGGL(tiles_scan_kernel, dim3(1), dim3(kThreads), 0, st, list_offsets, nlists,
+                     tile_m, tile_offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nlists == 0) return e;
+  int4* first = perm_seed ? tiles_tmp : tiles;
+  hipLaunchKernelGGL(index_tiles_kernel, dim3(nlists), dim3(64), 0, st, list_offsets,
+                     tile_offsets, tile_m, first);
+  if ((e = hipGetLastError()) != hipSuccess || !perm_seed || max_tiles <= 0) return e;
+  hipLaunchKernelGGL(tiles_permute_kernel, dim3((max_tiles + 255) / 256), dim3(256), 0, st,
+                     tiles_tmp, tile_offsets + nlists, perm_seed, max_tiles, tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int tile_m,
                         int32_t* chunk_counts, int32_t* list_count,
                         int32_t* list_offsets, int32_t* tile_offsets, int4* tiles,

@@ -636,6 +636,29 @@ bool index_unsupported(int seqlen, int hq, int hkv, int block, int topk) {
   if ((seqlen + block - 1) / block > kMaxBlocks) return true;
   return (long long)seqlen * (hq / hkv) >= (1ll << (32 - moba::entry_slot_bits(topk)));
 }
+
+// The history stage's tile list for kv_count kv-heads: tile rows, tile count bound,
+// and the workspace (tile offsets, the tiles, and a second tile array for a permuted
+// order).
+struct HistoryTiles {
+  int tile_m;
+  long long nlists, max_tiles;
+  size_t offsets_bytes, tiles_bytes;
+};
+HistoryTiles history_tiles(const Shape& s, int kv_count) {
+  HistoryTiles h;
+  const long long n_entries = (long long)s.b * kv_count * s.G() * entries_per_head(s);
+  h.tile_m = moba::history_tile_rows(s, n_entries);
+  h.nlists = (long long)s.b * kv_count * s.nb();
+  h.max_tiles = (n_entries + h.tile_m - 1) / h.tile_m + h.nlists;
+  h.offsets_bytes = align_up((size_t)(h.nlists + 1) * sizeof(int32_t));
+  h.tiles_bytes = align_up((size_t)h.max_tiles * sizeof(int4));
+  return h;
+}
+size_t history_stage_bytes(const Shape& s, int kv_count) {
+  const HistoryTiles h = history_tiles(s, kv_count);
+  return h.offsets_bytes + 2 * h.tiles_bytes;
+}
 }  // namespace
 
 extern "C" {
@@ -650,7 +673,9 @@ size_t moba_stage_workspace_bytes(int batch, int seqlen, int hq, int hkv, int he
   const size_t b2 = align_up((size_t)s.b * s.hkv * s.nb() * s.d * sizeof(uint16_t)) * 2;
   const size_t c = L.tiles - L.chunk_counts;
   size_t m = a > b2 ? a : b2;
-  return m > c ? m : c;
+  m = m > c ? m : c;
+  const size_t h = s.KH() > 0 ? history_stage_bytes(s, s.hkv) : 0;
+  return m > h ? m : h;
 }
 
 int moba_pool_centroids(const void* k, int batch, int seqlen, int hkv, int head_dim,
@@ -719,6 +744,54 @@ int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
       reinterpret_cast<int32_t*>(ws), reinterpret_cast<int32_t*>(ws + cc), list_offsets,
       reinterpret_cast<int32_t*>(ws + cc + lc), nullptr, entries,
       (long long)s.b * kv_count * s.G() * entries_per_head(s),
+      static_cast<hipStream_t>(stream)));
+}
+
+int moba_history_partials(const void* q, const void* k, const void* v, int batch,
+                          int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+                          float scale, int kv_begin, int kv_count,
+                          const int32_t* list_offsets, const uint32_t* entries,
+                          uint32_t tile_order_seed, void* part_o, float* part_lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !list_offsets || !entries || !part_o || !part_lse || !workspace)
+    return MOBA_ERR_INVALID_ARG;
+  if (kv_begin < 0 || kv_count <= 0 || kv_begin + kv_count > hkv) return MOBA_ERR_INVALID_ARG;
+  if (topk < 2) return MOBA_ERR_UNSUPPORTED;  // no history slots
+  if (index_unsupported(seqlen, hq, hkv, block, topk)) return MOBA_ERR_UNSUPPORTED;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  const HistoryTiles h = history_tiles(s, kv_count);
+  if (h.max_tiles >= (1ll << 31)) return MOBA_ERR_UNSUPPORTED;
+  if (h.offsets_bytes + 2 * h.tiles_bytes > workspace_bytes) return MOBA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws);
+  int4* tiles = reinterpret_cast<int4*>(ws + h.offsets_bytes);
+  int4* tmp = reinterpret_cast<int4*>(ws + h.offsets_bytes + h.tiles_bytes);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  MOBA_TRY(moba::launch_tiles(list_offsets, (int)h.nlists, h.tile_m, (int)h.max_tiles,
+                              tile_offsets, tiles, tile_order_seed, tmp, hs));
+  return hip_status(moba::launch_attn_history(
+      s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), scale, kv_begin, kv_count, tiles,
+      tile_offsets + h.nlists, (int)h.max_tiles, entries, static_cast<uint16_t*>(part_o),
+      part_lse, hs));
+}
+
+int moba_current_merge(const void* q, const void* k, const void* v, int batch, int seqlen,
+                       int hq, int hkv, int head_dim, int block, int topk, float scale,
+                       int kv_begin, int kv_count, const void* part_o,
+                       const float* part_lse, void* out, float* lse, void* stream) {
+  int st = check(batch, seqlen, hq, hkv, head_dim, block, topk, scale);
+  if (st != MOBA_OK) return st;
+  if (!q || !k || !v || !out || !lse) return MOBA_ERR_INVALID_ARG;
+  if (topk > 1 && (!part_o || !part_lse)) return MOBA_ERR_INVALID_ARG;
+  if (kv_begin < 0 || kv_count <= 0 || kv_begin + kv_count > hkv) return MOBA_ERR_INVALID_ARG;
+  const Shape s{batch, seqlen, hq, hkv, head_dim, block, topk};
+  return hip_status(moba::launch_attn_current(
+      s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), scale, kv_begin, kv_count,
+      static_cast<const uint16_t*>(part_o), part_lse, static_cast<uint16_t*>(out), lse,
       static_cast<hipStream_t>(stream)));
 }
 

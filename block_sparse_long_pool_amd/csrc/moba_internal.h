@@ -127,6 +127,12 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
                         int32_t* list_offsets, int32_t* tile_offsets,
                         int4* tiles, uint32_t* entries, long long cap,
                         hipStream_t st);
+// the tile list of lists given by their offsets (as moba_build_index writes them):
+// tile_offsets [nlists + 1] (the tile count last) and tiles; with perm_seed != 0 the
+// tiles are written in a seeded permuted order (through tiles_tmp, max_tiles long)
+hipError_t launch_tiles(const int32_t* list_offsets, int nlists, int tile_m, int max_tiles,
+                        int32_t* tile_offsets, int4* tiles, uint32_t perm_seed,
+                        int4* tiles_tmp, hipStream_t st);
 // (a4) history attention partials, (a5) current block fused with the merge
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,

@@ -340,6 +340,51 @@ int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
                      int32_t* list_offsets, uint32_t* entries, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* History attention (FlashMoBA story on hyper.ai, paragraph on Gather-and-Densify:
+ * the queries that chose a KV block are gathered into a dense tile and run against
+ * that block; paper summary page, "Approach": each query attends the keys of its
+ * selected blocks).  For every entry of the inverted index of kv-heads [kv_begin,
+ * kv_begin + kv_count) (list_offsets and entries exactly as moba_build_index writes
+ * them for the same range), softmax attention of the entry's query row (t, h) over
+ * all keys of its block j, written as a part:
+ *   part_o    bf16 [batch][kv_count * G][T][topk - 1][head_dim]: the part's output
+ *             (normalised, rounded to nearest even) at the row's slot of block j, its
+ *             head_dim values in the order the kernel's lanes hold them: position
+ *             p = hf * head_dim/2 + dt * 16 + ii * 4 + r holds dimension
+ *             dt * 32 + ii * 8 + hf * 4 + r (hf < 2, dt < head_dim/32, ii < 4, r < 4),
+ *             so that each lane reads and writes one contiguous half of a row;
+ *   part_lse  fp32 [topk - 1][batch][kv_count * G][T]: ln sum_u exp(scale q.k_u).
+ * Heads h = kv_begin * G .. are numbered from 0 within the range.  Slots a row does
+ * not have (t / block <= slot) are not written.  Splitting a row's keys into such
+ * parts and merging them by log-sum-exp (moba_current_merge) gives the one-softmax
+ * result.  tile_order_seed 0 runs the tiles in list order; any other value runs them
+ * in a seeded permuted order, which must give bit-identical parts: each part is
+ * written by exactly one tile, so the launch order does not matter (a check for
+ * races between tiles).  Needs topk >= 2 (MOBA_ERR_UNSUPPORTED otherwise) and the
+ * index limits of moba_build_index; workspace: moba_stage_workspace_bytes.  Enqueued
+ * on `stream` without synchronising. */
+int moba_history_partials(const void* q, const void* k, const void* v, int batch,
+                          int seqlen, int hq, int hkv, int head_dim, int block, int topk,
+                          float scale, int kv_begin, int kv_count,
+                          const int32_t* list_offsets, const uint32_t* entries,
+                          uint32_t tile_order_seed, void* part_o, float* part_lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Current block and merge (paper summary page, "Approach": each query also attends its
+ * own current block, causally).  For every query head of kv-heads [kv_begin, kv_begin +
+ * kv_count): causal attention of (t, h) over keys c*block .. t of its block c,
+ * merged by log-sum-exp with the row's min(c, topk - 1) history parts from
+ * moba_history_partials (same layout and kv range): L = ln(e^lse_c + sum_s e^lse_s),
+ * out = e^(lse_c - L) o_c + sum_s e^(lse_s - L) o_s, lse = L, written into out
+ * [batch, seqlen, hq, head_dim] bf16 and lse [batch, hq, seqlen] fp32 at those heads.
+ * part_o and part_lse may be NULL when topk == 1.  pool -> gate -> build_index ->
+ * history_partials -> current_merge over all kv-heads is moba_forward, bit for bit,
+ * when topk * block < seqlen.  Needs no workspace; enqueued on `stream`. */
+int moba_current_merge(const void* q, const void* k, const void* v, int batch, int seqlen,
+                       int hq, int hkv, int head_dim, int block, int topk, float scale,
+                       int kv_begin, int kv_count, const void* part_o,
+                       const float* part_lse, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

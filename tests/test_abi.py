@@ -26,7 +26,8 @@ def moba():
 def test_header_declares_the_path(moba):
     names = declared_functions()
     for n in ["moba_check_args", "moba_workspace_bytes", "moba_forward", "moba_strerror",
-              "moba_pool_centroids", "moba_gate_topk", "moba_build_index"]:
+              "moba_pool_centroids", "moba_gate_topk", "moba_build_index",
+              "moba_history_partials", "moba_current_merge"]:
         assert n in names
 
 
@@ -134,6 +135,36 @@ def test_forward_rejects_bad_args_before_any_launch(moba):
     assert lib.moba_forward_timed(*args, None) == -1
     ev = (ctypes.c_void_p * (len(moba.STAGES) + 1))(*([1] * len(moba.STAGES) + [None]))
     assert lib.moba_forward_timed(*args, ev) == -1
+
+
+def test_history_and_merge_stages_reject_bad_args_before_any_launch(moba):
+    lib = moba.lib
+    shape = (1, 4096, 8, 2, 128, 256, 4, 0.088)
+    one = ctypes.c_void_p(1)        # non-null, never dereferenced: every call below fails
+    ws_needed = lib.moba_stage_workspace_bytes(1, 4096, 8, 2, 128, 256, 4)
+    assert ws_needed > 0
+
+    def hist(kv_begin=0, kv_count=2, topk=4, ptr=one, ws=ws_needed, d=128):
+        b, T, hq, hkv, _, B, _, sc = shape
+        return lib.moba_history_partials(ptr, ptr, ptr, b, T, hq, hkv, d, B, topk, sc,
+                                         kv_begin, kv_count, ptr, ptr, 0, ptr, ptr, ptr, ws,
+                                         None)
+    assert hist(ptr=None) == -1                   # null pointers
+    assert hist(kv_begin=1, kv_count=2) == -1     # kv range past hkv
+    assert hist(kv_count=0) == -1
+    assert hist(topk=1) == -2                     # no history slots
+    assert hist(d=96) == -2                       # unsupported head dim, before pointers
+    assert hist(ws=ws_needed // 1000) == -3       # workspace too small
+    b, T, hq, hkv, d, B, k, sc = shape
+    m = lib.moba_current_merge
+    assert m(None, None, None, b, T, hq, hkv, d, B, k, sc, 0, 2, None, None, None, None,
+             None) == -1
+    # topk > 1 needs the parts
+    assert m(one, one, one, b, T, hq, hkv, d, B, k, sc, 0, 2, None, None, one, one,
+             None) == -1
+    assert m(one, one, one, b, T, hq, hkv, d, B, k, sc, 2, 1, one, one, one, one, None) == -1
+    assert m(one, one, one, b, T, hq, hkv, 96, B, k, sc, 0, 2, one, one, one, one,
+             None) == -2
 
 
 def test_decode_args_and_workspace(moba):
