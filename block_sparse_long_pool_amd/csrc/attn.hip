@@ -113,6 +113,19 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& r, const TileOffsets<D>& 
   }
 }
 
+// The same through a descriptor made once for a whole key range, the subtile selected
+// by the scalar byte offset soff; rows past the range's end read as zeros.
+template <int D>
+__device__ __forceinline__ void tile_load_rs(TileRegs<D>& r, const TileOffsets<D>& o,
+                                             __amdgpu_buffer_rsrc_t rsrc, int soff) {
+  using R = TileRegs<D>;
+#pragma unroll
+  for (int i = 0; i < R::NC; ++i) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(o.off[i] * 2), soff, 0);
+    r.c[i] = __builtin_bit_cast(u32x4_t, x);
+  }
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) char lds_char;   // a byte of LDS
@@ -192,6 +205,7 @@ struct Walker {
 #endif
   static constexpr int SS = MOBA_ATTN_SS;          // first staging slot of an interval
   static_assert(SS + 2 * NC < NQK && SS + 2 * NC < NPV, "staging fits in one phase");
+
   using Scores = f32x16_t[NH][QT];
   using POps = bf16x8_t[QT][KN / 16];
   using Ops = u32x4_t[PF];
@@ -205,6 +219,8 @@ struct Walker {
   uint32_t kl, vl;             // the lane's byte offsets of its K and V operand reads
   TileOffsets<D> to;
   TileRegs<D> kst, vst, pre;   // staging registers (pre: K(1) in the prologue only)
+  // one buffer descriptor each for the K and V rows of [key_begin, key_end) (not CHAIN)
+  __amdgpu_buffer_rsrc_t kdesc, vdesc;
   // CHAIN: the workgroup's tiles (tile s is tiles[blockIdx.x + s * gridDim.x]), their
   // count, and what locates a tile's block (key_end - key_begin keys, a multiple of KN,
   // so no subtile is masked); the walk's position (subtile im of tile it); the two
@@ -260,6 +276,11 @@ struct Walker {
   }
   // global -> registers: subtile i (the last one past the end) of K (isv false) or V
   __device__ __forceinline__ void load_sub(TileRegs<D>& r, bool isv, int i) {
+    if constexpr (!CHAIN) {
+      const int t = min(i, nsub - 1);
+      tile_load_rs<D>(r, to, isv ? vdesc : kdesc, t * (int)(KN * rs * sizeof(uint16_t)));
+      return;
+    }
     const int t = min(i, len() - 1);
     const uint16_t* p;
     if constexpr (CHAIN) p = (isv ? vbase : kbase) + tile_keys(t / nsub) + (size_t)(kb(t) - key_begin) * rs;
@@ -293,8 +314,12 @@ struct Walker {
     }
   }
 
+  // QK^T MFMA j: 32-key half qk_kk(j), k-step qk_ks(j) (the NH accumulator chains
+  // alternate, so consecutive MFMAs are independent)
+  __device__ __forceinline__ static constexpr int qk_kk(int j) { return j % NH; }
+  __device__ __forceinline__ static constexpr int qk_ks(int j) { return j / NH; }
   __device__ __forceinline__ static int k_off(int j) {
-    return (j / KSTEPS) * 32 * L::KS + (j % KSTEPS) * 32;
+    return qk_kk(j) * 32 * L::KS + qk_ks(j) * 32;
   }
   // K operand of QK^T MFMA j of a subtile in buffer kbufp
   __device__ __forceinline__ u32x4_t kread(const lds_char* kbufp, int j) const {
@@ -385,7 +410,7 @@ struct Walker {
 #pragma unroll
     for (int j = 0; j < NQK; ++j) {
       if (NEXT) {
-        const int kk = j / KSTEPS, ks = j % KSTEPS;
+        const int kk = qk_kk(j), ks = qk_ks(j);
         const bf16x8_t a = as_bf16x8(ops[j % PF]);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
@@ -434,8 +459,8 @@ struct Walker {
   // staging as in phase_a.
   template <bool NEXT, int NX, bool STAGE, typename Post>
   __device__ __forceinline__ void phase_b(WaveState<D, QT>& st, Scores& nxt, const POps& pb,
-                                          Ops& ops, const lds_char* vq, const lds_char* nb, int i,
-                                          int n, const int (&tpos)[QT], Post&& post) {
+                                          Ops& ops, const lds_char* vq, const lds_char* nb,
+                                          int i, int n, const int (&tpos)[QT], Post&& post) {
     if (NEXT && masked(i + 1)) mask_scores(nxt, i + 1, tpos);
     constexpr int MPS = 16 * NH / NPV;  // max elements per slot and query tile
     static_assert(MPS * NPV == 16 * NH, "the row max splits evenly over the PV slots");
@@ -481,9 +506,15 @@ struct Walker {
   __device__ __forceinline__ void iter(WaveState<D, QT>& st, Scores& cur, Scores& nxt,
                                        POps& pb, Ops& ops, int i, const int (&tpos)[QT],
                                        NextQ&& next_q, Bound&& bound) {
-    const int n = i + 1 - grp;
-    if (KIND < 2) phase_a<true, true, 2, true>(st, cur, nxt, pb, ops, kbuf(i + 1), vbuf(i), n);
-    else phase_a<false, true, 0, true>(st, cur, nxt, pb, ops, nullptr, nullptr, n);
+    // B(i) carries the staging of interval i + 1, in which it runs for both groups.
+    // A wavefront raises its priority for the exp-heavy phase A: the two waves of a
+    // SIMD then get through an interval at the same pace instead of the older one
+    // finishing its phases early and idling at the barrier while the other runs alone.
+    const int n = i + 1;
+    __builtin_amdgcn_s_setprio(1);
+    if (KIND < 2) phase_a<true, true, 2, false>(st, cur, nxt, pb, ops, kbuf(i + 1), vbuf(i), n);
+    else phase_a<false, true, 0, false>(st, cur, nxt, pb, ops, nullptr, nullptr, n);
+    __builtin_amdgcn_s_setprio(0);
     if (grp) __syncthreads();
     if constexpr (CHAIN && KIND == 0) {
       if (im == nsub - 2) next_q(it + 1);
@@ -494,11 +525,11 @@ struct Walker {
       }
     };
     if (KIND == 0)
-      phase_b<true, 1, false>(st, nxt, pb, ops, vbuf(i), kbuf(i + 2), i, n, tpos, post);
+      phase_b<true, 1, true>(st, nxt, pb, ops, vbuf(i), kbuf(i + 2), i, n, tpos, post);
     else if (KIND == 1)
-      phase_b<true, 2, false>(st, nxt, pb, ops, vbuf(i), vbuf(i + 1), i, n, tpos, post);
+      phase_b<true, 2, true>(st, nxt, pb, ops, vbuf(i), vbuf(i + 1), i, n, tpos, post);
     else
-      phase_b<false, 0, false>(st, nxt, pb, ops, vbuf(i), nullptr, i, n, tpos, post);
+      phase_b<false, 0, true>(st, nxt, pb, ops, vbuf(i), nullptr, i, n, tpos, post);
     if (!grp) __syncthreads();
     if constexpr (CHAIN) {
       if (++im == nsub) {
@@ -538,6 +569,11 @@ struct Walker {
       load_stream(pre, false, kt_l, kt_t, kt_off);
       load_stream(vst, true, vt_l, vt_t, vt_off);
     } else {
+      const int bytes = (int)((size_t)(key_end - key_begin) * rs * sizeof(uint16_t));
+      kdesc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(kbase + (size_t)key_begin * rs), (short)0, bytes, 0x00020000);
+      vdesc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(vbase + (size_t)key_begin * rs), (short)0, bytes, 0x00020000);
       load_sub(kst, false, 0);
       load_sub(pre, false, 1);
       load_sub(vst, true, 0);
@@ -569,14 +605,9 @@ struct Walker {
     Ops ops;
 #pragma unroll
     for (int j = 0; j < PF; ++j) ops[j] = kread(kbuf(0), j);
-    // P carries group 0's staging of interval 0 (group 1's is in its A(0))
-    if (grp == 0) {
-      if (nv > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
-      else phase_a<true, false, 2, true>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
-    } else {
-      if (nv > 1) phase_a<true, false, 1, false>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
-      else phase_a<true, false, 2, false>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
-    }
+    // P carries both groups' staging of interval 0
+    if (nv > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
+    else phase_a<true, false, 2, true>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
     max_all(st, sa, 0, tpos);
     if (!grp) __syncthreads();
     // two subtiles per iteration so that the score buffers keep their roles (S(i) in sa
