@@ -75,6 +75,18 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def history_kernel_name(w) -> str:
+    """The history-attention kernel the library launches for this workload (the rule in
+    launch_attn_history; the committed kernel statistics under profiles/ name the kernel
+    that ran)."""
+    if w.block <= 128:
+        return "attn_history_resident_kernel (block resident in LDS, gathered query rows)"
+    if w.block % 64 == 0 and 256 <= w.block <= 4096:
+        return ("attn_history_chain_kernel (one persistent workgroup per CU, tiles from a "
+                "queue, gathered query tiles)")
+    return "attn_history_kernel (one workgroup per tile of gathered query rows)"
+
+
 def read_counters(path: str, workload: str):
     """{'traffic': HBM bytes per dispatch, 'mfma_busy': fraction of SIMD cycles} from a
     committed rocprofv3 counter summary, or None when there is none, it was taken on
@@ -454,7 +466,7 @@ def main(argv=None):
     cur_ctr = read_counters(CURRENT_COUNTERS_FILE, w.name) if one_launch else None
     roofline = {
         "bound": "mfma",
-        "kernel": "attn_history_kernel (history attention, gathered query tiles)",
+        "kernel": history_kernel_name(w),
         "achieved": hist_tflops,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",

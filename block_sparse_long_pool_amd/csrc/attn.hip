@@ -221,21 +221,31 @@ struct Walker {
   TileRegs<D> kst, vst, pre;   // staging registers (pre: K(1) in the prologue only)
   // one buffer descriptor each for the K and V rows of [key_begin, key_end) (not CHAIN)
   __amdgpu_buffer_rsrc_t kdesc, vdesc;
-  // CHAIN: the workgroup's tiles (tile s is tiles[blockIdx.x + s * gridDim.x]), their
-  // count, and what locates a tile's block (key_end - key_begin keys, a multiple of KN,
-  // so no subtile is masked); the walk's position (subtile im of tile it); the two
-  // staging streams' next subtile (local index, tile, the tile's first-key offset)
+  // CHAIN: the tile list; the workgroup's tiles, taken from a queue: tq[s % 4] holds
+  // the index of its tile s for the tiles in use (s = it .. it + 2), and ntw is their
+  // count once known (before, the list's tile count, a bound: the launcher keeps
+  // nsub * ntiles below 2^30, so len() cannot overflow); what locates a tile's block (key_end -
+  // key_begin keys, a multiple of KN, so no subtile is masked); the walk's position
+  // (subtile im of tile it); the two staging streams' next subtile (local index,
+  // tile, the tile's first-key offset)
   const int4* tiles;
-  int ntw, nb, ng, g0, hkv;
+  __attribute__((address_space(3))) int* tq;
+  int* queue;
+  int qpend;
+  int ntiles, ntw, nb, ng, g0, hkv;
   SeqMap sq;
   int im, it;
   int kt_l, kt_t, vt_l, vt_t;
   size_t kt_off, vt_off;
   __device__ __forceinline__ int len() const { return CHAIN ? nsub * ntw : nsub; }
+  // index in the tile list of the workgroup's tile s (the last tile past the end)
+  __device__ __forceinline__ int tile_of(int s) const {
+    return __builtin_amdgcn_readfirstlane(tq[min(s, ntw - 1) & 3]);
+  }
   // element offset of the first key of the block of the workgroup's tile s (the last
   // tile past the end)
   __device__ __forceinline__ size_t tile_keys(int s) const {
-    const int list = tiles[blockIdx.x + min(s, ntw - 1) * gridDim.x].x;
+    const int list = tiles[tile_of(s)].x;
     const int j = list % nb, gi = (list / nb) % ng, b = list / (nb * ng);
     return (((size_t)sq.tok0(b) + (size_t)j * (key_end - key_begin)) * hkv + g0 + gi) * D;
   }
@@ -517,6 +527,15 @@ struct Walker {
     __builtin_amdgcn_s_setprio(0);
     if (grp) __syncthreads();
     if constexpr (CHAIN && KIND == 0) {
+      // the queue, two tiles ahead: thread 0 takes tile it + 2 at subtile 0 and
+      // publishes it at subtile 1; every wave reads it at subtile 2, after a barrier
+      // that follows the write for both groups (tiles have at least four subtiles)
+      if (threadIdx.x == 0) {
+        if (im == 0) qpend = atomicAdd(queue, 1);
+        else if (im == 1) tq[(it + 2) & 3] = (int)gridDim.x + qpend;
+      }
+      const int t2 = __builtin_amdgcn_readfirstlane(tq[(it + 2) & 3]);
+      ntw = (im == 2 && t2 >= ntiles) ? min(ntw, it + 2) : ntw;
       if (im == nsub - 2) next_q(it + 1);
     }
     auto post = [&] {
@@ -556,7 +575,7 @@ struct Walker {
     vl = (uint32_t)((4 * hf + ((lane & 15) >> 2)) * L::VS +
                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
     if constexpr (CHAIN) {
-      // tile 0's first subtiles (a tile has at least three); the streams then go on
+      // tile 0's first subtiles (a tile has at least four); the streams then go on
       // from K(3) and V(2)
       im = 0;
       it = 0;
@@ -580,10 +599,11 @@ struct Walker {
     }
   }
 
+  // CHAIN: the walk's length (len()) becomes known from the queue while it runs, at
+  // least a tile before its end.
   template <typename NextQ, typename Bound>
   __device__ __forceinline__ void run(WaveState<D, QT>& st, const int (&tpos)[QT],
                                       NextQ&& next_q, Bound&& bound) {
-    const int nv = len();
     // prologue: K(0), K(1) and V(0) into LDS, then the registers that interval 0
     // stages (K(2), V(1))
 #pragma unroll
@@ -606,23 +626,23 @@ struct Walker {
 #pragma unroll
     for (int j = 0; j < PF; ++j) ops[j] = kread(kbuf(0), j);
     // P carries both groups' staging of interval 0
-    if (nv > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
+    if (len() > 1) phase_a<true, false, 1, true>(st, sa, sa, pb, ops, kbuf(0), kbuf(1), 0);
     else phase_a<true, false, 2, true>(st, sa, sa, pb, ops, kbuf(0), vbuf(0), 0);
     max_all(st, sa, 0, tpos);
     if (!grp) __syncthreads();
     // two subtiles per iteration so that the score buffers keep their roles (S(i) in sa
     // for even i); the last ones move S(i+1) into sa instead
     int i = 0;
-    for (; i + 3 < nv; i += 2) {
+    for (; i + 3 < len(); i += 2) {
       iter<0>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
       iter<0>(st, sb, sa, pb, ops, i + 1, tpos, next_q, bound);
     }
-    if (i + 3 == nv) {
+    if (i + 3 == len()) {
       iter<0>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
       copy_scores(sa, sb);
       ++i;
     }
-    if (i + 2 == nv) {
+    if (i + 2 == len()) {
       iter<1>(st, sa, sb, pb, ops, i, tpos, next_q, bound);
       copy_scores(sa, sb);
       ++i;
@@ -841,7 +861,8 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_kern
 
 // ------------------------------------------------------ history, persistent (a4)
 // The same attention as attn_history_kernel, but one workgroup per CU walks all of its
-// tiles (tiles[blockIdx.x + s * gridDim.x], s = 0, 1, ...) as one continuous walk: the
+// tiles (its first, tile blockIdx.x, then those it takes from the tile queue) as one
+// continuous walk: the
 // staging runs into the next tile's block while the current tile finishes, the next
 // tile's query rows load during the last PV phase of the current one, and its first
 // QK^T shares a phase with the current tile's last exponentials.  So a tile pays no
@@ -852,23 +873,37 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_chai
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, SeqMap sq, int hq, int hkv, int block, int topk,
     float sl, int g0, int ng, int nb, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
+    int32_t* __restrict__ tile_count, const uint32_t* __restrict__ entries,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, size_t ls) {
   __shared__ __attribute__((aligned(16))) char lds[Lds<D>::TOTAL];
+  __shared__ int tq[4];
   const int ntiles = *tile_count;
   if ((int)blockIdx.x >= ntiles) return;
-  const int ntw = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // Tiles 0 .. gridDim.x - 1 go to the workgroups in order, the rest through the queue
+  // counter after the tile count (zero at launch): a workgroup that finishes its tiles
+  // early takes more, so the CUs finish together however their speeds differ.
+  int32_t* queue = tile_count + 1;
+  if (threadIdx.x == 0) {
+    tq[0] = blockIdx.x;
+    tq[1] = (int)gridDim.x + atomicAdd(queue, 1);
+  }
+  __syncthreads();
   const int G = hq / hkv, ngq = ng * G;
   const int wave = threadIdx.x >> 6, n = threadIdx.x & 31;
   const int sb = entry_slot_bits(topk);
+  Walker<D, 1, true> w;
+  w.tq = (__attribute__((address_space(3))) int*)tq;
+  w.ntiles = ntiles;
+  w.ntw = __builtin_amdgcn_readfirstlane(tq[1]) < ntiles ? ntiles : 1;
+  w.queue = queue;
   // this lane's index entry in the workgroup's tile s (all ones: no row)
   auto entry_of = [&](int s) -> uint32_t {
-    const int4 tl = tiles[blockIdx.x + s * gridDim.x];
+    const int4 tl = tiles[w.tile_of(s)];
     const int e = tl.y + wave * 32 + n;
     return e < tl.z ? entries[e] : 0xffffffffu;
   };
   auto tile_bg = [&](int s, int& b, int& gi) {
-    const int list = tiles[blockIdx.x + s * gridDim.x].x;
+    const int list = tiles[w.tile_of(s)].x;
     gi = (list / nb) % ng;
     b = list / (nb * ng);
   };
@@ -892,7 +927,6 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_chai
     store_partial(st, 0, valid, part_o + (row * (topk - 1) + slot) * D,
                   part_lse + (size_t)slot * ls + row);
   };
-  Walker<D, 1, true> w;
   w.lds = (lds_char*)lds;
   w.kbase = k;
   w.vbase = v;
@@ -903,7 +937,6 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_chai
   w.sl = sl;
   w.grp = __builtin_amdgcn_readfirstlane(wave) / (kAttnWaves / 2);
   w.tiles = tiles;
-  w.ntw = ntw;
   w.nb = nb;
   w.ng = ng;
   w.g0 = g0;
@@ -911,7 +944,7 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_chai
   w.sq = sq;
   w.begin();
   uint32_t ent_cur = entry_of(0);
-  uint32_t ent_nx = ntw > 1 ? entry_of(1) : 0xffffffffu;
+  uint32_t ent_nx = w.ntw > 1 ? entry_of(1) : 0xffffffffu;
   load_tile_q(0, ent_cur);
   state_init(st);
   w.run(st, tpos, [&](int s) { load_tile_q(s, ent_nx); },
@@ -919,9 +952,11 @@ __global__ __launch_bounds__(kAttnThreads, MOBA_ATTN_WPE) void attn_history_chai
           store_tile(s, ent_cur);
           state_init(st);
           ent_cur = ent_nx;
-          ent_nx = s + 2 < ntw ? entry_of(s + 2) : 0xffffffffu;
+          ent_nx = s + 2 < w.ntw ? entry_of(s + 2) : 0xffffffffu;
         });
-  store_tile(ntw - 1, ent_cur);
+  store_tile(w.ntw - 1, ent_cur);
+  // the last tile's queue request may still be in flight (its answer is not needed)
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ------------------------------------------------- history, blocks of <= 128 keys (a4)
@@ -1234,7 +1269,7 @@ static size_t part_lse_slot_stride(const Shape& s, int ng) {
 
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
-                               const int4* tiles, const int32_t* tile_count,
+                               const int4* tiles, int32_t* tile_count,
                                int max_tiles, const uint32_t* entries, uint16_t* part_o,
                                float* part_lse, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
@@ -1259,12 +1294,20 @@ hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t
 #undef MOBA_RES
     return hipGetLastError();
   }
-  // Blocks of up to 1024 keys (walks of up to 16 subtiles, where a tile's fixed cost is
-  // a large share) run the persistent chained kernel: 32K tokens with B = 512, 0.78 ->
-  // 0.72 ms.  Longer blocks keep one tile per workgroup: with 64-subtile walks the fixed
-  // cost is small, and the hardware's dynamic dispatch balances the CUs better than the
-  // chained kernel's fixed tile assignment (128K, B = 4096: 70.9 against 72.6 ms).
-  if (s.block % KN == 0 && s.block <= 16 * KN) {
+  // Blocks of 256 to 4096 keys run the persistent chained kernel, its workgroups taking
+  // tiles from a queue.  Where a tile's fixed cost is a large share (32K tokens, B = 512:
+  // walks of 8 subtiles) history takes 0.78 -> 0.74 ms; at 128K with B = 4096 it is
+  // 0.3% faster than one tile per workgroup (67.5 -> 67.3 ms), bit for bit the same.
+  // With a fixed round-robin assignment instead of the queue it was 2.4% slower there
+  // (the CUs do not all run at the same speed).  The queue needs tiles of at least four
+  // subtiles: the K staging stream, four subtiles ahead of the walk, enters tile it + 2
+  // at subtile 2 * nsub - 5 of tile it, which must not come before subtile 2, where
+  // every wave has read that tile's index.
+#ifndef MOBA_CHAIN_MAXSUB
+#define MOBA_CHAIN_MAXSUB 64
+#endif
+  if (s.block % KN == 0 && s.block >= 4 * KN && s.block <= MOBA_CHAIN_MAXSUB * KN &&
+      (long long)max_tiles * (s.block / KN) < (1ll << 30)) {
     // one persistent workgroup per CU (the kernel's LDS allows one)
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||

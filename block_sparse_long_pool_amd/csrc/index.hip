@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void index_scan_lists_kernel(
   if (threadIdx.x == 0) {
     list_offsets[nlists] = ca;
     tile_offsets[nlists] = cb;  // number of tiles
+    tile_offsets[nlists + 1] = 0;  // the history kernel's tile queue starts empty
   }
 }
 
@@ -244,7 +245,10 @@ __global__ __launch_bounds__(kThreads) void tiles_scan_kernel(
     if (threadIdx.x == kThreads - 1) cb = b0 + ib;
     __syncthreads();
   }
-  if (threadIdx.x == 0) tile_offsets[nlists] = cb;
+  if (threadIdx.x == 0) {
+    tile_offsets[nlists] = cb;
+    tile_offsets[nlists + 1] = 0;  // the history kernel's tile queue starts empty
+  }
 }
 
 // dst[i] = src[(a * i + c) mod n] for the n tiles: a is the first number coprime to n

@@ -119,7 +119,7 @@ Layout make_layout(const Shape& s, int ng, int tile_rows = 0) {
   L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
   L.list_count = take(nlists * sizeof(int32_t));
   L.list_offsets = take((nlists + 1) * sizeof(int32_t));
-  L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
+  L.tile_offsets = take((nlists + 2) * sizeof(int32_t));   // + count + queue counter
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
   const size_t prow = group_part_rows(s, ng);   // history slots only
@@ -162,7 +162,7 @@ BwdLayout make_bwd_layout(const Shape& s, int ng) {
   L.chunk_counts = take((size_t)s.b * ng * nchunks * nb * sizeof(int32_t));
   L.list_count = take(nlists * sizeof(int32_t));
   L.list_offsets = take((nlists + 1) * sizeof(int32_t));
-  L.tile_offsets = take((nlists + 1) * sizeof(int32_t));
+  L.tile_offsets = take((nlists + 2) * sizeof(int32_t));   // + count + queue counter
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.entries = take((size_t)L.n_entries * sizeof(uint32_t));
   L.dense_rows = take((size_t)L.n_entries * 2 * s.d * sizeof(uint16_t));
@@ -651,7 +651,7 @@ HistoryTiles history_tiles(const Shape& s, int kv_count) {
   h.tile_m = moba::history_tile_rows(s, n_entries);
   h.nlists = (long long)s.b * kv_count * s.nb();
   h.max_tiles = (n_entries + h.tile_m - 1) / h.tile_m + h.nlists;
-  h.offsets_bytes = align_up((size_t)(h.nlists + 1) * sizeof(int32_t));
+  h.offsets_bytes = align_up((size_t)(h.nlists + 2) * sizeof(int32_t));
   h.tiles_bytes = align_up((size_t)h.max_tiles * sizeof(int4));
   return h;
 }
@@ -736,7 +736,7 @@ int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
   const size_t cc = align_up((size_t)s.b * kv_count * moba::index_chunks(s) * s.nb() *
                              sizeof(int32_t));
   const size_t lc = align_up(nlists * sizeof(int32_t));
-  const size_t to = align_up((nlists + 1) * sizeof(int32_t));
+  const size_t to = align_up((nlists + 2) * sizeof(int32_t));
   if (cc + lc + to > workspace_bytes) return MOBA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   return hip_status(moba::launch_index(

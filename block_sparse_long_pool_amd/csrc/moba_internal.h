@@ -120,7 +120,7 @@ hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
 // 0 .. t / block ascending, then -1 up to topk
 hipError_t launch_idx_all_blocks(const Shape& s, int32_t* idx, hipStream_t st);
 int gate_max_history();                // the most history slots the gate ranks
-// (a3) inverted index over kv-heads [g0, g0 + ng)
+// (a3) inverted index over kv-heads [g0, g0 + ng); tile_offsets as for launch_tiles
 int index_chunks(const Shape& s);
 hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int tile_m,
                         int32_t* chunk_counts, int32_t* list_count,
@@ -128,15 +128,18 @@ hipError_t launch_index(const Shape& s, const int32_t* idx, int g0, int ng, int 
                         int4* tiles, uint32_t* entries, long long cap,
                         hipStream_t st);
 // the tile list of lists given by their offsets (as moba_build_index writes them):
-// tile_offsets [nlists + 1] (the tile count last) and tiles; with perm_seed != 0 the
+// tile_offsets [nlists + 2] (then the tile count, then a zeroed counter that the
+// persistent history kernel takes tiles from) and tiles; with perm_seed != 0 the
 // tiles are written in a seeded permuted order (through tiles_tmp, max_tiles long)
 hipError_t launch_tiles(const int32_t* list_offsets, int nlists, int tile_m, int max_tiles,
                         int32_t* tile_offsets, int4* tiles, uint32_t perm_seed,
                         int4* tiles_tmp, hipStream_t st);
 // (a4) history attention partials, (a5) current block fused with the merge
+// tile_count: the tile count, then the zeroed queue counter that launch_index and
+// launch_tiles write after it (the persistent kernel takes tiles from it)
 hipError_t launch_attn_history(const Shape& s, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, float scale, int g0, int ng,
-                               const int4* tiles, const int32_t* tile_count,
+                               const int4* tiles, int32_t* tile_count,
                                int max_tiles, const uint32_t* entries, uint16_t* part_o,
                                float* part_lse, hipStream_t st);
 // the current-block kernel also merges the history partials and writes out and lse

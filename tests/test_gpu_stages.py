@@ -3,9 +3,9 @@
 * pool -> gate -> build_index -> history_partials -> current_merge over kv-head ranges
   reproduces moba_forward bit for bit (out, lse, idx) when topk * block < T (with
   every block selected the forward runs the dense kernel), for every history kernel the
-  library dispatches to: blocks of at most 128 keys (resident block), 256 and 1024
-  keys (persistent chained walk), 2048 keys (one tile per workgroup), a partial last
-  block, and two kv-head ranges run separately.
+  library dispatches to: blocks of at most 128 keys (resident block), 256 to 4096 keys
+  (persistent chained walk fed by the tile queue), 192 keys (one tile per workgroup),
+  a partial last block, and two kv-head ranges run separately.
 * history_partials with the tiles launched in seeded permuted orders writes the same
   parts, bit for bit, as in list order: each part belongs to one tile, so the result
   may not depend on which tile runs first (a randomised launch-order check for races
@@ -67,7 +67,8 @@ CHAIN_SHAPES = [
     (1, 4, 1, 64, 2048, 64, 5, [(0, 1)]),            # resident, d = 64
     (1, 8, 2, 128, 4096, 256, 5, [(0, 2)]),          # chained persistent walk
     (2, 8, 4, 128, 4096, 1024, 3, [(0, 4)]),         # chained, 16 subtiles per tile
-    (1, 8, 2, 128, 8192, 2048, 3, [(0, 2)]),         # one tile per workgroup
+    (1, 8, 2, 128, 8192, 2048, 3, [(0, 2)]),         # chained, 32 subtiles per tile
+    (1, 8, 2, 128, 4032, 192, 6, [(0, 2)]),          # one tile per workgroup (3 subtiles)
     (1, 8, 4, 128, 4000, 256, 5, [(0, 4)]),          # partial last block
     (1, 16, 4, 128, 4096, 512, 4, [(0, 1), (1, 3)]),  # kv-head ranges run separately
     (1, 4, 2, 128, 1024, 256, 1, [(0, 2)]),          # no history slots
@@ -91,7 +92,8 @@ def test_stage_chain_is_the_forward(moba, b, hq, hkv, d, T, B, k, ranges):
 ORDER_SHAPES = [
     (1, 8, 2, 128, 4096, 128, 6),      # resident block
     (1, 8, 2, 128, 4096, 256, 5),      # chained persistent walk
-    (1, 8, 2, 128, 8192, 2048, 3),     # one tile per workgroup
+    (1, 8, 2, 128, 8192, 2048, 3),     # chained, 32 subtiles per tile
+    (1, 8, 2, 128, 4032, 192, 6),      # one tile per workgroup (3 subtiles)
     (2, 4, 2, 64, 3000, 192, 4),       # d = 64, partial last block, batch 2
 ]
 
@@ -118,7 +120,8 @@ def test_history_parts_do_not_depend_on_tile_order(moba, b, hq, hkv, d, T, B, k)
 @pytest.mark.parametrize("b,hq,hkv,d,T,B,k", [
     (1, 4, 2, 128, 2048, 256, 4),      # chained walk
     (1, 4, 1, 64, 1024, 128, 5),       # resident block, d = 64
-    (1, 2, 1, 128, 4096, 2048, 2),     # one tile per workgroup
+    (1, 2, 1, 128, 4096, 2048, 2),     # chained walk, 32 subtiles per tile
+    (1, 2, 1, 128, 1536, 192, 3),      # one tile per workgroup (3 subtiles)
 ])
 def test_history_parts_match_the_oracle(moba, b, hq, hkv, d, T, B, k):
     w = small_workload("parts", b, hq, hkv, d, T, B, k, "offset", 33)
