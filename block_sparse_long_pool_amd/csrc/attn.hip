@@ -708,6 +708,115 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
   if (hf == 0) *pl = (st.m[qt] + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
+// The parts are read CH at a time so that their loads are in flight together.
+#ifndef MOBA_MERGE_CH
+#define MOBA_MERGE_CH 4
+#endif
+constexpr int kMergeCH = MOBA_MERGE_CH;
+
+// the lane's half of part rows s0 .. s0 + CH - 1 (see store_partial); indices past nh
+// are clamped to the row's last part (their weight is 0)
+template <int D, int CH>
+struct PartRows {
+  u32x4_t x[CH][D / 16];
+};
+template <int D, int CH>
+__device__ __forceinline__ void load_parts(PartRows<D, CH>& p, const uint16_t* __restrict__ po,
+                                           int s0, int nh, int hf) {
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const uint16_t* ps = po + (size_t)min(s0 + u, nh - 1) * D + hf * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) p.x[u][c] = *reinterpret_cast<const u32x4_t*>(ps + c * 8);
+  }
+}
+// acc += sum_u w[u] * part row u, parts in order
+template <int D, int CH>
+__device__ __forceinline__ void add_parts(f32x4_t (&acc)[D / 32][4], const PartRows<D, CH>& p,
+                                          const float (&w)[CH]) {
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const u32x4_t& xc = p.x[u][dt * 2 + ii / 2];
+        const u32x2_t y = {xc[(ii & 1) * 2], xc[(ii & 1) * 2 + 1]};
+        const float xf[4] = {__uint_as_float(y[0] << 16), __uint_as_float(y[0] & 0xffff0000u),
+                             __uint_as_float(y[1] << 16), __uint_as_float(y[1] & 0xffff0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w[u], xf[r], acc[dt][ii][r]);
+      }
+}
+template <int D>
+__device__ __forceinline__ void store_merged(const f32x4_t (&acc)[D / 32][4], float L, int hf,
+                                             uint16_t* __restrict__ orow,
+                                             float* __restrict__ lrow) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      u32x2_t pk;
+      pk[0] = f32_to_bf16_rne(acc[dt][ii][0]) | (f32_to_bf16_rne(acc[dt][ii][1]) << 16);
+      pk[1] = f32_to_bf16_rne(acc[dt][ii][2]) | (f32_to_bf16_rne(acc[dt][ii][3]) << 16);
+      *reinterpret_cast<u32x2_t*>(orow + dt * 32 + ii * 8 + hf * 4) = pk;
+    }
+  if (hf == 0) *lrow = L;
+}
+
+// Merge of a row with 1 <= nh <= NL parts: the NL lse values (clamped indices) and the
+// first CHF part rows are loaded in one round, the lse then stay in registers, so the
+// merge waits on ceil(nh / CHF) rounds of loads instead of re-reading the lse for the
+// max, the sum and the weights.  Same arithmetic, in the same order, as the general
+// path.  Two part rows per round: at 128K (11 parts) the current-block kernel takes
+// 6.30 -> 6.12 ms, at 64K with 128-key blocks (15 parts) 2.30 -> 2.17 ms, bit for bit
+// the same; rounds of three or four part rows spill (the walk's registers are not all
+// free at the end).
+#ifndef MOBA_MERGE_CHF
+#define MOBA_MERGE_CHF 2
+#endif
+template <int D, int QT, int NL>
+__device__ __forceinline__ void merge_store_regs(const WaveState<D, QT>& st, int qt, int nh,
+                                                 float lc, float lse_c,
+                                                 const uint16_t* __restrict__ po,
+                                                 const float* __restrict__ pl, size_t ls,
+                                                 int hf, uint16_t* __restrict__ orow,
+                                                 float* __restrict__ lrow) {
+  constexpr int CH = MOBA_MERGE_CHF;
+  float lv[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) lv[u] = pl[(size_t)min(u, nh - 1) * ls];
+  PartRows<D, CH> p;
+  load_parts<D, CH>(p, po, 0, nh, hf);
+  float mx = lse_c;
+#pragma unroll
+  for (int u = 0; u < NL; ++u) mx = fmaxf(mx, lv[u]);
+  float den = expf(lse_c - mx);
+#pragma unroll
+  for (int u = 0; u < NL; ++u)
+    if (u < nh) den += expf(lv[u] - mx);
+  const float L = mx + logf(den);
+  const float wc = expf(lse_c - L) / lc;
+  f32x4_t acc[D / 32][4];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dt][ii][r] = st.o[qt][dt][ii * 4 + r] * wc;
+#pragma unroll
+  for (int s0 = 0; s0 < NL; s0 += CH) {
+    if (s0 >= nh) break;
+    if (s0 > 0) load_parts<D, CH>(p, po, s0, nh, hf);
+    float w[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+      w[u] = (s0 + u < NL && s0 + u < nh) ? expf(lv[s0 + u < NL ? s0 + u : 0] - L) : 0.f;
+    add_parts<D, CH>(acc, p, w);
+  }
+  store_merged<D>(acc, L, hf, orow, lrow);
+}
+
 // Log-sum-exp merge of a row's current-block result (in registers) with its nh history
 // partials, written as the final output: L = ln(e^lse_c + sum_s e^lse_s), out =
 // e^(lse_c - L) o_c + sum_s e^(lse_s - L) o_s (bf16, round to nearest even), lse = L.
@@ -723,12 +832,15 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
   if (!valid) return;
   const float ln2 = 0.69314718055994530942f;
   const float lse_c = (st.m[qt] + __log2f(lc)) * ln2;
-  // The parts are read CH at a time so that their loads are in flight together;
-  // indices past nh are clamped to the row's last part and given weight 0.
-#ifndef MOBA_MERGE_CH
-#define MOBA_MERGE_CH 4
-#endif
-  constexpr int CH = MOBA_MERGE_CH;
+  // nh is the same for every row of a workgroup (min(block, k - 1))
+  if (nh >= 1 && nh <= 4)
+    return merge_store_regs<D, QT, 4>(st, qt, nh, lc, lse_c, po, pl, ls, hf, orow, lrow);
+  if (nh >= 1 && nh <= 8)
+    return merge_store_regs<D, QT, 8>(st, qt, nh, lc, lse_c, po, pl, ls, hf, orow, lrow);
+  if (nh >= 1 && nh <= 16)
+    return merge_store_regs<D, QT, 16>(st, qt, nh, lc, lse_c, po, pl, ls, hf, orow, lrow);
+  // general path (no parts, or more than 16): the lse are read again for each use
+  constexpr int CH = kMergeCH;
   float mx = lse_c;
   for (int s0 = 0; s0 < nh; s0 += CH) {
     float v[CH];
@@ -756,40 +868,15 @@ __device__ __forceinline__ void merge_store(const WaveState<D, QT>& st, int qt, 
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[dt][ii][r] = st.o[qt][dt][ii * 4 + r] * wc;
   for (int s0 = 0; s0 < nh; s0 += CH) {
-    u32x4_t x[CH][D / 16];     // the lane's half of each part row (see store_partial)
+    PartRows<D, CH> p;
+    load_parts<D, CH>(p, po, s0, nh, hf);
     float w[CH];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int sc = min(s0 + u, nh - 1);
-      const uint16_t* ps = po + (size_t)sc * D + hf * (D / 2);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) x[u][c] = *reinterpret_cast<const u32x4_t*>(ps + c * 8);
-      w[u] = s0 + u < nh ? expf(pl[(size_t)sc * ls] - L) : 0.f;
-    }
-#pragma unroll
     for (int u = 0; u < CH; ++u)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const u32x4_t& xc = x[u][dt * 2 + ii / 2];
-          const u32x2_t y = {xc[(ii & 1) * 2], xc[(ii & 1) * 2 + 1]};
-          const float xf[4] = {__uint_as_float(y[0] << 16), __uint_as_float(y[0] & 0xffff0000u),
-                               __uint_as_float(y[1] << 16), __uint_as_float(y[1] & 0xffff0000u)};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[dt][ii][r] = fmaf(w[u], xf[r], acc[dt][ii][r]);
-        }
+      w[u] = s0 + u < nh ? expf(pl[(size_t)min(s0 + u, nh - 1) * ls] - L) : 0.f;
+    add_parts<D, CH>(acc, p, w);
   }
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      u32x2_t pk;
-      pk[0] = f32_to_bf16_rne(acc[dt][ii][0]) | (f32_to_bf16_rne(acc[dt][ii][1]) << 16);
-      pk[1] = f32_to_bf16_rne(acc[dt][ii][2]) | (f32_to_bf16_rne(acc[dt][ii][3]) << 16);
-      *reinterpret_cast<u32x2_t*>(orow + dt * 32 + ii * 8 + hf * 4) = pk;
-    }
-  if (hf == 0) *lrow = L;
+  store_merged<D>(acc, L, hf, orow, lrow);
 }
 
 template <int D, int QT>
