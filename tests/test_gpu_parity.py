@@ -273,6 +273,9 @@ SMALL = [
     # G = 3 (does not divide the eight waves: heads in rounds) and G = 16 (two rounds)
     ("g3", small_workload("g3", 1, 6, 2, 128, 2048, 128, 4, "offset", 16)),
     ("g16_d64", small_workload("g16_d64", 1, 16, 1, 64, 1024, 64, 5, "offset", 17)),
+    # top-20 over 24 blocks of 256 keys (the queued chained history kernel): rows with
+    # 1-4, 5-8, 9-16 and 19 history parts, every path of the current-block merge
+    ("k20_chain", small_workload("k20_chain", 1, 4, 2, 128, 6144, 256, 20, "offset", 18)),
 ]
 
 
