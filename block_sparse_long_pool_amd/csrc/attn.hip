@@ -221,13 +221,16 @@ struct Walker {
   TileRegs<D> kst, vst, pre;   // staging registers (pre: K(1) in the prologue only)
   // one buffer descriptor each for the K and V rows of [key_begin, key_end) (not CHAIN)
   __amdgpu_buffer_rsrc_t kdesc, vdesc;
-  // CHAIN: the tile list; the workgroup's tiles, taken from a queue: tq[s % 4] holds
-  // the index of its tile s for the tiles in use (s = it .. it + 2), and ntw is their
-  // count once known (before, the list's tile count, a bound: the launcher keeps
-  // nsub * ntiles below 2^30, so len() cannot overflow); what locates a tile's block (key_end -
-  // key_begin keys, a multiple of KN, so no subtile is masked); the walk's position
-  // (subtile im of tile it); the two staging streams' next subtile (local index,
-  // tile, the tile's first-key offset)
+  // CHAIN:
+  //  * the tile list, and the workgroup's tiles taken from a queue: tq[s % 4] holds the
+  //    index of its tile s for the tiles in use (s = it .. it + 2); queue is the
+  //    counter, qpend thread 0's request in flight; ntiles is the list's tile count;
+  //  * ntw, the workgroup's tile count once known, and ntiles before (a bound; the
+  //    launcher keeps nsub * ntiles below 2^30, so len() cannot overflow);
+  //  * what locates a tile's block (key_end - key_begin keys, a multiple of KN, so no
+  //    subtile is masked);
+  //  * the walk's position (subtile im of tile it), and the two staging streams' next
+  //    subtile (local index, tile, the tile's first-key offset).
   const int4* tiles;
   __attribute__((address_space(3))) int* tq;
   int* queue;
@@ -534,6 +537,8 @@ struct Walker {
         if (im == 0) qpend = atomicAdd(queue, 1);
         else if (im == 1) tq[(it + 2) & 3] = (int)gridDim.x + qpend;
       }
+      // (a select, not a branch: as a branch next to the divergent one above, this
+      // compiler fails with an illegal VGPR to SGPR copy)
       const int t2 = __builtin_amdgcn_readfirstlane(tq[(it + 2) & 3]);
       ntw = (im == 2 && t2 >= ntiles) ? min(ntw, it + 2) : ntw;
       if (im == nsub - 2) next_q(it + 1);
