@@ -1,7 +1,8 @@
 """Randomly drawn shapes (seeded, the same every run) through the forward, the
 backward, the packed forward and the decode, every row or element against the
 oracle.  They complement the hand-picked cases with combinations nobody chose: odd
-lengths, block sizes from 16 to 256, G = 1 to 8, top-k from 1 to 13, d = 64 and 128.
+lengths, block sizes from 16 to 256 (and 256 to 2048 for the chained history kernel),
+G = 1 to 8, top-k from 1 to 13, d = 64 and 128.
 Bars are those of tests/parity_util.py (forward), tests/test_gpu_backward.py
 (backward) and tests/test_gpu_decode.py (decode).
 """
@@ -58,6 +59,42 @@ def test_forward_random_shape(moba, seed):
     b, T, hq, hkv, d, B, k = draw(seed)
     say(f"[random fwd] seed={seed}: b={b} T={T} hq={hq} hkv={hkv} d={d} B={B} k={k}")
     w = small_workload("rnd", b, hq, hkv, d, T, B, k, "offset", seed=seed)
+    inp = make_inputs(w)
+    out, lse, idx = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), B, k)
+    torch.cuda.synchronize()
+    go, gl, gi = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    Q, K, V = (bf16_to_f64(inp[x]) for x in "qkv")
+    rows = [(bi, t, h) for bi in range(b) for t in range(T) for h in range(hq)]
+    st = compare_rows(Q, K, V, B, k, w.sm_scale, rows,
+                      np.stack([go[bi, t, h] for bi, t, h in rows]),
+                      np.array([gl[bi, h, t] for bi, t, h in rows]),
+                      np.stack([gi[bi, h, t] for bi, t, h in rows]))
+    say(f"       {st}")
+
+
+def draw_chained(seed, max_rows=24000):
+    """(b, T, hq, hkv, d, B, k) with blocks of 256 to 2048 keys (multiples of 64: the
+    persistent chained history kernel fed by its tile queue), more than k + 1 blocks
+    (so the rows of the later blocks choose among their history blocks) and a ragged
+    T; the launches range from fewer tiles than workgroups to several per workgroup."""
+    r = np.random.default_rng(seed)
+    d = int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4]))
+    hkv = int(r.choice([1, 2]))
+    hq = G * hkv
+    k = int(r.integers(2, 7))
+    bmax = max(4, min(32, max_rows // (hq * (k + 2) * 64)))
+    B = 64 * int(r.integers(4, bmax + 1))
+    lo = (k + 1) * B + 1
+    T = int(r.integers(lo, max(lo + 1, min(max_rows // hq, (k + 5) * B))))
+    return 1, T, hq, hkv, d, B, k
+
+
+@pytest.mark.parametrize("seed", range(300, 306))
+def test_forward_random_chained_history(moba, seed):
+    b, T, hq, hkv, d, B, k = draw_chained(seed)
+    say(f"[random chained fwd] seed={seed}: b={b} T={T} hq={hq} hkv={hkv} d={d} B={B} k={k}")
+    w = small_workload("rndc", b, hq, hkv, d, T, B, k, "offset", seed=seed)
     inp = make_inputs(w)
     out, lse, idx = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), B, k)
     torch.cuda.synchronize()
