@@ -25,7 +25,6 @@
 // lane l holds column l%32 and rows (i/4)*8 + (l/32)*4 + i%4, and a transposed operand
 // is read from a row-major LDS tile with ds_read_b64_tr_b16 in the order the result
 // registers hold the summation index.
-#include <type_traits>
 
 #include "moba_internal.h"
 
@@ -535,8 +534,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   // 16-byte access touch consecutive bytes
   char* px = lds + 2 * L::BUF + tile * 2048 + lane * 16;
   // One 32-row group.  Register e of a 32x32 result holds row (e/4)*8 + hf*4 + e%4.
-  auto compute = [&](int buf, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
+  // One code path for both buffers and with or without the causal mask (a uniform
+  // branch around the mask alone): copies of it for each case had the compiler keep
+  // the accumulators in different registers in each copy and move them between them.
+  auto compute = [&](int buf, bool masked) {
     const char* base = lds + buf * L::BUF;
     const float* mf = reinterpret_cast<const float*>(base + 2 * (L::QR + L::QT));
     // S = Q K^T (wave P) or dP = dO V^T (wave dS): rows x keys
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
         for (int r = 0; r < 4; ++r)
           p[q4 * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[q4 * 4 + r], sl, -lf[r]));
       }
-      if (MASKED) {
+      if (masked) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int4 lt = *reinterpret_cast<const int4*>(mf + 64 + q4 * 8 + hf * 4);
@@ -613,21 +614,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   fetch_rows(0, rd);             // group 0
   store_rows(rd, 0);
   __syncthreads();
-  using Mask = std::true_type;
-  using NoMask = std::false_type;
   // groups [gm0, gm1) hold the rows that need the causal mask
   const int gm0 = mask_lo / 32, gm1 = (mask_hi + 31) / 32;
-  for (int gidx = 0; gidx < ngroups; gidx += 2) {
+  for (int gidx = 0; gidx < ngroups; ++gidx) {
     fetch_rows((gidx + 1) * 32, rd);     // group gidx + 1
-    if (gidx >= gm0 && gidx < gm1) compute(0, Mask{});
-    else compute(0, NoMask{});
-    store_rows(rd, 1);
-    __syncthreads();
-    if (gidx + 1 >= ngroups) break;
-    fetch_rows((gidx + 2) * 32, rd);     // group gidx + 2
-    if (gidx + 1 >= gm0 && gidx + 1 < gm1) compute(1, Mask{});
-    else compute(1, NoMask{});
-    store_rows(rd, 0);
+    compute(gidx & 1, gidx >= gm0 && gidx < gm1);
+    store_rows(rd, (gidx + 1) & 1);
     __syncthreads();
   }
 
