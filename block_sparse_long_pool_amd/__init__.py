@@ -657,14 +657,14 @@ def build_index(idx, hkv: int, block: int, topk: int, kv_begin: int = 0,
 
 def part_dim_order(head_dim: int) -> list:
     """The head dimension held at each position of a ``history_partials`` part row:
-    position p = hf*d/2 + dt*16 + ii*4 + r holds dimension dt*32 + ii*8 + hf*4 + r."""
-    half = head_dim // 2
+    position p = dt*32 + j*16 + hf*8 + u*4 + r holds dimension dt*32 + (2j+u)*8 + hf*4 + r."""
     order = []
     for p in range(head_dim):
-        hf, rem = divmod(p, half)
-        dt, rem = divmod(rem, 16)
-        ii, r = divmod(rem, 4)
-        order.append(dt * 32 + ii * 8 + hf * 4 + r)
+        dt, rem = divmod(p, 32)
+        j, rem = divmod(rem, 16)
+        hf, rem = divmod(rem, 8)
+        u, r = divmod(rem, 4)
+        order.append(dt * 32 + (2 * j + u) * 8 + hf * 4 + r)
     return order
 
 

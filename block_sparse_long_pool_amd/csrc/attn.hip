@@ -695,9 +695,12 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
   const float ltot = pair_sum(st.l[qt]);
   if (!valid) return;
   const float inv = 1.f / ltot;
-  // lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row; they are stored as
-  // the contiguous half hf of the row (position hf*D/2 + dt*16 + ii*4 + r), so each
-  // lane writes, and the merge reads, whole 16-byte chunks
+  // lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row, in 16-byte chunks
+  // (dt, ii / 2).  Chunk (dt, j) of lane hf is stored at position dt*32 + j*16 + hf*8,
+  // next to the same chunk of the pair's other lane, so each store (and each merge
+  // load) moves 32 contiguous bytes of a row: half the memory requests of storing
+  // each lane's half row apart (at 64K tokens with 128-key blocks, history
+  // 4.85 -> 4.29 ms).
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -708,7 +711,7 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
                          pack_bf16x2(o[a + 2] * inv, o[a + 3] * inv),
                          pack_bf16x2(o[a + 4] * inv, o[a + 5] * inv),
                          pack_bf16x2(o[a + 6] * inv, o[a + 7] * inv)};
-      *reinterpret_cast<u32x4_t*>(po + hf * (D / 2) + dt * 16 + i2 * 8) = w;
+      *reinterpret_cast<u32x4_t*>(po + (dt * 2 + i2) * 16 + hf * 8) = w;
     }
   if (hf == 0) *pl = (st.m[qt] + __log2f(ltot)) * 0.69314718055994530942f;
 }
@@ -719,7 +722,7 @@ __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt
 #endif
 constexpr int kMergeCH = MOBA_MERGE_CH;
 
-// the lane's half of part rows s0 .. s0 + CH - 1 (see store_partial); indices past nh
+// the lane's chunks of part rows s0 .. s0 + CH - 1 (see store_partial); indices past nh
 // are clamped to the row's last part (their weight is 0)
 template <int D, int CH>
 struct PartRows {
@@ -730,9 +733,9 @@ __device__ __forceinline__ void load_parts(PartRows<D, CH>& p, const uint16_t* _
                                            int s0, int nh, int hf) {
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
-    const uint16_t* ps = po + (size_t)min(s0 + u, nh - 1) * D + hf * (D / 2);
+    const uint16_t* ps = po + (size_t)min(s0 + u, nh - 1) * D + hf * 8;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) p.x[u][c] = *reinterpret_cast<const u32x4_t*>(ps + c * 8);
+    for (int c = 0; c < D / 16; ++c) p.x[u][c] = *reinterpret_cast<const u32x4_t*>(ps + c * 16);
   }
 }
 // acc += sum_u w[u] * part row u, parts in order

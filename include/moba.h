@@ -350,9 +350,10 @@ int moba_build_index(const int32_t* idx, int batch, int seqlen, int hq, int hkv,
  *   part_o    bf16 [batch][kv_count * G][T][topk - 1][head_dim]: the part's output
  *             (normalised, rounded to nearest even) at the row's slot of block j, its
  *             head_dim values in the order the kernel's lanes hold them: position
- *             p = hf * head_dim/2 + dt * 16 + ii * 4 + r holds dimension
- *             dt * 32 + ii * 8 + hf * 4 + r (hf < 2, dt < head_dim/32, ii < 4, r < 4),
- *             so that each lane reads and writes one contiguous half of a row;
+ *             p = dt * 32 + j * 16 + hf * 8 + u * 4 + r holds dimension
+ *             dt * 32 + (2 * j + u) * 8 + hf * 4 + r (dt < head_dim/32, j, hf, u < 2,
+ *             r < 4), so that the two lanes that own a row read and write 32
+ *             contiguous bytes of it at a time;
  *   part_lse  fp32 [topk - 1][batch][kv_count * G][T]: ln sum_u exp(scale q.k_u).
  * Heads h = kv_begin * G .. are numbered from 0 within the range.  Slots a row does
  * not have (t / block <= slot) are not written.  Splitting a row's keys into such
