@@ -94,6 +94,8 @@ SMALL = [
     ("g7_b2", 2, 7, 1, 64, 768, 128, 3, "offset", 44),
     ("g12", 1, 12, 1, 128, 512, 64, 5, "offset", 45),
     ("g16_d64", 1, 16, 1, 64, 512, 128, 3, "offset", 46),
+    # top-16 over 125 blocks of 32 keys: the index stages each chunk's entries in LDS
+    ("k16_b32_staged", 1, 2, 1, 64, 4000, 32, 16, "offset", 47),
 ]
 
 

@@ -191,6 +191,9 @@ def cpu_index(idx, hkv, B, topk, kv_begin, kv_count, chunk=256):
     (2, 2048, 4, 1, 64, 9, 0, 1),
     (1, 8192, 32, 8, 512, 3, 3, 4),
     (1, 2048, 4, 4, 16, 33, 1, 2),
+    # at least 8 history slots over many short lists: the entries staged in LDS
+    (1, 8192, 8, 2, 64, 12, 0, 2),
+    (2, 4000, 4, 2, 32, 16, 1, 1),      # and a partial last block
 ])
 def test_inverted_index(moba, b, T, hq, hkv, B, k, kv_begin, kv_count):
     w = small_workload("idx", b, hq, hkv, 64, T, B, k, "iid", seed=B + k)
@@ -276,6 +279,9 @@ SMALL = [
     # top-20 over 24 blocks of 256 keys (the queued chained history kernel): rows with
     # 1-4, 5-8, 9-16 and 19 history parts, every path of the current-block merge
     ("k20_chain", small_workload("k20_chain", 1, 4, 2, 128, 6144, 256, 20, "offset", 18)),
+    # top-16 over 125 blocks of 32 keys, the last one partial: the index stages each
+    # chunk's entries in LDS
+    ("k16_b32_staged", small_workload("k16_b32_staged", 1, 4, 2, 128, 4000, 32, 16, "offset", 19)),
 ]
 
 
