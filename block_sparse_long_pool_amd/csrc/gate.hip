@@ -22,9 +22,9 @@
 // whose low nbits hold (mask - j), so larger key = better, and exactly equal scores
 // rank the lower block first.  Scores closer than ~2^-(23-nbits) relative compare
 // as equal (well inside the 1e-3-relative near-tie band).  Per 32-block tile a lane
-// sorts its keys with bitonic networks and merges them into a running sorted
-// top-KHMAX list (KHMAX = 16, 32 or 64).  No branch depends on the data, so the
-// wavefront never diverges.
+// sorts its keys in two halves of 16 (odd-even merge networks), merges them, and
+// merges the result into a running sorted top-KHMAX list (KHMAX = 16, 32 or 64;
+// bitonic merges).  No branch depends on the data, so the wavefront never diverges.
 #include "moba_internal.h"
 
 namespace moba {
@@ -46,23 +46,48 @@ __device__ __forceinline__ void cas_desc(uint32_t (&a)[N], int i, int k) {
   a[k] = min(x, y);
 }
 
-// full bitonic sort, descending
-template <int N>
-__device__ __forceinline__ void bitonic_sort_desc(uint32_t (&a)[N]) {
-#pragma unroll
-  for (int kk = 2; kk <= N; kk <<= 1) {
-#pragma unroll
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          if ((i & kk) == 0) cas_desc(a, i, ixj);
-          else cas_desc(a, ixj, i);
-        }
-      }
+// Batcher's odd-even merge sort network for 16 keys (63 comparators, against the
+// bitonic network's 80), built at compile time.  Comparator (a, b), a < b, leaves the
+// larger key at a, so the network sorts descending.
+struct SortNet16 {
+  int n;
+  unsigned char a[63], b[63];
+};
+constexpr void oem_merge(SortNet16& net, int lo, int hi, int r) {
+  const int step = r * 2;
+  if (step < hi - lo) {
+    oem_merge(net, lo, hi, step);
+    oem_merge(net, lo + r, hi, step);
+    for (int i = lo + r; i < hi - r; i += step) {
+      net.a[net.n] = (unsigned char)i;
+      net.b[net.n] = (unsigned char)(i + r);
+      ++net.n;
     }
+  } else {
+    net.a[net.n] = (unsigned char)lo;
+    net.b[net.n] = (unsigned char)(lo + r);
+    ++net.n;
   }
+}
+constexpr void oem_sort(SortNet16& net, int lo, int hi) {
+  if (hi - lo >= 1) {
+    const int mid = lo + (hi - lo) / 2;
+    oem_sort(net, lo, mid);
+    oem_sort(net, mid + 1, hi);
+    oem_merge(net, lo, hi, 1);
+  }
+}
+constexpr SortNet16 make_sort16() {
+  SortNet16 net{};
+  oem_sort(net, 0, 15);
+  return net;
+}
+constexpr SortNet16 kSort16 = make_sort16();
+static_assert(kSort16.n == 63, "odd-even merge sort of 16 keys has 63 comparators");
+
+__device__ __forceinline__ void sort16_desc(uint32_t (&a)[16]) {
+#pragma unroll
+  for (int i = 0; i < kSort16.n; ++i) cas_desc(a, kSort16.a[i], kSort16.b[i]);
 }
 
 // a bitonic sequence -> sorted descending
@@ -196,6 +221,7 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
   for (int p = 0; p < KHMAX; ++p) L[p] = 0u;
 
   const int cmax = wave_max_i32(c);
+  const int cmin = -wave_max_i32(valid ? -c : -0x7fffffff);
   const size_t cbase = (size_t)(k.b * hkv + g) * nb;
   for (int jt = 0; jt * 32 < cmax; ++jt) {
     const int jrow = min(jt * 32 + n, nb - 1);
@@ -222,16 +248,26 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
     // query l from lane l - 32 and keeps the second.  A[i] then holds block
     // (i/4)*8 + i%4 and B[i] block (i/4)*8 + 4 + i%4 of this tile, for query t0 + lane.
     uint32_t A[16], B[16];
+    // a tile below every lane's current block needs no causal mask
+    const bool full = (jt + 1) * 32 <= cmin;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[i]),
                                                       __float_as_uint(acc1[i]), false, false);
       const int ja = jt * 32 + (i >> 2) * 8 + (i & 3), jb = ja + 4;
-      A[i] = ja < c ? gate_key(__uint_as_float(r[0]), mask - ja, mask) : 0u;
-      B[i] = jb < c ? gate_key(__uint_as_float(r[1]), mask - jb, mask) : 0u;
+      A[i] = gate_key(__uint_as_float(r[0]), mask - ja, mask);
+      B[i] = gate_key(__uint_as_float(r[1]), mask - jb, mask);
     }
-    bitonic_sort_desc(A);
-    bitonic_sort_desc(B);
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ja = jt * 32 + (i >> 2) * 8 + (i & 3), jb = ja + 4;
+        A[i] = ja < c ? A[i] : 0u;
+        B[i] = jb < c ? B[i] : 0u;
+      }
+    }
+    sort16_desc(A);
+    sort16_desc(B);
     if (KHMAX == 16) {
       // top 16 of the tile: A descending + B reversed is bitonic after the max
 #pragma unroll
