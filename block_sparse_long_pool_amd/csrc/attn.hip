@@ -686,33 +686,72 @@ __device__ __forceinline__ void attend_range(WaveState<D, QT>& st, char* lds,
   w.run(st, tpos, [](int) {}, [](int) {});
 }
 
+// value held by lane (lane ^ 1): a DPP quad permute [1, 0, 3, 2]
+__device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
 // normalise and store one query tile's partial: o rounded to bf16 (nearest even) [D],
-// lse (natural log) in fp32
-template <int D, int QT>
+// lse (natural log) in fp32.  Every lane of the wavefront must call it (with PAIRED
+// the lanes exchange data); only valid rows are written.
+//
+// Lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row, in 16-byte chunks
+// c = (dt, ii / 2).  Chunk c of lane hf is stored at position c*16 + hf*8, next to
+// the same chunk of the pair's other lane, so each store (and each merge load) moves
+// 32 contiguous bytes of a row: half the memory requests of storing each lane's half
+// row apart (at 64K tokens with 128-key blocks, history 4.85 -> 4.29 ms).
+//
+// PAIRED: a row's 64-byte segment s holds chunks 2s and 2s+1 of both lanes.  The
+// lanes of rows n and n ^ 1 trade one chunk per segment, and each store then writes
+// whole 64-byte segments: the lanes of row 2m write its chunk 2s and those of row 2m+1
+// its chunk 2s+1 (first store), and the reverse for row 2m+1 (second store).  Half
+// the requests again (64K with 128-key blocks: 4.24 -> 3.89 ms, same bytes); in the
+// MFMA-bound chained kernel the exchange costs more than it saves (+0.4% at 128K).
+template <int D, int QT, bool PAIRED = false>
 __device__ __forceinline__ void store_partial(const WaveState<D, QT>& st, int qt, bool valid,
                                               uint16_t* __restrict__ po, float* __restrict__ pl) {
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const float ltot = pair_sum(st.l[qt]);
-  if (!valid) return;
+  if (!PAIRED && !valid) return;
   const float inv = 1.f / ltot;
-  // lane (n, hf) holds dims dt*32 + ii*8 + hf*4 + r of its row, in 16-byte chunks
-  // (dt, ii / 2).  Chunk (dt, j) of lane hf is stored at position dt*32 + j*16 + hf*8,
-  // next to the same chunk of the pair's other lane, so each store (and each merge
-  // load) moves 32 contiguous bytes of a row: half the memory requests of storing
-  // each lane's half row apart (at 64K tokens with 128-key blocks, history
-  // 4.85 -> 4.29 ms).
+  u32x4_t wc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
       const f32x16_t& o = st.o[qt][dt];
       const int a = 8 * i2;
-      const u32x4_t w = {pack_bf16x2(o[a] * inv, o[a + 1] * inv),
-                         pack_bf16x2(o[a + 2] * inv, o[a + 3] * inv),
-                         pack_bf16x2(o[a + 4] * inv, o[a + 5] * inv),
-                         pack_bf16x2(o[a + 6] * inv, o[a + 7] * inv)};
-      *reinterpret_cast<u32x4_t*>(po + (dt * 2 + i2) * 16 + hf * 8) = w;
+      wc[dt * 2 + i2] = u32x4_t{pack_bf16x2(o[a] * inv, o[a + 1] * inv),
+                                pack_bf16x2(o[a + 2] * inv, o[a + 3] * inv),
+                                pack_bf16x2(o[a + 4] * inv, o[a + 5] * inv),
+                                pack_bf16x2(o[a + 6] * inv, o[a + 7] * inv)};
     }
+  if (PAIRED) {
+    const bool odd = lane & 1;
+    const uint64_t pa = reinterpret_cast<uint64_t>(po);
+    const uint64_t pb = ((uint64_t)swap_adjacent((uint32_t)(pa >> 32)) << 32) |
+                        swap_adjacent((uint32_t)pa);
+    const bool pvalid = swap_adjacent(valid ? 1u : 0u) != 0u;
+    char* const row_e = reinterpret_cast<char*>(odd ? pb : pa);
+    char* const row_o = reinterpret_cast<char*>(odd ? pa : pb);
+    const bool ve = odd ? pvalid : valid, vo = odd ? valid : pvalid;
+    const int off = (odd ? 32 : 0) + 16 * hf;
+#pragma unroll
+    for (int sg = 0; sg < D / 32; ++sg) {
+      const u32x4_t E = wc[2 * sg], O = wc[2 * sg + 1];
+      u32x4_t x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = swap_adjacent(odd ? E[i] : O[i]);
+      const u32x4_t a = odd ? x : E, b = odd ? O : x;
+      if (ve) *reinterpret_cast<u32x4_t*>(row_e + 64 * sg + off) = a;
+      if (vo) *reinterpret_cast<u32x4_t*>(row_o + 64 * sg + off) = b;
+    }
+    if (!valid) return;
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      *reinterpret_cast<u32x4_t*>(po + c * 16 + hf * 8) = wc[c];
+  }
   if (hf == 0) *pl = (st.m[qt] + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
@@ -1226,8 +1265,8 @@ __global__ __launch_bounds__(64 * kResidentWaves, 2) void attn_history_resident_
     const int rr = valid ? (int)(ent_cur >> sb) : 0;
     const int slot = (int)(ent_cur & ((1u << sb) - 1u));
     const size_t row = sq.prow(b, gi * G + rr % G, ngq) + rr / G;
-    store_partial(st, 0, valid, part_o + (row * (topk - 1) + slot) * D,
-                  part_lse + (size_t)slot * ls + row);
+    store_partial<D, 1, true>(st, 0, valid, part_o + (row * (topk - 1) + slot) * D,
+                              part_lse + (size_t)slot * ls + row);
   };
 
   constexpr int W = kResidentWaves;
