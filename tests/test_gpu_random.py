@@ -2,7 +2,8 @@
 backward, the packed forward and the decode, every row or element against the
 oracle.  They complement the hand-picked cases with combinations nobody chose: odd
 lengths, block sizes from 16 to 256 (and 256 to 2048 for the chained history kernel),
-G = 1 to 8, top-k from 1 to 13, d = 64 and 128.
+G = 1 to 8, top-k from 1 to 13 (6 to 17 over many blocks of at most 128 keys), d = 64
+and 128.
 Bars are those of tests/parity_util.py (forward), tests/test_gpu_backward.py
 (backward) and tests/test_gpu_decode.py (decode).
 """
@@ -59,6 +60,47 @@ def test_forward_random_shape(moba, seed):
     b, T, hq, hkv, d, B, k = draw(seed)
     say(f"[random fwd] seed={seed}: b={b} T={T} hq={hq} hkv={hkv} d={d} B={B} k={k}")
     w = small_workload("rnd", b, hq, hkv, d, T, B, k, "offset", seed=seed)
+    inp = make_inputs(w)
+    out, lse, idx = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), B, k)
+    torch.cuda.synchronize()
+    go, gl, gi = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    Q, K, V = (bf16_to_f64(inp[x]) for x in "qkv")
+    rows = [(bi, t, h) for bi in range(b) for t in range(T) for h in range(hq)]
+    st = compare_rows(Q, K, V, B, k, w.sm_scale, rows,
+                      np.stack([go[bi, t, h] for bi, t, h in rows]),
+                      np.array([gl[bi, h, t] for bi, t, h in rows]),
+                      np.stack([gi[bi, h, t] for bi, t, h in rows]))
+    say(f"       {st}")
+
+
+def draw_resident(seed, max_rows=24000):
+    """(b, T, hq, hkv, d, B, k) with blocks of at most 128 keys (the history kernel that
+    holds the block in LDS, with its paired loads and stores), top-6 to top-17 and a
+    ragged length of at least k + 2 blocks, up to 160 blocks: rows with 5 to 16 history
+    parts, index tiles with odd tails, and (with at least 8 history slots over many
+    blocks) the index's staged scatter."""
+    r = np.random.default_rng(seed)
+    d = int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4, 8]))
+    hkv = int(r.choice([1, 2]))
+    hq = G * hkv
+    B = 16 * int(r.integers(1, 9))
+    k = int(r.integers(6, 18))
+    b = int(r.choice([1, 2]))
+    lo = (k + 2) * B
+    hi = max(min(max_rows // (b * hq), 160 * B), lo + 2)
+    T = int(r.integers(lo, hi))
+    return b, T, hq, hkv, d, B, k
+
+
+@pytest.mark.parametrize("seed", range(400, 410))
+def test_forward_random_small_blocks(moba, seed):
+    b, T, hq, hkv, d, B, k = draw_resident(seed)
+    nb = -(-T // B)
+    staged = k - 1 >= 8 and 256 * (k - 1) < 32 * nb
+    say(f"[random small-block fwd] seed={seed}: b={b} T={T} hq={hq} hkv={hkv} d={d} "
+        f"B={B} k={k} nb={nb} staged_index={staged}")
+    w = small_workload("rnd_res", b, hq, hkv, d, T, B, k, "offset", seed=seed)
     inp = make_inputs(w)
     out, lse, idx = moba.forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), B, k)
     torch.cuda.synchronize()

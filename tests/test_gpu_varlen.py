@@ -111,6 +111,8 @@ def check_packed(moba, lengths, hq, hkv, d, B, k, seed, label):
     ((300, 1500, 64, 900), 8, 8, 128, 64, 9),
     ((2500,), 4, 2, 128, 512, 2),
     ((16, 17, 15, 2000, 33), 16, 2, 128, 16, 6),
+    # top-12 over up to 94 blocks of 32 keys: the index stages each chunk's entries
+    ((3000, 700, 2500, 45), 4, 2, 64, 32, 12),
 ])
 def test_varlen_all_rows(moba, lengths, hq, hkv, d, B, k):
     check_packed(moba, lengths, hq, hkv, d, B, k, seed=sum(lengths) + B, label="all rows")
