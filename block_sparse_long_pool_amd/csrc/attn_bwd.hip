@@ -18,13 +18,14 @@
 //                      into entry order so that the dK/dV kernel reads them contiguously
 //   bwd_dkdv_kernel    per 128 keys of one block: every row that attends them (the
 //                      block's history list, then the block's own rows causally) in
-//                      groups of 32: S = Q K^T, dP = dO V^T, P, dS, then
+//                      groups of 64: S = Q K^T, dP = dO V^T, P, dS, then
 //                      dV^T += dO^T P and dK^T += Q^T dS; dK and dV stay in registers
 //                      and each key is written by exactly one workgroup.
 // MFMA layouts are those of the forward (v_mfma_f32_32x32x16_bf16): a 32x32 result
 // lane l holds column l%32 and rows (i/4)*8 + (l/32)*4 + i%4, and a transposed operand
 // is read from a row-major LDS tile with ds_read_b64_tr_b16 in the order the result
-// registers hold the summation index.
+// registers hold the summation index.  Tiles read both ways are stored once, with their
+// 16-byte chunks permuted per row (kv_swz below).
 
 #include "moba_internal.h"
 
@@ -38,12 +39,6 @@ constexpr int kKvThreads = 2 * 64 * kKvTiles;   // two waves each
 constexpr int kBwdKN = 64;                  // keys per subtile in the dQ kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
-struct BwdStrides {
-  static constexpr int RS = 2 * D + 16;     // rows read 16 bytes per lane (operand rows)
-  static constexpr int TS = 2 * D + 64;     // rows read with the transpose read
-};
-
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -52,18 +47,6 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 __device__ __forceinline__ u32x2_t tr16(const char* p) {
   const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
   return __builtin_bit_cast(u32x2_t, r);
-}
-
-// A = X^T for rows 16ks .. 16ks+15 of a row-major tile with TS-byte rows, dims
-// dt*32 .. +31: the order matches result registers (i/4)*8 + hf*4 + i%4.
-template <int D>
-__device__ __forceinline__ bf16x8_t read_t_operand(const char* tile, int ks, int dt) {
-  const int lane = threadIdx.x & 63, hf = lane >> 5;
-  const char* p = tile + (4 * hf + ((lane & 15) >> 2)) * BwdStrides<D>::TS +
-                  (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2 + dt * 64;
-  const u32x2_t lo = tr16(p + (16 * ks) * BwdStrides<D>::TS);
-  const u32x2_t hi = tr16(p + (16 * ks + 8) * BwdStrides<D>::TS);
-  return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // 16 bytes of global memory through a buffer descriptor covering `bytes` from base
@@ -112,6 +95,49 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   else delta[((token / sq.T) * hq + h) * sq.T + token % sq.T] = acc;
 }
 
+// Row tiles that are read both as MFMA operand rows and with the transpose read (the
+// dQ kernel's K subtiles, the dK/dV kernel's Q and dO row groups; V in the dQ kernel
+// too) are stored once, unpadded (2D bytes per row), with the 16-byte chunks of row r
+// permuted: chunk c sits at position c ^ kv_swz<D>(r).  That one copy serves both
+// reads without bank conflicts: the operand read (16 rows, one chunk each, per LDS
+// pass) needs the 16 rows' chunks on distinct 16-byte bank groups, and the transpose
+// read (4 rows x 64 bytes per pass, rows 4i .. 4i+3) needs the four rows' 64-byte
+// spans on distinct quarters of the 256-byte bank line.  (Padded rows serve one of the
+// two reads each, so they needed two copies.)
+//   D = 128 (16 chunks a row, one row a line): bits 0-1 of r pick the 64-byte quarter,
+//           bits 2-3 the chunk within it;
+//   D = 64 (8 chunks a row, two rows a line): with x = bits 1-3 of r, bit 0 of x picks
+//           the 64-byte half of the row and bits 1-2 the chunk within it.
+// kv_swz depends on r mod 16 only, so every 16-row step keeps the permutation.
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  }
+}
+
+// byte offset of byte `col` (< 2D) of row r in a swizzled group tile
+template <int D>
+__device__ __forceinline__ int kv_off(int r, int col) {
+  return r * (2 * D) + (((col >> 4) ^ kv_swz<D>(r)) << 4) + (col & 15);
+}
+
+// A = X^T for rows 16ks .. 16ks+15 of a swizzled group tile, dims dt*32 .. +31, in the
+// order the result registers hold the summation index
+template <int D>
+__device__ __forceinline__ bf16x8_t read_t_swz(const char* tile, int ks, int dt) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const int r = 4 * hf + ((lane & 15) >> 2);            // < 8: rows r and r + 8
+  const int col = 32 * ((lane >> 4) & 1) + 8 * (lane & 3) + dt * 64;
+  const char* p = tile + 16 * ks * (2 * D);             // kv_swz(16 ks + r) = kv_swz(r)
+  const u32x2_t lo = tr16(p + kv_off<D>(r, col));
+  const u32x2_t hi = tr16(p + kv_off<D>(r + 8, col));
+  return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+
 // ------------------------------------------------------------------------- dQ kernel
 // One workgroup = kBwdWaves * 32 rows against the keys [kbeg, kend) of one kv-head.
 // History: a tile of the inverted index (rows that chose block j; no mask), writing
@@ -119,11 +145,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 // of kv-head g (as the forward), causal, then the sum with the history partials.
 template <int D>
 struct DqLds {
-  using S = BwdStrides<D>;
-  static constexpr int KR = kBwdKN * S::RS;   // K rows for S^T = K Q^T
-  static constexpr int KT = kBwdKN * S::TS;   // K rows for the transpose read (K^T)
-  static constexpr int VR = kBwdKN * S::RS;   // V rows for dP^T = V dO^T
-  static constexpr int BUF = KR + KT + VR;
+  static constexpr int KR = kBwdKN * 2 * D;   // K rows (swizzled): S^T = K Q^T and K^T
+  static constexpr int VR = kBwdKN * 2 * D;   // V rows (swizzled) for dP^T = V dO^T
+  static constexpr int BUF = KR + VR;
   static constexpr int TOTAL = 2 * BUF;
 };
 
@@ -136,7 +160,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const int4* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint32_t* __restrict__ entries, float* __restrict__ dq_part,
     uint16_t* __restrict__ dq) {
-  using S = BwdStrides<D>;
   using L = DqLds<D>;
   constexpr int KS = D / 16, CPR = D / 8;
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
@@ -240,9 +263,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
       const int ci = threadIdx.x + c * kBwdThreads;
       if ((kBwdKN * CPR) % kBwdThreads == 0 || ci < kBwdKN * CPR) {
         const int row = ci / CPR, col = (ci % CPR) * 16;
-        *reinterpret_cast<u32x4_t*>(base + row * S::RS + col) = rk[c];
-        *reinterpret_cast<u32x4_t*>(base + L::KR + row * S::TS + col) = rk[c];
-        *reinterpret_cast<u32x4_t*>(base + L::KR + L::KT + row * S::RS + col) = rv[c];
+        *reinterpret_cast<u32x4_t*>(base + kv_off<D>(row, col)) = rk[c];
+        *reinterpret_cast<u32x4_t*>(base + L::KR + kv_off<D>(row, col)) = rv[c];
       }
     }
   };
@@ -252,8 +274,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   for (int i = 0; i < nsub; ++i) {
     if (i + 1 < nsub) load_sub(i + 1);
     const char* kr = lds + (i & 1) * L::BUF;
-    const char* kt = kr + L::KR;
-    const char* vr = kt + L::KT;
+    const char* vr = kr + L::KR;
     const int kb = kbeg + i * kBwdKN;
     // S^T and dP^T for the subtile's two 32-key halves
     f32x16_t s[2], dp[2];
@@ -261,13 +282,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kk][e] = dp[kk][e] = 0.f;
-      const char* kp = kr + (kk * 32 + n) * S::RS + hf * 16;
-      const char* vp = vr + (kk * 32 + n) * S::RS + hf * 16;
+      const char* kp = kr + (kk * 32 + n) * (2 * D);
+      const char* vp = vr + (kk * 32 + n) * (2 * D);
+      const int sw = kv_swz<D>(n);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + ks * 32)),
+        const int co = ((2 * ks + hf) ^ sw) << 4;
+        s[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + co)),
                              bq[ks], s[kk]);
-        dp[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(vp + ks * 32)),
+        dp[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(vp + co)),
                               bo[ks], dp[kk]);
       }
     }
@@ -296,7 +319,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = mfma32x32x16(read_t_operand<D>(kt, ks, dt), ds[ks], acc[dt]);
+        acc[dt] = mfma32x32x16(read_t_swz<D>(kr, ks, dt), ds[ks], acc[dt]);
     if (i + 1 < nsub) store_sub((i + 1) & 1);
     __syncthreads();
   }
@@ -385,20 +408,26 @@ __global__ __launch_bounds__(256) void bwd_densify_kernel(
 // ----------------------------------------------------------------------- dK/dV kernel
 // One workgroup = 32 * kKvTiles keys of block j of kv-head g.  Rows: the history list
 // of (b, g, j) from the inverted index, then the rows of block j from token kc0 on
-// (causal: key u is attended by token t >= u), G heads each, in groups of 32.
+// (causal: key u is attended by token t >= u), G heads each, in groups of kKvRG.
 // Each 32-key tile has two waves on one SIMD: wave "P" computes S = Q K^T, P, and
 // dV^T += dO^T P; wave "dS" computes dP = dO V^T, takes P through LDS, and
 // dK^T += Q^T dS with dS = P (dP - D).  Each wave keeps one 32 x D accumulator and one
 // B operand, so two waves fit per SIMD and one's VALU work overlaps the other's MFMAs.
 // The history rows are read from bwd_densify_kernel's copy: every workgroup of the
 // block streams the same contiguous rows instead of gathering them from all over Q.
+#ifndef MOBA_KV_RG
+#define MOBA_KV_RG 64
+#endif
+constexpr int kKvRG = MOBA_KV_RG;     // rows per staged group: 32 or 64
+constexpr int kKvRB = kKvRG / 32;     // 32-row MFMA blocks per group
+static_assert(kKvRG == 32 || kKvRG == 64, "groups of one or two 32-row blocks");
+
 template <int D>
 struct KvLds {
-  using S = BwdStrides<D>;
-  static constexpr int QR = 32 * S::RS;
-  static constexpr int QT = 32 * S::TS;
-  static constexpr int BUF = 2 * (QR + QT) + 3 * 32 * 4;   // Q, dO; lse2, delta, t
-  static constexpr int PX = kKvTiles * 64 * 32;             // P tiles, 32 bytes per lane
+  static constexpr int RB = 2 * D;                      // bytes per row
+  static constexpr int QB = kKvRG * RB;                 // Q (or dO) rows of a group
+  static constexpr int BUF = 2 * QB + 3 * kKvRG * 4;    // Q, dO; lse2, delta, t
+  static constexpr int PX = kKvTiles * kKvRB * 64 * 32; // P, 32 bytes per lane and block
   static constexpr int TOTAL = 2 * BUF + PX;
 };
 
@@ -411,7 +440,6 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
     const int32_t* __restrict__ list_offsets, const uint16_t* __restrict__ dense_rows,
     const float* __restrict__ dense_meta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv) {
-  using S = BwdStrides<D>;
   using L = KvLds<D>;
   constexpr int KS = D / 16, CPR = D / 8;
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
@@ -447,13 +475,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  // Staging of a 32-row group: thread x moves 16-byte chunk x % (32*CPR) of Q (x <
-  // 32*CPR) or of dO; threads 0..31 also the rows' lse2, delta and causal limit t.
-  // History rows come from the densified copy of the list (entry order, contiguous);
-  // the block's own rows are token kc0 + rc / G, head rc % G.  Rows past the end read a
-  // valid row and get p = 0 from lse2 = +inf, so the fetch has no branches.  Group i+1
-  // is in flight while group i is computed.
-  constexpr int CHUNKS = 2 * 32 * CPR;
+  // Staging of a group: thread x moves 16-byte chunk x % (kKvRG*CPR) of Q (x <
+  // kKvRG*CPR) or of dO; threads 0..kKvRG-1 also the rows' lse2, delta and causal
+  // limit t.  History rows come from the densified copy of the list (entry order,
+  // contiguous); the block's own rows are token kc0 + rc / G, head rc % G.  Rows past
+  // the end read a valid row and get p = 0 from lse2 = +inf, so the fetch has no
+  // branches.  Group i+1 is in flight while group i is computed.
+  constexpr int CHUNKS = 2 * kKvRG * CPR;
   constexpr int NC = CHUNKS / kKvThreads;
   static_assert(CHUNKS % kKvThreads == 0, "every thread moves whole chunks");
   // own-block row rc is token kc0 + rc / G, head rc % G (shifts when G is a power of 2)
@@ -469,14 +497,15 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   const size_t row_base = (size_t)tok0 * hq + g * G;   // row of (b, t = 0, head g*G)
   const size_t meta_base = sq.lrow(b, g * G, hq);     // lse/delta of (b, g*G, t = 0)
   const int lhs = sq.lhead();                          // lse stride between heads
-  int crow[NC], ccol[NC];
+  int crow[NC], ccol[NC], soff[NC];
   bool cdo[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int x = threadIdx.x + c * kKvThreads;
-    cdo[c] = x >= 32 * CPR;
-    crow[c] = (x % (32 * CPR)) / CPR;
+    cdo[c] = x >= kKvRG * CPR;
+    crow[c] = (x % (kKvRG * CPR)) / CPR;
     ccol[c] = (x % CPR) * 8;
+    soff[c] = (cdo[c] ? L::QB : 0) + kv_off<D>(crow[c], ccol[c] * 2);
   }
   struct Rows {
     u32x4_t c[NC];
@@ -496,7 +525,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
       const uint16_t* csrc = (cdo[c] ? dout : q) + cur_row(r) * D;
       rd.c[c] = *reinterpret_cast<const u32x4_t*>((r < nhist ? hsrc : csrc) + ccol[c]);
     }
-    const int r = r0 + (threadIdx.x & 31);
+    const int r = r0 + (threadIdx.x & (kKvRG - 1));
     float lv, dv0;
     if (r < nhist) {
       const float* m = dense_meta + (size_t)(hbeg + r) * 2;
@@ -515,109 +544,129 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
   auto store_rows = [&](const Rows& rd, int buf) {
     char* base = lds + buf * L::BUF;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      char* t0 = base + (cdo[c] ? L::QR + L::QT : 0) + crow[c] * S::RS + ccol[c] * 2;
-      *reinterpret_cast<u32x4_t*>(t0) = rd.c[c];
-      *reinterpret_cast<u32x4_t*>(t0 + L::QR + crow[c] * (S::TS - S::RS)) = rd.c[c];
-    }
-    if (threadIdx.x < 32) {
-      float* mf = reinterpret_cast<float*>(base + 2 * (L::QR + L::QT));
+    for (int c = 0; c < NC; ++c) *reinterpret_cast<u32x4_t*>(base + soff[c]) = rd.c[c];
+    if (threadIdx.x < kKvRG) {
+      float* mf = reinterpret_cast<float*>(base + 2 * L::QB);
       mf[threadIdx.x] = rd.f;
-      mf[32 + threadIdx.x] = rd.d;
-      reinterpret_cast<int*>(mf + 64)[threadIdx.x] = rd.t;
+      mf[kKvRG + threadIdx.x] = rd.d;
+      reinterpret_cast<int*>(mf + 2 * kKvRG)[threadIdx.x] = rd.t;
     }
   };
   // rows nhist + (0 .. 32*kKvTiles*G - 1) are the tokens kc0 .. kc0 + 32*kKvTiles - 1,
   // the only ones that see keys after themselves; other groups need no causal mask
   const int mask_lo = nhist, mask_hi = nhist + 32 * kKvTiles * G;
-  // this lane's P slot: two 16-byte planes 1 KB apart, so that the 64 lanes of a
-  // 16-byte access touch consecutive bytes
-  char* px = lds + 2 * L::BUF + tile * 2048 + lane * 16;
-  // One 32-row group.  Register e of a 32x32 result holds row (e/4)*8 + hf*4 + e%4.
-  // One code path for both buffers and with or without the causal mask (a uniform
-  // branch around the mask alone): copies of it for each case had the compiler keep
-  // the accumulators in different registers in each copy and move them between them.
+  // this lane's P slots: per 32-row block two 16-byte planes 1 KB apart, so that the
+  // 64 lanes of a 16-byte access touch consecutive bytes
+  char* px = lds + 2 * L::BUF + tile * (kKvRB * 2048) + lane * 16;
+  // this lane's operand-row offset (row n of each 32-row block, k-step 0)
+  const int aoff = n * (2 * D);
+  const int aswz = kv_swz<D>(n);
+  // One group.  Register e of a 32x32 result holds row (e/4)*8 + hf*4 + e%4 of its
+  // 32-row block.  One code path for both buffers and with or without the causal mask
+  // (a uniform branch around the mask alone): copies of it for each case had the
+  // compiler keep the accumulators in different registers in each copy and move them
+  // between them.
   auto compute = [&](int buf, bool masked) {
     const char* base = lds + buf * L::BUF;
-    const float* mf = reinterpret_cast<const float*>(base + 2 * (L::QR + L::QT));
-    // S = Q K^T (wave P) or dP = dO V^T (wave dS): rows x keys
-    const char* ar = base + (role_ds ? L::QR + L::QT : 0) + n * S::RS + hf * 16;
-    f32x16_t sc = {};
+    const float* mf = reinterpret_cast<const float*>(base + 2 * L::QB);
+    // S = Q K^T (wave P) or dP = dO V^T (wave dS): rows x keys, one chain per 32-row
+    // block, the chains alternating
+    const char* ar = base + (role_ds ? L::QB : 0) + aoff;
+    f32x16_t sc[kKvRB];
+#pragma unroll
+    for (int rb = 0; rb < kKvRB; ++rb) sc[rb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      sc = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(ar + ks * 32)), bkv[ks],
-                        sc);
-    bf16x8_t op[2];
+#pragma unroll
+      for (int rb = 0; rb < kKvRB; ++rb)
+        sc[rb] = mfma32x32x16(
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+                ar + rb * 32 * (2 * D) + (((2 * ks + hf) ^ aswz) << 4))),
+            bkv[ks], sc[rb]);
+    bf16x8_t op[2 * kKvRB];
     if (!role_ds) {
-      float p[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(mf + q4 * 8 + hf * 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          p[q4 * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[q4 * 4 + r], sl, -lf[r]));
-      }
-      if (masked) {
+      for (int rb = 0; rb < kKvRB; ++rb) {
+        float p[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int4 lt = *reinterpret_cast<const int4*>(mf + 64 + q4 * 8 + hf * 4);
-          const int tt[4] = {lt.x, lt.y, lt.z, lt.w};
+          const f32x4_t lf =
+              *reinterpret_cast<const f32x4_t*>(mf + rb * 32 + q4 * 8 + hf * 4);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (u > tt[r]) p[q4 * 4 + r] = 0.f;
+            p[q4 * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[rb][q4 * 4 + r], sl, -lf[r]));
         }
-      }
+        if (masked) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t w[4];
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int4 lt = *reinterpret_cast<const int4*>(mf + 2 * kKvRG + rb * 32 +
+                                                           q4 * 8 + hf * 4);
+            const int tt[4] = {lt.x, lt.y, lt.z, lt.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
-        op[hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
-        *reinterpret_cast<u32x4_t*>(px + 1024 * hh) = u32x4_t{w[0], w[1], w[2], w[3]};
+            for (int r = 0; r < 4; ++r)
+              if (u > tt[r]) p[q4 * 4 + r] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = pack_bf16x2(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+          op[2 * rb + hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+          *reinterpret_cast<u32x4_t*>(px + 1024 * (2 * rb + hh)) =
+              u32x4_t{w[0], w[1], w[2], w[3]};
+        }
       }
     }
     __syncthreads();   // P of every tile is in LDS
     if (role_ds) {
       // dS = P (dP - D), P as rounded to bf16 by wave P
-      const u32x4_t pw0 = *reinterpret_cast<const u32x4_t*>(px);
-      const u32x4_t pw1 = *reinterpret_cast<const u32x4_t*>(px + 1024);
-      const uint32_t pw[8] = {pw0[0], pw0[1], pw0[2], pw0[3], pw1[0], pw1[1], pw1[2], pw1[3]};
-      float x[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t ld = *reinterpret_cast<const f32x4_t*>(mf + 32 + q4 * 8 + hf * 4);
+      for (int rb = 0; rb < kKvRB; ++rb) {
+        const u32x4_t pw0 = *reinterpret_cast<const u32x4_t*>(px + 1024 * (2 * rb));
+        const u32x4_t pw1 = *reinterpret_cast<const u32x4_t*>(px + 1024 * (2 * rb + 1));
+        const uint32_t pw[8] = {pw0[0], pw0[1], pw0[2], pw0[3],
+                                pw1[0], pw1[1], pw1[2], pw1[3]};
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = q4 * 4 + r;
-          const float pe = (e & 1) ? bf16hi(pw[e >> 1]) : bf16lo(pw[e >> 1]);
-          x[e] = pe * (sc[e] - ld[r]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t ld =
+              *reinterpret_cast<const f32x4_t*>(mf + kKvRG + rb * 32 + q4 * 8 + hf * 4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = q4 * 4 + r;
+            const float pe = (e & 1) ? bf16hi(pw[e >> 1]) : bf16lo(pw[e >> 1]);
+            x[e] = pe * (sc[rb][e] - ld[r]);
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
+          op[2 * rb + hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
         }
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
-        op[hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
-      }
     }
-    // dV^T += dO^T P (wave P) or dK^T += Q^T dS (wave dS), over the group's 32 rows
-    const char* tt = base + (role_ds ? 0 : L::QR + L::QT) + L::QR;
+    // dV^T += dO^T P (wave P) or dK^T += Q^T dS (wave dS), over the group's rows
+    const char* tt = base + (role_ds ? 0 : L::QB);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2 * kKvRB; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = mfma32x32x16(read_t_operand<D>(tt, ks, dt), op[ks], acc[dt]);
+        acc[dt] = mfma32x32x16(read_t_swz<D>(tt, ks, dt), op[ks], acc[dt]);
   };
-  const int ngroups = (nrows + 31) / 32;
+  const int ngroups = (nrows + kKvRG - 1) / kKvRG;
   Rows rd;
   fetch_rows(0, rd);             // group 0
   store_rows(rd, 0);
   __syncthreads();
   // groups [gm0, gm1) hold the rows that need the causal mask
-  const int gm0 = mask_lo / 32, gm1 = (mask_hi + 31) / 32;
+  const int gm0 = mask_lo / kKvRG, gm1 = (mask_hi + kKvRG - 1) / kKvRG;
   for (int gidx = 0; gidx < ngroups; ++gidx) {
-    fetch_rows((gidx + 1) * 32, rd);     // group gidx + 1
+    fetch_rows((gidx + 1) * kKvRG, rd);     // group gidx + 1
     compute(gidx & 1, gidx >= gm0 && gidx < gm1);
     store_rows(rd, (gidx + 1) & 1);
     __syncthreads();
