@@ -199,7 +199,7 @@ struct CentLds {
 
 // Rank one chunk (its rows compete) with its query operands bq.  The centroids come
 // from global memory, or from the workgroup's LDS image lds (nb <= CentLds::MAX_NB).
-template <int D, int KHMAX, bool CLDS>
+template <int D, int KHMAX, bool CLDS, bool ONE = false>
 __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], const GateChunk& k,
                                            const uint16_t* __restrict__ chi,
                                            const uint16_t* __restrict__ clo,
@@ -223,7 +223,8 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
   const int cmax = wave_max_i32(c);
   const int cmin = -wave_max_i32(valid ? -c : -0x7fffffff);
   const size_t cbase = (size_t)(k.b * hkv + g) * nb;
-  for (int jt = 0; jt * 32 < cmax; ++jt) {
+  // ONE (nb <= 32): a single tile, so the query operands are dead after its MFMAs
+  for (int jt = 0; ONE ? jt < 1 : jt * 32 < cmax; ++jt) {
     const int jrow = min(jt * 32 + n, nb - 1);
     const uint16_t* ph = chi + (cbase + jrow) * D + 8 * hf;
     const uint16_t* pl = clo + (cbase + jrow) * D + 8 * hf;
@@ -351,9 +352,9 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
 // KHMAX: list length (16, 32 or 64) >= topk-1.  D: head_dim.  One wavefront per chunk.
 // Three wavefronts per SIMD: the loads of one chunk hide behind the ranking of others;
 // the 64-long list needs the registers of two.
-template <int KHMAX>
+template <int KHMAX, bool ONE = false>
 struct GateWaves {
-  static constexpr int value = KHMAX > 32 ? 2 : 3;
+  static constexpr int value = KHMAX > 32 ? 2 : (ONE && KHMAX == 16 ? 4 : 3);
 };
 
 template <int D, int KHMAX>
@@ -381,13 +382,15 @@ __global__ __launch_bounds__(kThreads, GateWaves<KHMAX>::value) void gate_topk_k
 // The same with the centroids in LDS (nb <= CentLds::MAX_NB): a workgroup takes four
 // chunks of one (batch, kv-head) group, blockIdx.y = b * hkv + g, and first copies that
 // kv-head's hi/lo centroids into LDS.
-template <int D, int KHMAX>
-__global__ __launch_bounds__(kThreads, GateWaves<KHMAX>::value) void gate_topk_lds_kernel(
+// ONE: nb <= 32, one tile of blocks: the LDS image is sized for 32 rows and, with the
+// 16-long list, the kernel fits four wavefronts per SIMD (more query loads in flight).
+template <int D, int KHMAX, bool ONE>
+__global__ __launch_bounds__(kThreads, (GateWaves<KHMAX, ONE>::value)) void gate_topk_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
     const uint16_t* __restrict__ clo, int batch, SeqMap sq, int hq, int hkv, int block,
     int nb, int topk, int nbits, int32_t* __restrict__ idx) {
   using CL = CentLds<D>;
-  __shared__ __attribute__((aligned(16))) char lds[CL::BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[ONE ? 2 * 32 * CL::CS : CL::BYTES];
   const int G = hq / hkv, nct = (sq.T + 63) / 64;
   const int b = blockIdx.y / hkv, g = blockIdx.y % hkv;
   const int ci = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // chunk in group
@@ -410,7 +413,8 @@ __global__ __launch_bounds__(kThreads, GateWaves<KHMAX>::value) void gate_topk_l
   }
   bf16x8_t bq[2][D / 16];
   gate_load_q<D>(bq, q, k.T, hq, k.tok0, k.h, k.t0, true);
-  gate_chunk<D, KHMAX, true>(bq, k, chi, clo, lds, hq, hkv, block, nb, topk, nbits, idx);
+  gate_chunk<D, KHMAX, true, ONE>(bq, k, chi, clo, lds, hq, hkv, block, nb, topk, nbits,
+                                  idx);
 }
 
 hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
@@ -428,9 +432,13 @@ hipError_t launch_gate(const Shape& s, const uint16_t* q, const uint16_t* chi,
   const dim3 grid_lds((unsigned)((group_chunks + per_block - 1) / per_block), s.b * s.hkv);
 #define MOBA_GATE(DD, KK)                                                                \
   do {                                                                                   \
-    if (clds)                                                                            \
-      hipLaunchKernelGGL((gate_topk_lds_kernel<DD, KK>), grid_lds, dim3(kThreads), 0, st, \
-                         q, chi, clo, s.b, s.seqs(), s.hq, s.hkv, s.block, nb, s.topk,    \
+    if (clds && nb <= 32)                                                                \
+      hipLaunchKernelGGL((gate_topk_lds_kernel<DD, KK, true>), grid_lds, dim3(kThreads), 0, \
+                         st, q, chi, clo, s.b, s.seqs(), s.hq, s.hkv, s.block, nb, s.topk, \
+                         nbits, idx);                                                    \
+    else if (clds)                                                                       \
+      hipLaunchKernelGGL((gate_topk_lds_kernel<DD, KK, false>), grid_lds, dim3(kThreads), 0, \
+                         st, q, chi, clo, s.b, s.seqs(), s.hq, s.hkv, s.block, nb, s.topk, \
                          nbits, idx);                                                    \
     else                                                                                 \
       hipLaunchKernelGGL((gate_topk_kernel<DD, KK>), grid, dim3(kThreads), 0, st, q, chi, \
