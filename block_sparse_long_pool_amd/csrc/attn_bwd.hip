@@ -276,50 +276,55 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const char* kr = lds + (i & 1) * L::BUF;
     const char* vr = kr + L::KR;
     const int kb = kbeg + i * kBwdKN;
-    // S^T and dP^T for the subtile's two 32-key halves
-    f32x16_t s[2], dp[2];
+    // per 32-key half kk: S^T and dP^T (16 MFMAs), then P^T and dS^T (keys past kend,
+    // and in the current block keys after t, get p = 0), then dQ^T += K^T dS^T over the
+    // half's two k-steps.  Only one half's scores are live at a time (233 VGPRs instead
+    // of 252 for the whole subtile at once; the sums run in the same order).
+    const int sw = kv_swz<D>(n);
+    auto scores = [&](int kk, f32x16_t& sk, f32x16_t& pk) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kk][e] = dp[kk][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sk[e] = pk[e] = 0.f;
       const char* kp = kr + (kk * 32 + n) * (2 * D);
       const char* vp = vr + (kk * 32 + n) * (2 * D);
-      const int sw = kv_swz<D>(n);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int co = ((2 * ks + hf) ^ sw) << 4;
-        s[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + co)),
-                             bq[ks], s[kk]);
-        dp[kk] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(vp + co)),
-                              bo[ks], dp[kk]);
+        sk = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(kp + co)), bq[ks], sk);
+        pk = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4_t*>(vp + co)), bo[ks], pk);
       }
-    }
-    // P^T and dS^T; keys past kend, and in the current block keys after t, get p = 0
-    bf16x8_t ds[4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    };
+    auto dsop = [&](int kk, const f32x16_t& sk, const f32x16_t& pk, bf16x8_t (&d2)[2]) {
       float x[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int u = kb + kk * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
         const bool keep = u < kend && (!CUR || u <= t);
-        const float p = keep ? __builtin_amdgcn_exp2f(fmaf(s[kk][e], sl, -lse2)) : 0.f;
-        x[e] = p * (dp[kk][e] - dlt);
+        const float p = keep ? __builtin_amdgcn_exp2f(fmaf(sk[e], sl, -lse2)) : 0.f;
+        x[e] = p * (pk[e] - dlt);
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
-        ds[2 * kk + hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+        d2[hh] = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
       }
+    };
+    auto dqh = [&](int kk, const bf16x8_t (&d2)[2]) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = mfma32x32x16(read_t_swz<D>(kr, 2 * kk + hh, dt), d2[hh], acc[dt]);
+    };
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x16_t sk, pk;
+      bf16x8_t d2[2];
+      scores(kk, sk, pk);
+      dsop(kk, sk, pk, d2);
+      dqh(kk, d2);
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = mfma32x32x16(read_t_swz<D>(kr, ks, dt), ds[ks], acc[dt]);
     if (i + 1 < nsub) store_sub((i + 1) & 1);
     __syncthreads();
   }
