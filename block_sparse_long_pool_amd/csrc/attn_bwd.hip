@@ -36,7 +36,10 @@ constexpr int kBwdWaves = 8;                // dQ kernel
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kKvTiles = 4;                 // dK/dV kernel: 32-key tiles per workgroup,
 constexpr int kKvThreads = 2 * 64 * kKvTiles;   // two waves each
-constexpr int kBwdKN = 64;                  // keys per subtile in the dQ kernel
+#ifndef MOBA_BWD_KN
+#define MOBA_BWD_KN 128
+#endif
+constexpr int kBwdKN = MOBA_BWD_KN;         // keys per subtile in the dQ kernel (64, 128)
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
           acc[dt] = mfma32x32x16(read_t_swz<D>(kr, 2 * kk + hh, dt), d2[hh], acc[dt]);
     };
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kBwdKN / 32; ++kk) {
       f32x16_t sk, pk;
       bf16x8_t d2[2];
       scores(kk, sk, pk);
