@@ -76,23 +76,27 @@ __device__ __forceinline__ void load_row_operand(bf16x8_t (&x)[D / 16], const ui
 }  // namespace
 
 // ------------------------------------------------------------------- D = rowsum(dO*O)
-// rows are (token, head) of the [tokens, hq, d] tensors; delta is laid out like lse
+// rows are (token, head) of the [tokens, hq, d] tensors; delta is laid out like lse.
+// d/8 consecutive lanes share a row, one 16-byte chunk of out and of dout each, so the
+// loads of a wavefront cover whole rows; the lanes' sums are then added pairwise.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ out,
                                                         const uint16_t* __restrict__ dout,
                                                         SeqMap sq, int hq, int d, long rows,
                                                         float* __restrict__ delta) {
-  const long r = (long)blockIdx.x * 256 + threadIdx.x;   // row index token*hq + h
-  if (r >= rows) return;
-  const uint16_t* o = out + r * d;
-  const uint16_t* g = dout + r * d;
+  const int lsh = d == 128 ? 4 : 3;                       // lanes per row: 16 or 8
+  const long r = ((long)blockIdx.x * 256 + threadIdx.x) >> lsh;  // row token*hq + h
+  const int lpr = 1 << lsh, c = (int)(threadIdx.x & (lpr - 1)) * 8;
   float acc = 0.f;
-  for (int c = 0; c < d; c += 8) {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(o + c);
-    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(g + c);
+  if (r < rows) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(out + r * d + c);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(dout + r * d + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       acc += bf16lo(a[e]) * bf16lo(b[e]) + bf16hi(a[e]) * bf16hi(b[e]);
   }
+  // every lane takes part in the exchanges (rows past the end add zeros)
+  for (int o = lpr / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (r >= rows || c != 0) return;
   const long h = r % hq, token = r / hq;
   if (sq.cu) delta[h * sq.total + token] = acc;
   else delta[((token / sq.T) * hq + h) * sq.T + token % sq.T] = acc;
@@ -705,8 +709,9 @@ bool bwd_supported(const Shape& s) { return s.G() >= 1; }
 hipError_t launch_bwd_delta(const Shape& s, const uint16_t* out, const uint16_t* dout,
                             float* delta, hipStream_t st) {
   const long rows = (s.cu ? (long)s.total : (long)s.b * s.T) * s.hq;
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
-                     out, dout, s.seqs(), s.hq, s.d, rows, delta);
+  const long threads = rows * (s.d / 8);                   // d/8 lanes per row
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     st, out, dout, s.seqs(), s.hq, s.d, rows, delta);
   return hipGetLastError();
 }
 
