@@ -632,7 +632,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
       }
     }
     __syncthreads();   // P of every tile is in LDS
+    // Wave dS runs the second phase at raised priority: its dS VALU and then its dK
+    // MFMAs issue first and wave P's dV MFMAs fill the gaps, so the two waves of a SIMD
+    // reach the next barrier together instead of wave dS finishing alone.
     if (role_ds) {
+      __builtin_amdgcn_s_setprio(1);
       // dS = P (dP - D), P as rounded to bf16 by wave P
 #pragma unroll
       for (int rb = 0; rb < kKvRB; ++rb) {
@@ -669,6 +673,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
         acc[dt] = mfma32x32x16(read_t_swz<D>(tt, ks, dt), op[ks], acc[dt]);
+    if (role_ds) __builtin_amdgcn_s_setprio(0);
   };
   const int ngroups = (nrows + kKvRG - 1) / kKvRG;
   Rows rd;
