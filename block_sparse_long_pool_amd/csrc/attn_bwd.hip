@@ -329,7 +329,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
       f32x16_t sk, pk;
       bf16x8_t d2[2];
       scores(kk, sk, pk);
+      // the exponentials at raised priority, next to the other wave's MFMAs
+      __builtin_amdgcn_s_setprio(1);
       dsop(kk, sk, pk, d2);
+      __builtin_amdgcn_s_setprio(0);
       dqh(kk, d2);
     }
     if (i + 1 < nsub) store_sub((i + 1) & 1);
