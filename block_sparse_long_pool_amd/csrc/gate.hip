@@ -351,7 +351,8 @@ __device__ __forceinline__ void gate_chunk(const bf16x8_t (&bq)[2][D / 16], cons
 
 // KHMAX: list length (16, 32 or 64) >= topk-1.  D: head_dim.  One wavefront per chunk.
 // Three wavefronts per SIMD: the loads of one chunk hide behind the ranking of others;
-// the 64-long list needs the registers of two.
+// the 64-long list needs the registers of two, and the single-tile LDS kernel (ONE)
+// with the 16-long list fits four.
 template <int KHMAX, bool ONE = false>
 struct GateWaves {
   static constexpr int value = KHMAX > 32 ? 2 : (ONE && KHMAX == 16 ? 4 : 3);
@@ -385,7 +386,8 @@ __global__ __launch_bounds__(kThreads, GateWaves<KHMAX>::value) void gate_topk_k
 // ONE: nb <= 32, one tile of blocks: the LDS image is sized for 32 rows and, with the
 // 16-long list, the kernel fits four wavefronts per SIMD (more query loads in flight).
 template <int D, int KHMAX, bool ONE>
-__global__ __launch_bounds__(kThreads, (GateWaves<KHMAX, ONE>::value)) void gate_topk_lds_kernel(
+__global__ __launch_bounds__(kThreads, (GateWaves<KHMAX, ONE>::value))
+void gate_topk_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ chi,
     const uint16_t* __restrict__ clo, int batch, SeqMap sq, int hq, int hkv, int block,
     int nb, int topk, int nbits, int32_t* __restrict__ idx) {
