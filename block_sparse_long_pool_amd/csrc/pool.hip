@@ -3,11 +3,13 @@
 // ("MoBA: Mixture of Block Attention for Long-Context LLMs", paper summary page,
 // section "Approach": a block is represented by its mean-pooled key).
 //
-// HBM-bound.  A token's keys for all kv-heads are one contiguous row of hkv*d bf16,
-// so a workgroup reads whole rows with 16-byte loads (fully coalesced) and keeps one
-// float32 partial sum per column.  Blocks are split into `splits` token ranges so the
-// grid has enough workgroups; a second pass adds the split partials in a fixed order
-// (deterministic, no atomics) and divides by the token count.
+// HBM-bound.  When (sequence, block, kv-head) triples fill the chip (at least 256),
+// one workgroup pools one block of one kv-head in a single pass: d/8 threads read a
+// key row's d columns with 16-byte loads, sixteen rows in flight per thread, and the
+// per-thread float32 sums are added in a fixed order in LDS (deterministic, no
+// atomics).  Otherwise a token's keys for all kv-heads, one contiguous row of hkv*d
+// bf16, are read by workgroups over `splits` token ranges of each block, and a second
+// pass adds the split partials in a fixed order and divides by the token count.
 #include "moba_internal.h"
 
 namespace moba {
@@ -94,6 +96,56 @@ __global__ __launch_bounds__(kThreads) void pool_finalize_kernel(
   if (chi != nullptr) split_hi_lo(c, chi + i, clo + i);
 }
 
+// one block j of kv-head g of sequence b, in one pass (the layout of cent, chi, clo is
+// [b][hkv][nb][d]); a block past the end of a shorter packed sequence gets 0
+template <int D>
+__global__ __launch_bounds__(kThreads) void pool_block_kernel(
+    const uint16_t* __restrict__ k, SeqMap sq, int hkv, int block, int nb,
+    float* __restrict__ cent, uint16_t* __restrict__ chi, uint16_t* __restrict__ clo) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int RP = kThreads / CPR;         // rows per pass
+  constexpr int U = 16;                      // rows in flight per thread
+  __shared__ float red[RP * D];
+  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int T = sq.len(b), tok0 = sq.tok0(b);
+  const int row0 = j * block, row1 = min((j + 1) * block, T);
+  const int tid = threadIdx.x, rsub = tid / CPR, cc = tid % CPR;
+  const size_t rs = (size_t)hkv * D;         // elements from one token's keys to the next
+  const uint16_t* base = k + ((size_t)tok0 * hkv + g) * D + cc * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  auto add = [&](const u32x4_t& v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16lo(v[e]);
+      acc[2 * e + 1] += bf16hi(v[e]);
+    }
+  };
+  int row = row0 + rsub;
+  for (; row + (U - 1) * RP < row1; row += U * RP) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = *reinterpret_cast<const u32x4_t*>(base + (size_t)(row + u * RP) * rs);
+#pragma unroll
+    for (int u = 0; u < U; ++u) add(v[u]);
+  }
+  for (; row < row1; row += RP) add(*reinterpret_cast<const u32x4_t*>(base + (size_t)row * rs));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rsub * D + cc * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.f;
+    for (int r = 0; r < RP; ++r) sum += red[r * D + tid];
+    const int n = row1 - row0;
+    const float c = n > 0 ? sum / (float)n : 0.f;
+    const size_t i = (((size_t)b * hkv + g) * nb + j) * D + tid;
+    cent[i] = c;
+    if (chi != nullptr) split_hi_lo(c, chi + i, clo + i);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void centroid_split_kernel(
     const float* __restrict__ cent, size_t total, uint16_t* __restrict__ chi,
     uint16_t* __restrict__ clo) {
@@ -112,6 +164,16 @@ int pool_splits(const Shape& s) {
 hipError_t launch_pool(const Shape& s, const uint16_t* k, float* partial, float* cent,
                        uint16_t* chi, uint16_t* clo, hipStream_t st) {
   const int nb = s.nb();
+  if ((long)s.b * nb * s.hkv >= 256) {
+    const dim3 grid(s.hkv, nb, s.b);
+    if (s.d == 128)
+      hipLaunchKernelGGL(pool_block_kernel<128>, grid, dim3(kThreads), 0, st, k, s.seqs(),
+                         s.hkv, s.block, nb, cent, chi, clo);
+    else
+      hipLaunchKernelGGL(pool_block_kernel<64>, grid, dim3(kThreads), 0, st, k, s.seqs(),
+                         s.hkv, s.block, nb, cent, chi, clo);
+    return hipGetLastError();
+  }
   const int splits = pool_splits(s);
   const int rows_per_split = (s.block + splits - 1) / splits;
   const int cols = s.hkv * s.d;
