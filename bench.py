@@ -456,6 +456,7 @@ def main(argv=None):
     hist_tflops = flop_hist / (stage["history"] * 1e-3) / 1e12 if stage["history"] else None
     gbytes = gate_bytes(w, needed_only=False)
     gbytes_needed = gate_bytes(w, needed_only=True)
+    pbytes = w.batch * w.seqlen * w.hkv * w.head_dim * 2
     gate_s = stage["gate"] * 1e-3
     gate_gbs = gbytes / gate_s / 1e9 if gate_s else None
     gate_gbs_needed = gbytes_needed / gate_s / 1e9 if gate_s else None
@@ -505,6 +506,11 @@ def main(argv=None):
         "gate_needed_gbs": gate_gbs_needed,
         "gate_needed_frac_of_hbm_peak": (gate_gbs_needed / PEAK_HBM_GBS
                                          if gate_gbs_needed else None),
+        # the centroid pool reads every key once: T * Hkv * d bf16
+        "pool_gbs": pbytes / (stage["pool"] * 1e-3) / 1e9 if stage["pool"] else None,
+        "pool_frac_of_hbm_peak": (pbytes / (stage["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+                                  if stage["pool"] else None),
+        "pool_algorithmic_bytes": pbytes,
         "roofline": roofline,
         "current_kernel": {
             "ms": stage["current"],
