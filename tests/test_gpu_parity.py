@@ -68,6 +68,9 @@ def full_compare(moba, w, inp=None, label=""):
 @pytest.mark.parametrize("b,T,hkv,d,B", [
     (1, 2048, 1, 64, 128), (2, 4096, 8, 128, 512), (1, 1024, 2, 128, 16),
     (1, 8192, 8, 128, 4096), (1, 512, 32, 64, 256),
+    # at least 256 (sequence, block, kv-head) triples: the one-pass kernel
+    (1, 8192, 8, 128, 128), (2, 4096, 4, 64, 64), (1, 8000, 8, 128, 128),
+    (1, 16384, 8, 128, 512),
 ])
 def test_pool_centroids(moba, b, T, hkv, d, B):
     w = small_workload("pool", b, hkv, hkv, d, T, B, 1, "offset", seed=T + d)
@@ -80,16 +83,18 @@ def test_pool_centroids(moba, b, T, hkv, d, B):
     np.testing.assert_allclose(got, ref, rtol=2e-6, atol=2e-6)
 
 
-def test_pool_constant_blocks_exact(moba):
-    """A block of one constant key has exactly that centroid (power-of-two B)."""
-    b, T, hkv, d, B = 1, 1024, 2, 64, 256
+@pytest.mark.parametrize("T,hkv,B", [(1024, 2, 256), (4096, 8, 16)])
+def test_pool_constant_blocks_exact(moba, T, hkv, B):
+    """A block of one constant key has exactly that centroid (power-of-two B); the
+    second shape has 2048 (block, kv-head) pairs, so the one-pass kernel runs."""
+    b, d = 1, 64
     k = np.zeros((b, T, hkv, d), np.uint16)
     vals = np.array([0x3FA0, 0xC040, 0x3E80, 0x4110], np.uint16)   # 1.25, -3, 0.25, 9
-    for j in range(4):
-        k[:, j * B:(j + 1) * B] = vals[j]
+    for j in range(T // B):
+        k[:, j * B:(j + 1) * B] = vals[j % 4]
     c = moba.pool_centroids(dev(k), B).cpu().numpy()
-    for j in range(4):
-        assert np.all(c[0, :, j] == bf16_to_f64(vals[j:j + 1])[0])
+    for j in range(T // B):
+        assert np.all(c[0, :, j] == bf16_to_f64(vals[j % 4:j % 4 + 1])[0])
 
 
 # ------------------------------------------------------------------------- (a2)
