@@ -107,6 +107,7 @@ def test_pool_constant_blocks_exact(moba, T, hkv, B):
     (1, 16384, 32, 8, 128, 512, 3, "iid"),        # GQA 4
     (1, 4096, 8, 8, 128, 256, 1, "iid"),          # no history slots
     (1, 2048, 1, 1, 64, 16, 5, "offset"),         # G=1, B=16: a tile spans two blocks
+    (1, 4096, 4, 2, 64, 128, 24, "iid"),          # nb=32 single tile, KH=23 -> 32-list
 ])
 def test_gate_topk(moba, b, T, hq, hkv, d, B, k, recipe):
     w = small_workload("gate", b, hq, hkv, d, T, B, k, recipe, seed=T + k)
